@@ -1,0 +1,158 @@
+/*
+ * moe_decode.h -- C ABI of the persistent MoE decode layer for MI355X (gfx950).
+ *
+ * One call of moe_decode_run computes, for T token rows x[T][H] (bf16):
+ *
+ *   logits[t][e] = sum_h x[t][h] * router_w[e][h] (+ router_bias[e])
+ *   score        = sigmoid(logits); the K highest scores of each row are
+ *                  selected (score descending, ties to the lower expert id)
+ *                  and their weights w[t][k] renormalised to sum to 1
+ *   rows are placed into 8-row tiles of their experts, in row order,
+ *                  without a sort (per-expert row bitmaps + population counts)
+ *   per selected expert e (and the shared expert, slot E, for every row):
+ *       g = W_gate[e] x,  u = W_up[e] x,  h = bf16(silu(g) * u),  o_e = W_down[e] h
+ *       (FP8 e4m3fn weights, one fp32 scale per 32 contiguous K elements)
+ *   y[t] = bf16( o_shared[t] + sum_k w[t][k] * o_{idx[t][k]}[t] )
+ *
+ * in ONE persistent kernel launch.  Sources (page titles and sections):
+ *   - "SGLang's Low-Latency Mode Boosts DeepSeek-V4.1-Flash Speed by 1.56x on
+ *     AMD": section "NVIDIA overlaps the dependency chain" (routing without
+ *     sorting: 8-row tiles, bitmap and population counts, top-k preserved);
+ *     section "AMD keeps the layer resident" (persistent kernel including
+ *     the MoE, waits with deadlines); section "Four stages keep megakernels
+ *     outside core" (Register / Guard / Build / Runtime, fallback).
+ *   - "FlyDSL Mono Kernels for High-Interactivity LLM Serving in ATOM":
+ *     sections "What FlyDSL Provides" and "MiniMax-M3: Connecting Attention
+ *     and Experts" (blocks that stay resident and hand ready results on
+ *     through tagged buffers, early weight loads, routed and shared expert
+ *     up/gate and down projections fused in one path).
+ *   - "Beyond Day-0: Optimizing DeepSeek-V4.1 Flash in SGLang", section 2.1
+ *     (group32 FP8 weights and scales reorganised for the kernel; router
+ *     emitting the downstream layout; fused weighted reduction of expert
+ *     outputs plus shared-expert addition; scratch buffers reused across
+ *     calls) and section 3.1 (fused SwiGLU keeping the intermediate rounding).
+ *
+ * Conventions: every pointer named "device" is a HIP device pointer on the
+ * handle's device; streams are hipStream_t passed as void* (NULL = the null
+ * stream).  No function prints, aborts or throws; all report moe_status.
+ */
+#ifndef MOE_DECODE_H
+#define MOE_DECODE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_DECODE_ABI_VERSION 1
+
+typedef int32_t moe_status;
+#define MOE_OK                0  /* success */
+#define MOE_ERR_INVALID_ARG   1  /* NULL / misaligned pointer, T out of range, bad config */
+#define MOE_ERR_UNSUPPORTED   2  /* shape outside what the kernel handles: use another path */
+#define MOE_ERR_HIP           3  /* a HIP runtime call failed */
+#define MOE_ERR_OUT_OF_MEMORY 4  /* device allocation failed in create */
+#define MOE_ERR_TIMEOUT       5  /* an in-kernel wait passed its deadline (reported by check) */
+
+/* Layer shape and limits, fixed at create time. */
+typedef struct moe_decode_config {
+  int32_t max_tokens;    /* largest T any run on the handle may pass; 1..4096 */
+  int32_t hidden;        /* H; multiple of 64, <= 16384 */
+  int32_t num_experts;   /* E routed experts; 1..256 */
+  int32_t top_k;         /* K experts per row; 1..min(E, 16) */
+  int32_t intermediate;  /* I per expert; multiple of 64, <= 8192 */
+  int32_t num_shared;    /* S always-on shared experts; 0 or 1 */
+  int32_t deadline_us;   /* bound on every in-kernel wait, microseconds; 0 = 1 s */
+  uint32_t flags;        /* reserved; must be 0 */
+} moe_decode_config;
+
+/*
+ * Weights, all device pointers, row-major and contiguous.  create() reads
+ * them once (it re-lays the FP8 matrices out into the kernel's tile order in
+ * memory the handle owns), so the caller may free them after create returns.
+ *   router_w    [E][H]               fp32
+ *   router_bias [E]                  fp32, or NULL for no bias
+ *   w13         [E+S][2I][H]         FP8 e4m3fn (OCP); rows [0,I) gate, [I,2I) up
+ *   s13         [E+S][2I][H/32]      fp32 scale of each 32 contiguous K elements
+ *   w2          [E+S][H][I]          FP8 e4m3fn (down projection)
+ *   s2          [E+S][H][I/32]       fp32
+ * Slot E (the last) is the shared expert when S = 1.  A weight's value is
+ * e4m3fn(q) * scale; codes 0x7F/0xFF (NaN) must not occur.
+ */
+typedef struct moe_decode_weights {
+  const float* router_w;
+  const float* router_bias;
+  const uint8_t* w13;
+  const float* s13;
+  const uint8_t* w2;
+  const float* s2;
+} moe_decode_weights;
+
+/*
+ * Optional copies of intermediate results (each pointer may be NULL; device
+ * memory, written by the same kernel, valid once the run's stream reaches it):
+ *   topk_idx     [T][K] int32  selected experts, score descending
+ *   topk_w       [T][K] fp32   renormalised weights
+ *   pair_rank    [T][K] int32  position of row t among the rows of expert
+ *                              topk_idx[t][k] (tile = rank / 8, slot = rank % 8)
+ *   expert_count [E]    int32  rows routed to each expert
+ *   logits       [T][E] fp32   router logits including the bias
+ */
+typedef struct moe_decode_debug {
+  int32_t* topk_idx;
+  float* topk_w;
+  int32_t* pair_rank;
+  int32_t* expert_count;
+  float* logits;
+} moe_decode_debug;
+
+typedef struct moe_decode_handle moe_decode_handle;
+
+/* Register: the ABI version this library implements (MOE_DECODE_ABI_VERSION). */
+int32_t moe_decode_abi_version(void);
+
+/*
+ * Guard: MOE_OK if a handle created with cfg can run T rows, MOE_ERR_UNSUPPORTED
+ * if the shape is outside the kernel's limits (the caller should fall back to
+ * a general path), MOE_ERR_INVALID_ARG for a NULL cfg.  No device access.
+ */
+moe_status moe_decode_supported(const moe_decode_config* cfg, int32_t T);
+
+/*
+ * Build: allocate the handle's workspace (sized for cfg->max_tokens), copy the
+ * router and re-lay the expert weights into tile order on device `device`.
+ * Synchronous.  On success *out owns all of it until moe_decode_destroy.
+ */
+moe_status moe_decode_create(const moe_decode_config* cfg, const moe_decode_weights* w,
+                             int32_t device, moe_decode_handle** out);
+
+/*
+ * Runtime: enqueue one layer call on hip_stream.  x and y are device pointers to
+ * [T][H] bf16, 16-byte aligned, not overlapping; dbg may be NULL.  T = 0 is a
+ * no-op.  Asynchronous: no allocation, no host synchronisation, one kernel
+ * launch.  Runs on one handle must be ordered on one stream (they share the
+ * workspace).  A wait that passes the deadline makes the kernel exit early
+ * (y is then undefined) and is reported by moe_decode_check.
+ */
+moe_status moe_decode_run(moe_decode_handle* h, const void* x, int32_t T, void* y,
+                          const moe_decode_debug* dbg, void* hip_stream);
+
+/*
+ * Wait for the last run's stream and report its in-kernel status:
+ * MOE_OK, or MOE_ERR_TIMEOUT if a deadline fired (the status is then cleared,
+ * so the next run starts clean).
+ */
+moe_status moe_decode_check(moe_decode_handle* h);
+
+/* Free everything the handle owns (synchronises its device first). NULL is a no-op. */
+void moe_decode_destroy(moe_decode_handle* h);
+
+/* Static description of a status code. */
+const char* moe_decode_status_string(moe_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_DECODE_H */

@@ -1,0 +1,194 @@
+"""ctypes binding of the C ABI in include/moe_decode.h (argument marshalling only).
+
+The functions keep the C names.  Tensors are torch tensors on the handle's
+device; only their data pointers cross the boundary.  Every step of the layer
+runs in the HIP library; if it has not been built, loading fails loudly.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "_moe_decode.so")
+
+MOE_OK = 0
+MOE_ERR_INVALID_ARG = 1
+MOE_ERR_UNSUPPORTED = 2
+MOE_ERR_HIP = 3
+MOE_ERR_OUT_OF_MEMORY = 4
+MOE_ERR_TIMEOUT = 5
+
+# Functions declared in include/moe_decode.h, in declaration order.
+EXPORTS = (
+    "moe_decode_abi_version",
+    "moe_decode_supported",
+    "moe_decode_create",
+    "moe_decode_run",
+    "moe_decode_check",
+    "moe_decode_destroy",
+    "moe_decode_status_string",
+)
+
+
+class moe_decode_config(ctypes.Structure):
+    _fields_ = [
+        ("max_tokens", ctypes.c_int32),
+        ("hidden", ctypes.c_int32),
+        ("num_experts", ctypes.c_int32),
+        ("top_k", ctypes.c_int32),
+        ("intermediate", ctypes.c_int32),
+        ("num_shared", ctypes.c_int32),
+        ("deadline_us", ctypes.c_int32),
+        ("flags", ctypes.c_uint32),
+    ]
+
+
+class moe_decode_weights(ctypes.Structure):
+    _fields_ = [
+        ("router_w", ctypes.c_void_p),
+        ("router_bias", ctypes.c_void_p),
+        ("w13", ctypes.c_void_p),
+        ("s13", ctypes.c_void_p),
+        ("w2", ctypes.c_void_p),
+        ("s2", ctypes.c_void_p),
+    ]
+
+
+class moe_decode_debug(ctypes.Structure):
+    _fields_ = [
+        ("topk_idx", ctypes.c_void_p),
+        ("topk_w", ctypes.c_void_p),
+        ("pair_rank", ctypes.c_void_p),
+        ("expert_count", ctypes.c_void_p),
+        ("logits", ctypes.c_void_p),
+    ]
+
+
+class MoeDecodeError(RuntimeError):
+    def __init__(self, where: str, status: int):
+        super().__init__(f"{where}: {moe_decode_status_string(status)} (status {status})")
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: run __graft_entry__.build() to compile the HIP library")
+        L = ctypes.CDLL(LIB_PATH)
+        P = ctypes.c_void_p
+        L.moe_decode_abi_version.restype = ctypes.c_int32
+        L.moe_decode_abi_version.argtypes = []
+        L.moe_decode_supported.restype = ctypes.c_int32
+        L.moe_decode_supported.argtypes = [ctypes.POINTER(moe_decode_config), ctypes.c_int32]
+        L.moe_decode_create.restype = ctypes.c_int32
+        L.moe_decode_create.argtypes = [ctypes.POINTER(moe_decode_config),
+                                        ctypes.POINTER(moe_decode_weights), ctypes.c_int32,
+                                        ctypes.POINTER(P)]
+        L.moe_decode_run.restype = ctypes.c_int32
+        L.moe_decode_run.argtypes = [P, P, ctypes.c_int32, P, ctypes.POINTER(moe_decode_debug), P]
+        L.moe_decode_check.restype = ctypes.c_int32
+        L.moe_decode_check.argtypes = [P]
+        L.moe_decode_destroy.restype = None
+        L.moe_decode_destroy.argtypes = [P]
+        L.moe_decode_status_string.restype = ctypes.c_char_p
+        L.moe_decode_status_string.argtypes = [ctypes.c_int32]
+        _lib = L
+    return _lib
+
+
+# ---- thin wrappers with the C names ---------------------------------------
+def moe_decode_abi_version() -> int:
+    return lib().moe_decode_abi_version()
+
+
+def moe_decode_status_string(status: int) -> str:
+    return lib().moe_decode_status_string(status).decode()
+
+
+def moe_decode_supported(cfg: moe_decode_config, T: int) -> int:
+    return lib().moe_decode_supported(ctypes.byref(cfg), T)
+
+
+def moe_decode_create(cfg: moe_decode_config, w: moe_decode_weights, device: int):
+    h = ctypes.c_void_p()
+    st = lib().moe_decode_create(ctypes.byref(cfg), ctypes.byref(w), device, ctypes.byref(h))
+    return st, h
+
+
+def moe_decode_run(h, x_ptr: int, T: int, y_ptr: int, dbg: moe_decode_debug | None,
+                   stream: int) -> int:
+    return lib().moe_decode_run(h, x_ptr, T, y_ptr, ctypes.byref(dbg) if dbg is not None else None,
+                                stream)
+
+
+def moe_decode_check(h) -> int:
+    return lib().moe_decode_check(h)
+
+
+def moe_decode_destroy(h) -> None:
+    lib().moe_decode_destroy(h)
+
+
+# ---- convenience layer over torch tensors ---------------------------------
+def make_config(T_max, H, E, K, I, S, deadline_us=0) -> moe_decode_config:
+    return moe_decode_config(T_max, H, E, K, I, S, deadline_us, 0)
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+class MoeDecode:
+    """One handle: weights re-laid out on the device, workspace for max_tokens rows.
+
+    ``weights`` maps router_w, router_bias (or None), w13, s13, w2, s2 to
+    contiguous torch tensors on ``device`` in the layouts of the header.
+    """
+
+    def __init__(self, cfg: moe_decode_config, weights: dict, device: int = 0):
+        for name in ("router_w", "w13", "s13", "w2", "s2"):
+            t = weights[name]
+            assert t.is_cuda and t.is_contiguous(), name
+        w = moe_decode_weights(_ptr(weights["router_w"]), _ptr(weights.get("router_bias")),
+                               _ptr(weights["w13"]), _ptr(weights["s13"]),
+                               _ptr(weights["w2"]), _ptr(weights["s2"]))
+        st, h = moe_decode_create(cfg, w, device)
+        if st != MOE_OK:
+            raise MoeDecodeError("moe_decode_create", st)
+        self.cfg = cfg
+        self.handle = h
+
+    def run(self, x, y, T: int | None = None, debug: dict | None = None, stream=None) -> None:
+        """Enqueue one layer call: x [T][H] bf16 -> y [T][H] bf16 (torch tensors)."""
+        import torch
+        if T is None:
+            T = x.shape[0]
+        dbg = None
+        if debug:
+            dbg = moe_decode_debug(_ptr(debug.get("topk_idx")), _ptr(debug.get("topk_w")),
+                                   _ptr(debug.get("pair_rank")), _ptr(debug.get("expert_count")),
+                                   _ptr(debug.get("logits")))
+        s = stream if stream is not None else torch.cuda.current_stream()
+        st = moe_decode_run(self.handle, x.data_ptr(), T, y.data_ptr(), dbg, s.cuda_stream)
+        if st != MOE_OK:
+            raise MoeDecodeError("moe_decode_run", st)
+
+    def check(self) -> int:
+        return moe_decode_check(self.handle)
+
+    def close(self) -> None:
+        if self.handle:
+            moe_decode_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -1,0 +1,81 @@
+"""The C-ABI library loads, exports every function include/moe_decode.h declares,
+and its host-side argument checks (Guard) answer without touching a GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from moe_decode_layer_amd import binding
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include",
+                      "moe_decode.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(moe_decode_\w+)\s*\(", text, flags=re.M)
+
+
+def test_header_declarations_match_binding():
+    assert tuple(declared_functions()) == binding.EXPORTS
+
+
+def test_library_exports_every_declared_symbol():
+    L = binding.lib()
+    for name in declared_functions():
+        assert isinstance(getattr(L, name), ctypes._CFuncPtr), name
+
+
+def test_abi_version_and_status_strings():
+    assert binding.moe_decode_abi_version() == 1
+    for st in range(6):
+        assert binding.moe_decode_status_string(st) != "unknown status"
+    assert binding.moe_decode_status_string(99) == "unknown status"
+
+
+def cfg(**kw):
+    base = dict(T_max=384, H=4096, E=256, K=8, I=512, S=1)
+    base.update(kw)
+    return binding.make_config(base["T_max"], base["H"], base["E"], base["K"], base["I"], base["S"])
+
+
+@pytest.mark.parametrize("kw,T,want", [
+    ({}, 6, binding.MOE_OK),
+    ({}, 384, binding.MOE_OK),
+    ({}, 0, binding.MOE_OK),
+    ({}, 385, binding.MOE_ERR_UNSUPPORTED),
+    ({}, -1, binding.MOE_ERR_INVALID_ARG),
+    ({"H": 4000}, 6, binding.MOE_ERR_UNSUPPORTED),
+    ({"I": 576}, 6, binding.MOE_OK),
+    ({"I": 96}, 6, binding.MOE_ERR_UNSUPPORTED),
+    ({"K": 17, "E": 32}, 6, binding.MOE_ERR_UNSUPPORTED),
+    ({"K": 9, "E": 8}, 6, binding.MOE_ERR_UNSUPPORTED),
+    ({"E": 257}, 6, binding.MOE_ERR_UNSUPPORTED),
+    ({"S": 2}, 6, binding.MOE_ERR_UNSUPPORTED),
+    ({"T_max": 513}, 6, binding.MOE_ERR_UNSUPPORTED),
+    ({"T_max": 0}, 0, binding.MOE_ERR_INVALID_ARG),
+    ({"E": 0}, 1, binding.MOE_ERR_INVALID_ARG),
+])
+def test_guard(kw, T, want):
+    assert binding.moe_decode_supported(cfg(**kw), T) == want
+
+
+def test_null_arguments_are_rejected_before_any_device_call():
+    L = binding.lib()
+    assert L.moe_decode_supported(None, 1) == binding.MOE_ERR_INVALID_ARG
+    h = ctypes.c_void_p()
+    w = binding.moe_decode_weights()
+    assert L.moe_decode_create(None, ctypes.byref(w), 0, ctypes.byref(h)) == binding.MOE_ERR_INVALID_ARG
+    c = cfg()
+    assert L.moe_decode_create(ctypes.byref(c), None, 0, ctypes.byref(h)) == binding.MOE_ERR_INVALID_ARG
+    assert L.moe_decode_create(ctypes.byref(c), ctypes.byref(w), 0, ctypes.byref(h)) == \
+        binding.MOE_ERR_INVALID_ARG          # NULL weight pointers
+    assert L.moe_decode_create(ctypes.byref(c), ctypes.byref(w), 0, None) == binding.MOE_ERR_INVALID_ARG
+    bad = cfg(H=100)
+    assert L.moe_decode_create(ctypes.byref(bad), ctypes.byref(w), 0, ctypes.byref(h)) == \
+        binding.MOE_ERR_UNSUPPORTED
+    assert L.moe_decode_run(None, None, 1, None, None, None) == binding.MOE_ERR_INVALID_ARG
+    assert L.moe_decode_check(None) == binding.MOE_ERR_INVALID_ARG
+    L.moe_decode_destroy(None)
