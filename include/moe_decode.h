@@ -57,7 +57,7 @@ typedef int32_t moe_status;
 
 /* Layer shape and limits, fixed at create time. */
 typedef struct moe_decode_config {
-  int32_t max_tokens;    /* largest T any run on the handle may pass; 1..4096 */
+  int32_t max_tokens;    /* largest T any run on the handle may pass; 1..512 */
   int32_t hidden;        /* H; multiple of 64, <= 16384 */
   int32_t num_experts;   /* E routed experts; 1..256 */
   int32_t top_k;         /* K experts per row; 1..min(E, 16) */
@@ -105,6 +105,18 @@ typedef struct moe_decode_debug {
   int32_t* pair_rank;
   int32_t* expert_count;
   float* logits;
+  /*
+   * Per-workgroup timeline (profiling the waits).  trace is device memory of
+   * int64 [trace_blocks][1 + trace_cap][4]; workgroups with index >=
+   * trace_blocks record nothing.  Row 0 of a block: {kernel entry, exit,
+   * items recorded, workgroups in the grid}; row 1 + i: {ticket | kind << 32,
+   * ticket granted, inputs ready (after any wait), item done}.  Times are
+   * the 100 MHz device wall clock.  kind: 0 router, 1 shared gate/up,
+   * 2 top-k, 3 shared down, 4 routed gate/up, 5 routed down, 6 exit ticket.
+   */
+  int64_t* trace;
+  int32_t trace_blocks;
+  int32_t trace_cap;
 } moe_decode_debug;
 
 typedef struct moe_decode_handle moe_decode_handle;

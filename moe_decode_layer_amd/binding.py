@@ -62,6 +62,9 @@ class moe_decode_debug(ctypes.Structure):
         ("pair_rank", ctypes.c_void_p),
         ("expert_count", ctypes.c_void_p),
         ("logits", ctypes.c_void_p),
+        ("trace", ctypes.c_void_p),
+        ("trace_blocks", ctypes.c_int32),
+        ("trace_cap", ctypes.c_int32),
     ]
 
 
@@ -171,9 +174,12 @@ class MoeDecode:
             T = x.shape[0]
         dbg = None
         if debug:
+            tr = debug.get("trace")
             dbg = moe_decode_debug(_ptr(debug.get("topk_idx")), _ptr(debug.get("topk_w")),
                                    _ptr(debug.get("pair_rank")), _ptr(debug.get("expert_count")),
-                                   _ptr(debug.get("logits")))
+                                   _ptr(debug.get("logits")), _ptr(tr),
+                                   0 if tr is None else tr.shape[0],
+                                   0 if tr is None else tr.shape[1] - 1)
         s = stream if stream is not None else torch.cuda.current_stream()
         st = moe_decode_run(self.handle, x.data_ptr(), T, y.data_ptr(), dbg, s.cuda_stream)
         if st != MOE_OK:

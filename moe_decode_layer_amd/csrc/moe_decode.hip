@@ -1,46 +1,52 @@
 // Persistent MoE decode layer for MI355X (gfx950, CDNA4) behind the C ABI of
 // include/moe_decode.h.
 //
-// One launch runs the whole layer.  Workgroups stay resident and pull work
-// items from one ticket counter (an in-kernel queue); an item that needs the
-// result of earlier items waits on a counter those items bump when done.  The
-// idea of blocks that stay resident, hand ready results on through tagged
-// buffers and keep at it across stages is the one described in "FlyDSL Mono
+// One launch runs the whole layer.  Every workgroup stays resident and walks
+// its own share of one global list of work items (item i belongs to
+// workgroup i mod G, taken in order); an item that needs earlier results
+// waits on a counter the producing items bump when done.  Blocks that stay
+// resident across stages, pass ready results on through tagged buffers and
+// load weights while earlier stages still compute follow "FlyDSL Mono
 // Kernels for High-Interactivity LLM Serving in ATOM" (sections "What FlyDSL
 // Provides" and "MiniMax-M3: Connecting Attention and Experts"); the deadline
 // on every wait follows "SGLang's Low-Latency Mode Boosts DeepSeek-V4.1-Flash
 // Speed by 1.56x on AMD" (section "AMD keeps the layer resident").
 //
-// Tickets, in this order (an item only ever waits on items with smaller
-// tickets, which were taken by workgroups already running, so the queue makes
-// progress whether or not every workgroup is resident):
-//   router   : logits for 4 experts x 8 rows
-//   shared gate/up (no routing needed), 16 weight rows (8 gate + 8 up)
-//   top-k    : 4 rows, one per wave           -- waits: all router items
-//   shared down, 128 output rows              -- waits: shared gate/up
-//   routed gate/up, 16 weight rows per item   -- waits: all top-k items
-//   routed down, 128 output rows per item     -- waits: that expert's gate/up
+// Item list, in this order (an item only waits on items earlier in the list;
+// each workgroup takes its items in list order and all workgroups are
+// resident together, so every wait is eventually satisfied -- and if they
+// were not all resident, the deadline turns the stall into an error):
+//   router          : logits of one expert for up to 8 rows
+//   shared gate/up  : 16 weight rows (8 gate + 8 up) of the shared expert
+//   top-k           : 4 rows, one per wave (only for batches of more than 32
+//                     rows; smaller batches select top-k in every workgroup)
+//   routed gate/up  : 16 weight rows of one routed expert      -- waits: routing
+//   shared down     : 128 output rows of the shared expert     -- waits: its gate/up
+//   routed down     : 128 output rows of one routed expert     -- waits: its gate/up
 // The weighted combine runs in whichever down item arrives last for a
-// (row, 128-column chunk).
+// (row, 128-column chunk).  A gate/up or down item covers up to 64 rows of
+// its expert (four 16-row MFMA blocks); experts with more rows get one item
+// per 64 rows.
 //
 // Expert weights are re-laid out once, at create time, into 1 KiB tiles of
 // 16 weight rows x 64 K: lane l of a wave reads bytes [16 l, 16 l + 16) of a
-// tile, i.e. every wave-wide load is one contiguous KiB.  Lane l = (n, kq),
-// n = l % 16, kq = l / 16, holds row n's K elements [8 kq, 8 kq + 8) of the
-// tile's first 32-element group and the same of its second group, which is
-// exactly the B-operand layout of v_mfma_f32_16x16x32_bf16 for one group per
-// instruction.  So one MFMA covers exactly one scale group: its fp32 result is
-// multiplied by that group's scale and accumulated.  FP8 e4m3fn -> bf16 is
-// exact (v_cvt_scalef32_pk_bf16_fp8 with scale 1), bf16 x bf16 products are
-// exact in fp32, so the only rounding is fp32 accumulation.  The activation
-// tile (up to 16 rows) is the A operand; rows beyond the expert's row count
-// are zero.
+// tile, so every wave-wide weight load is one contiguous KiB.  Lane l =
+// (n, kq), n = l % 16, kq = l / 16, holds row n's K elements [8 kq, 8 kq + 8)
+// of the tile's first 32-element group and the same of its second group:
+// exactly the B operand of v_mfma_f32_16x16x32_bf16, one scale group per
+// instruction.  The fp32 result of each MFMA is multiplied by its group's
+// scale and accumulated.  FP8 e4m3fn -> bf16 is exact
+// (v_cvt_scalef32_pk_bf16_fp8 with scale 1) and bf16 x bf16 products are
+// exact in fp32, so the only rounding before the declared bf16 points is
+// fp32 accumulation.  Activation rows are the A operand; rows past the
+// expert's row count are zero.
 #include <hip/hip_runtime.h>
 
 #include <limits.h>
 #include <stdint.h>
 #include <string.h>
 
+#include <algorithm>
 #include <mutex>
 #include <new>
 
@@ -64,20 +70,35 @@ constexpr int kGroup = 32;
 constexpr int kMaxTokens = 512;
 constexpr int kMaxExperts = 256;
 constexpr int kMaxTopK = 16;
+constexpr int kLocalTopkRows = 32;          // at most this many rows: top-k in every workgroup
+constexpr size_t kXsMaxBytes = 64 * 1024;   // x kept in LDS up to this size
+constexpr int kHsMaxI = 1024;               // h staged in LDS up to this intermediate width
+constexpr int kFullTiles = 16;              // tiles per wave of the fully unrolled items (H 4096, I 512)
 
-// counter block
-constexpr int kCtrTicket = 0;
-constexpr int kCtrRouterDone = 1;
-constexpr int kCtrTopkDone = 2;
-constexpr int kCtrExit = 3;
-constexpr int kCtrStatus = 4;
-constexpr int kCtrHReady = 8;               // [E+S]
+// counter block (int32 words)
+constexpr int kCtrRouterDone = 0;
+constexpr int kCtrTopkDone = 16;
+constexpr int kCtrExit = 32;
+constexpr int kCtrStatus = 48;
+constexpr int kCtrHReady = 64;              // [E+S] (E+S <= 257)
+// "go" flags raised once by the last producer and polled by many workgroups:
+// kGoLines copies, 1 KiB apart, so the pollers spread over memory channels
+constexpr int kGoLines = 64;
+constexpr int kGoStride = 256;              // words
+constexpr int kCtrRouterGo = 512;
+constexpr int kCtrTopkGo = kCtrRouterGo + kGoLines * kGoStride;
+constexpr int kCtrHead = kCtrTopkGo + kGoLines * kGoStride;
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+#define GLOBAL __attribute__((address_space(1)))
+#define CONSTANT __attribute__((address_space(4)))
+#define SHARED __attribute__((address_space(3)))
 
 struct Params {
   int T, H, E, K, S, I;
@@ -92,7 +113,7 @@ struct Params {
   const float* s2p;    // [E+S][H/16][I/64][16][2]
   // workspace
   float* logits;       // [T][E]
-  int* topk_idx;       // [T][K]
+  int* topk_idx;       // [T][K]  (distributed top-k only)
   float* topk_w;       // [T][K]
   uint16_t* h_scr;     // [T*K + T*S][I] bf16, rows grouped by expert
   float* o_scr;        // [T*K + T*S][H]
@@ -104,9 +125,11 @@ struct Params {
   int* dbg_rank;
   int* dbg_count;
   float* dbg_logits;
+  long long* trace;    // [trace_blocks][1 + trace_cap][4]
+  int trace_blocks, trace_cap;
   // derived
   long long deadline_ticks;  // wall-clock ticks (100 MHz)
-  int n_eb;            // router expert blocks: ceil(E/4)
+  int local_topk;      // 1: every workgroup selects top-k itself
   int n_rb13;          // gate/up row blocks per expert: I/8
   int n_q13;           // tiles along H: H/64
   int n_rb2;           // down row blocks: H/16
@@ -114,13 +137,21 @@ struct Params {
   int n_rg;            // down row groups: ceil(H/128)
   int n_mr_sh;         // shared M-ranges: ceil(T/64) (0 without a shared expert)
   int nch;             // 64-row chunks: ceil(T/64)
-  // ticket ranges [start, end)
-  int t_router_end, t_sgu_end, t_topk_end, t_sdn_end;
+  // item list boundaries
   int n_router, n_topk;
+  int i_router_end, i_sgu_end, i_topk_end;
+  int n_sdn;           // shared down items
   // LDS offsets (bytes)
-  int lds_bm, lds_cp, lds_cnt, lds_base, lds_nmrb, lds_mrlist, lds_rows, lds_red, lds_comb, lds_misc;
+  int lds_bm, lds_cp, lds_cnt, lds_base, lds_nmrb, lds_mrlist, lds_rows, lds_tki, lds_tkw,
+      lds_red, lds_misc, lds_tks, lds_xs, lds_hs, lds_lg;
   int lds_bytes;
+  int xs_stride;       // x rows in LDS (bf16 elements per row), 0 when x stays in global memory
+  int hs_stride;       // h rows staged in LDS for a down item, 0 when read from global memory
 };
+// The kernel reads its parameters in place, from the constant kernel-argument
+// segment, so the compiler can reload a field with a scalar load instead of
+// keeping every field resident in scalar registers.
+typedef const CONSTANT Params KParams;
 
 // ----------------------------------------------------------------------------
 // Small device helpers
@@ -155,83 +186,176 @@ __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, zero, 0, 0, 0);
 }
 
-__device__ __forceinline__ u32x4 load_nt(const u32x4* p) { return __builtin_nontemporal_load(p); }
+// Global-memory loads (explicit address space: no flat instructions).
+template <typename T>
+__device__ __forceinline__ T ld(const T* p) { return *(const GLOBAL T*)p; }
+__device__ __forceinline__ u32x4 ld_stream(const u32x4* p) {
+  return __builtin_nontemporal_load((const GLOBAL u32x4*)p);
+}
+template <typename T>
+__device__ __forceinline__ void st(T* p, T v) { *(GLOBAL T*)p = v; }
 
+// DPP lane exchange within 16-lane rows (VALU, no LDS round trip).
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, true);
+}
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141; // lane i <- 7 - i within 8
+constexpr int kDppMirror = 0x140;     // lane i <- 15 - i within 16
+constexpr int kDppRowShl1 = 0x101;    // lane i <- i + 1
+constexpr int kDppRowRor8 = 0x128;    // lane i <- (i + 8) mod 16
+
+// Sum over the 64 lanes, the same value in every lane, in a fixed order.
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
+  v += dpp<kDppXor1>(v);
+  v += dpp<kDppXor2>(v);
+  v += dpp<kDppHalfMirror>(v);
+  v += dpp<kDppMirror>(v);
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return (r0 + r1) + (r2 + r3);
 }
 
 __device__ __forceinline__ int atomic_add_agent(int* p, int v) {
-  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return __hip_atomic_fetch_add((GLOBAL int*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ int load_agent(int* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return __hip_atomic_load((GLOBAL int*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ void store_agent(int* p, int v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store((GLOBAL int*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ void fence_release_agent() { __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent"); }
-__device__ __forceinline__ void fence_acquire_agent() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
 
-// Thread 0 of the workgroup publishes "one more item done" on *ctr after
-// every thread's stores of the item (barrier first, then an agent-scope
-// release, then the increment).
-__device__ void publish_done(int* ctr) {
+// Data handed from one workgroup to another (logits, top-k, h, o) is written
+// and read with device-scope relaxed atomic stores and loads: they go to the
+// device coherence point instead of a workgroup's L1 or its XCD's L2, so no
+// cache-wide write-back or invalidate is ever needed.  A producer waits until
+// its stores are acknowledged (s_waitcnt) before it bumps a counter; a
+// consumer reads the data only after it has seen the counter.
+__device__ __forceinline__ void st_coh(float* p, float v) {
+  __hip_atomic_store((GLOBAL float*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_coh(int* p, int v) {
+  __hip_atomic_store((GLOBAL int*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_coh(uint32_t* p, uint32_t v) {
+  __hip_atomic_store((GLOBAL uint32_t*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_coh(const float* p) {
+  return __hip_atomic_load((GLOBAL float*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int ld_coh(const int* p) {
+  return __hip_atomic_load((GLOBAL int*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ u32x4 ld_coh16(const void* p) {
+  const uint64_t a = __hip_atomic_load((GLOBAL uint64_t*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const uint64_t b = __hip_atomic_load((GLOBAL uint64_t*)p + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return (u32x4){(uint32_t)a, (uint32_t)(a >> 32), (uint32_t)b, (uint32_t)(b >> 32)};
+}
+// Wait until this wave's outstanding memory operations are acknowledged.
+__device__ __forceinline__ void wait_stores() { __builtin_amdgcn_s_waitcnt(0); }
+
+// The copy of a go flag this workgroup polls.
+__device__ __forceinline__ int* go_flag(int* base) { return base + (blockIdx.x % kGoLines) * kGoStride; }
+
+// Thread 0 publishes "one more item done" on *ctr once every wave's stores of
+// the item are acknowledged.  With a flag, the last of `target` items also
+// raises the flag (one write that many waiters poll instead of the contended
+// counter).
+__device__ void publish_done(int* ctr, int target = 0, int* flag = nullptr) {
+  wait_stores();
   __syncthreads();
   if (threadIdx.x == 0) {
-    fence_release_agent();
-    atomic_add_agent(ctr, 1);
+    const int old = atomic_add_agent(ctr, 1);
+    if (flag && old == target - 1)
+      for (int i = 0; i < kGoLines; ++i) store_agent(flag + i * kGoStride, 1);
   }
 }
 
-// Workgroup-wide wait until *ctr >= target.  Thread 0 spins with a deadline;
-// the result is broadcast through LDS.  false: deadline passed or another
-// workgroup already reported an error -- the caller stops taking work.
-__device__ bool wait_geq(const Params& p, int* ctr, int target, int* lds_flag) {
+// Workgroup-wide wait until *ctr >= target.  Thread 0 spins (with a pause
+// that grows to ~0.4 us) under a deadline; the result is broadcast through
+// LDS, and the barrier orders every wave's later (coherent) loads after it.
+// false: deadline passed or another workgroup reported an error.
+__device__ bool wait_geq(KParams& p, int* ctr, int target, SHARED int* lds_flag) {
   if (threadIdx.x == 0) {
     int ok = 1;
     if (load_agent(ctr) < target) {
       const long long t_end = (long long)wall_clock64() + p.deadline_ticks;
+      int spins = 0;
       while (true) {
         if (load_agent(ctr) >= target) break;
-        if (load_agent(p.ctr + kCtrStatus) != 0) { ok = 0; break; }
+        if ((spins & 7) == 7 && load_agent(p.ctr + kCtrStatus) != 0) { ok = 0; break; }
         if ((long long)wall_clock64() > t_end) {
           int expected = 0;
-          __hip_atomic_compare_exchange_strong(p.ctr + kCtrStatus, &expected, MOE_ERR_TIMEOUT,
+          __hip_atomic_compare_exchange_strong((GLOBAL int*)(p.ctr + kCtrStatus), &expected, MOE_ERR_TIMEOUT,
                                                __ATOMIC_RELAXED, __ATOMIC_RELAXED,
                                                __HIP_MEMORY_SCOPE_AGENT);
           ok = 0;
           break;
         }
-        __builtin_amdgcn_s_sleep(2);
+        __builtin_amdgcn_s_sleep(8);
+        ++spins;
       }
     }
-    if (ok) fence_acquire_agent();
     *lds_flag = ok;
   }
   __syncthreads();
-  int ok = *lds_flag;
+  const int ok = *lds_flag;
   __syncthreads();
   return ok != 0;
 }
 
+// Copy n 16-byte (or 8-byte) words with the whole workgroup, kBatch loads in
+// flight per thread before any LDS write, so a copy costs about one memory
+// round trip per kBatch * kThreads words instead of one per kThreads.
+constexpr int kBatch = 8;
+template <typename Word, typename LoadFn, typename StoreFn>
+__device__ __forceinline__ void batched_copy(int n, LoadFn load, StoreFn store) {
+  for (int i0 = threadIdx.x; i0 < n; i0 += kBatch * kThreads) {
+    Word v[kBatch];
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b) {
+      const int i = i0 + b * kThreads;
+      if (i < n) v[b] = load(i);
+    }
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b) {
+      const int i = i0 + b * kThreads;
+      if (i < n) store(i, v[b]);
+    }
+  }
+}
+
 // Block-wide exclusive prefix sum of one int per thread (kThreads values).
-__device__ int block_exclusive_scan(int v, int* lds4, int* total) {
+// Within a wave: Kogge-Stone over 16-lane rows with DPP row shifts, then the
+// row totals carried across rows with row broadcasts.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ int dpp_add_src(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, ROWS, 0xF, false);
+}
+__device__ int block_exclusive_scan(int v, SHARED int* lds4, int* total) {
   const int lane = lane_id(), w = wave_id();
   int incl = v;
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    int n = __shfl_up(incl, o, kWave);
-    if (lane >= o) incl += n;
-  }
+  incl += __builtin_amdgcn_update_dpp(0, incl, 0x111, 0xF, 0xF, true);   // row_shr:1
+  incl += __builtin_amdgcn_update_dpp(0, incl, 0x112, 0xF, 0xF, true);   // row_shr:2
+  incl += __builtin_amdgcn_update_dpp(0, incl, 0x114, 0xF, 0xF, true);   // row_shr:4
+  incl += __builtin_amdgcn_update_dpp(0, incl, 0x118, 0xF, 0xF, true);   // row_shr:8
+  incl += dpp_add_src<0x142, 0xA>(incl);                                 // row_bcast:15
+  incl += dpp_add_src<0x143, 0xC>(incl);                                 // row_bcast:31
   if (lane == kWave - 1) lds4[w] = incl;
   __syncthreads();
   int off = 0, tot = 0;
 #pragma unroll
   for (int i = 0; i < kWaves; ++i) {
-    int s = lds4[i];
+    const int s = lds4[i];
     if (i < w) off += s;
     tot += s;
   }
@@ -244,30 +368,40 @@ __device__ int block_exclusive_scan(int v, int* lds4, int* total) {
 // Workgroup view of the routing (LDS), built once per workgroup
 // ----------------------------------------------------------------------------
 struct Lds {
-  unsigned long long* bm;  // [E][nch] row bitmap of each expert
-  int* cp;                 // [E][nch] rows of the expert in earlier chunks
-  int* cnt;                // [E] rows per expert
-  int* base;               // [E] first scratch row of the expert
-  int* nmrb;               // [E+1] prefix of M-ranges per expert
-  int* mrlist;             // [n_mr] expert of each routed M-range
-  int16_t* rows;           // [T*K] row -> token, grouped by expert
-  float* red;              // [kWaves][4][64][4] partial sums
-  int* comb;               // combine staging
-  int* misc;               // [0] ticket, [1] flag, [2] n_mr, [3..7) scan scratch, [8] n_comb
+  SHARED unsigned long long* bm;  // [E][nch] row bitmap of each expert
+  SHARED int* cp;                 // [E][nch] rows of the expert in earlier chunks
+  SHARED int* cnt;                // [E] rows per expert
+  SHARED int* base;               // [E] first scratch row of the expert
+  SHARED int* nmrb;               // [E+1] prefix of M-ranges per expert
+  SHARED int* mrlist;             // [n_mr] expert of each routed M-range
+  SHARED int16_t* rows;           // [T*K] scratch row -> token, grouped by expert
+  SHARED int16_t* tki;            // [T][K] selected experts
+  SHARED float* tkw;              // [T][K] their weights
+  SHARED float* red;              // partial sums of the 4 waves
+  SHARED int* misc;               // [0] n_mr, [1] flag, [3..7) scan scratch
+  SHARED uint32_t* tks;           // [kWaves][64] top-k scratch of each wave
+  SHARED uint16_t* xs;            // [T][xs_stride] the layer input (small batches)
+  SHARED uint16_t* hs;            // [16][hs_stride] h rows of the current down item
+  SHARED float* lg;               // [T][E] router logits (small batches)
 };
 
-__device__ Lds lds_view(const Params& p, char* smem) {
+__device__ Lds lds_view(KParams& p, SHARED char* smem) {
   Lds L;
-  L.bm = (unsigned long long*)(smem + p.lds_bm);
-  L.cp = (int*)(smem + p.lds_cp);
-  L.cnt = (int*)(smem + p.lds_cnt);
-  L.base = (int*)(smem + p.lds_base);
-  L.nmrb = (int*)(smem + p.lds_nmrb);
-  L.mrlist = (int*)(smem + p.lds_mrlist);
-  L.rows = (int16_t*)(smem + p.lds_rows);
-  L.red = (float*)(smem + p.lds_red);
-  L.comb = (int*)(smem + p.lds_comb);
-  L.misc = (int*)(smem + p.lds_misc);
+  L.bm = (SHARED unsigned long long*)(smem + p.lds_bm);
+  L.cp = (SHARED int*)(smem + p.lds_cp);
+  L.cnt = (SHARED int*)(smem + p.lds_cnt);
+  L.base = (SHARED int*)(smem + p.lds_base);
+  L.nmrb = (SHARED int*)(smem + p.lds_nmrb);
+  L.mrlist = (SHARED int*)(smem + p.lds_mrlist);
+  L.rows = (SHARED int16_t*)(smem + p.lds_rows);
+  L.tki = (SHARED int16_t*)(smem + p.lds_tki);
+  L.tkw = (SHARED float*)(smem + p.lds_tkw);
+  L.red = (SHARED float*)(smem + p.lds_red);
+  L.misc = (SHARED int*)(smem + p.lds_misc);
+  L.tks = (SHARED uint32_t*)(smem + p.lds_tks);
+  L.xs = (SHARED uint16_t*)(smem + p.lds_xs);
+  L.hs = (SHARED uint16_t*)(smem + p.lds_hs);
+  L.lg = (SHARED float*)(smem + p.lds_lg);
   return L;
 }
 
@@ -276,18 +410,18 @@ __device__ Lds lds_view(const Params& p, char* smem) {
 // Every pair (t, k) sets bit t of expert idx[t][k]'s bitmap; an expert's
 // count is the popcount of its bitmap; a pair's rank is the popcount of the
 // expert's bits below t.  Row r of expert e lives at scratch row base[e] + r.
-__device__ void build_placement(const Params& p, const Lds& L) {
+__device__ __forceinline__ void build_placement(KParams& p, const Lds& L) {
   const int tid = threadIdx.x;
   const int E = p.E, K = p.K, T = p.T, nch = p.nch;
   for (int i = tid; i < E * nch; i += kThreads) L.bm[i] = 0ull;
   __syncthreads();
   for (int i = tid; i < T * K; i += kThreads) {
     const int t = i / K;
-    const int e = p.topk_idx[i];
-    atomicOr(&L.bm[e * nch + (t >> 6)], 1ull << (t & 63));
+    const int e = L.tki[i];
+    __hip_atomic_fetch_or(&L.bm[e * nch + (t >> 6)], 1ull << (t & 63), __ATOMIC_RELAXED,
+                          __HIP_MEMORY_SCOPE_WORKGROUP);
   }
   __syncthreads();
-  // counts, chunk prefixes, expert bases and M-range prefixes (E <= kThreads)
   int c = 0, nmr = 0;
   if (tid < E) {
     for (int ch = 0; ch < nch; ++ch) {
@@ -307,12 +441,12 @@ __device__ void build_placement(const Params& p, const Lds& L) {
   }
   if (tid == 0) {
     L.nmrb[E] = tot_mr;
-    L.misc[2] = tot_mr;
+    L.misc[0] = tot_mr;
   }
   __syncthreads();
   for (int i = tid; i < T * K; i += kThreads) {
     const int t = i / K;
-    const int e = p.topk_idx[i];
+    const int e = L.tki[i];
     const unsigned long long below = L.bm[e * nch + (t >> 6)] & ((1ull << (t & 63)) - 1ull);
     const int rank = L.cp[e * nch + (t >> 6)] + __popcll(below);
     L.rows[L.base[e] + rank] = (int16_t)t;
@@ -320,453 +454,867 @@ __device__ void build_placement(const Params& p, const Lds& L) {
   __syncthreads();
 }
 
-// Rank of row t among expert e's rows -- valid after build_placement.
-__device__ __forceinline__ int pair_rank(const Params& p, const Lds& L, int t, int e) {
+__device__ __forceinline__ int pair_rank(KParams& p, const Lds& L, int t, int e) {
   const unsigned long long below = L.bm[e * p.nch + (t >> 6)] & ((1ull << (t & 63)) - 1ull);
   return L.cp[e * p.nch + (t >> 6)] + __popcll(below);
 }
-__device__ __forceinline__ int pair_row(const Params& p, const Lds& L, int t, int e) {
-  return L.base[e] + pair_rank(p, L, t, e);
-}
 
-// Optional debug copies of the placement (written by one workgroup).
-__device__ void write_placement_debug(const Params& p, const Lds& L) {
+// Optional debug copies of routing and placement (written by workgroup 0).
+__device__ __forceinline__ void write_routing_debug(KParams& p, const Lds& L) {
+  for (int i = threadIdx.x; i < p.T * p.K; i += kThreads) {
+    if (p.dbg_idx) st(p.dbg_idx + i, (int)L.tki[i]);
+    if (p.dbg_w) st(p.dbg_w + i, L.tkw[i]);
+    if (p.dbg_rank) st(p.dbg_rank + i, pair_rank(p, L, i / p.K, L.tki[i]));
+  }
   if (p.dbg_count)
-    for (int e = threadIdx.x; e < p.E; e += kThreads) p.dbg_count[e] = L.cnt[e];
-  if (p.dbg_rank)
-    for (int i = threadIdx.x; i < p.T * p.K; i += kThreads)
-      p.dbg_rank[i] = pair_rank(p, L, i / p.K, p.topk_idx[i]);
+    for (int e = threadIdx.x; e < p.E; e += kThreads) st(p.dbg_count + e, L.cnt[e]);
 }
 
 // ----------------------------------------------------------------------------
-// Router: logits for 4 experts (one per wave) x up to 8 rows.
+// Router: logits of expert e for up to 8 rows; the 4 waves split H.  x comes
+// from LDS when the batch is small enough to keep it there.
 // ----------------------------------------------------------------------------
-__device__ void router_item(const Params& p, int item) {
+__device__ __forceinline__ void router_item(KParams& p, const Lds& L, int item) {
   const int w = wave_id(), lane = lane_id();
-  const int e = (item % p.n_eb) * kWaves + w;
-  const int t0 = (item / p.n_eb) * kRouterRows;
+  const int e = item % p.E;
+  const int t0 = (item / p.E) * kRouterRows;
   const int nt = min(kRouterRows, p.T - t0);
-  if (e < p.E) {
-    float acc[kRouterRows];
+  const int nc = p.H / 4;                      // 4-element chunks
+  const int c_lo = w * (nc / kWaves), c_hi = c_lo + nc / kWaves;
+  float acc[kRouterRows];
 #pragma unroll
-    for (int j = 0; j < kRouterRows; ++j) acc[j] = 0.f;
-    const float4* wr = (const float4*)(p.router_w + (size_t)e * p.H);
-    const int n4 = p.H / 4;
-    for (int c = lane; c < n4; c += kWave) {
-      const float4 wv = wr[c];
+  for (int j = 0; j < kRouterRows; ++j) acc[j] = 0.f;
+  const f32x4* wr = (const f32x4*)(p.router_w + (size_t)e * p.H);
+  const bool xl = false;                       // x in LDS is staged after the router
+  const u32x2* xg[kRouterRows];                // rows past nt reread the last row
+  const SHARED u32x2* xsh[kRouterRows];
 #pragma unroll
-      for (int j = 0; j < kRouterRows; ++j) {
-        if (j < nt) {
-          const u32x2 xv = *(const u32x2*)(p.x + (size_t)(t0 + j) * p.H + 4 * c);
-          acc[j] += wv.x * bf16_to_f32(xv.x & 0xffffu) + wv.y * bf16_to_f32(xv.x >> 16) +
-                    wv.z * bf16_to_f32(xv.y & 0xffffu) + wv.w * bf16_to_f32(xv.y >> 16);
-        }
-      }
-    }
-    const float b = p.router_b ? p.router_b[e] : 0.f;
+  for (int j = 0; j < kRouterRows; ++j) {
+    const int t = t0 + min(j, nt - 1);
+    xg[j] = (const u32x2*)(p.x + (size_t)t * p.H);
+    xsh[j] = (const SHARED u32x2*)(L.xs + (size_t)t * p.xs_stride);
+  }
+#pragma unroll 4
+  for (int c = c_lo + lane; c < c_hi; c += kWave) {
+    const f32x4 wv = ld(wr + c);
 #pragma unroll
     for (int j = 0; j < kRouterRows; ++j) {
-      if (j < nt) {
-        const float s = wave_sum(acc[j]) + b;
-        if (lane == 0) {
-          p.logits[(size_t)(t0 + j) * p.E + e] = s;
-          if (p.dbg_logits) p.dbg_logits[(size_t)(t0 + j) * p.E + e] = s;
-        }
+      const u32x2 xv = xl ? xsh[j][c] : ld(xg[j] + c);
+      acc[j] += wv.x * bf16_to_f32(xv.x & 0xffffu) + wv.y * bf16_to_f32(xv.x >> 16) +
+                wv.z * bf16_to_f32(xv.y & 0xffffu) + wv.w * bf16_to_f32(xv.y >> 16);
+    }
+  }
+  SHARED float* part = L.red;                  // [kWaves][8]
+#pragma unroll
+  for (int j = 0; j < kRouterRows; ++j) {
+    const float s = wave_sum(acc[j]);
+    if (lane == 0) part[w * kRouterRows + j] = s;
+  }
+  __syncthreads();
+  if (threadIdx.x < nt) {
+    const int j = threadIdx.x;
+    float s = part[j];
+#pragma unroll
+    for (int ww = 1; ww < kWaves; ++ww) s += part[ww * kRouterRows + j];
+    s += p.router_b ? ld(p.router_b + e) : 0.f;
+    st_coh(p.logits + (size_t)(t0 + j) * p.E + e, s);
+    if (p.dbg_logits) st(p.dbg_logits + (size_t)(t0 + j) * p.E + e, s);
+  }
+}
+
+// ----------------------------------------------------------------------------
+// Top-k of one row (one wave).  Lane l holds experts l, l+64, l+128, l+192 as
+// order-preserving unsigned keys of their logits (ranking by logit equals
+// ranking by sigmoid score).  A 32-step radix select over ballots finds the
+// K-th largest key; every larger key is selected, then the lowest-id keys
+// equal to it.  The K picks are ordered by (key desc, id asc) through LDS.
+// Weights: sigmoid of the selected logits over their sum.
+// ----------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t order_ukey(float v) {
+  // NaN maps to 1, just above absent experts (0), so it never displaces a score
+  if (v != v) return 1u;
+  const int b = __float_as_int(v);
+  const int k = b >= 0 ? b : (b ^ 0x7fffffff);
+  return (uint32_t)k ^ 0x80000000u;
+}
+__device__ __forceinline__ float ukey_value(uint32_t u) {
+  const int k = (int)(u ^ 0x80000000u);
+  return __int_as_float(k >= 0 ? k : (k ^ 0x7fffffff));
+}
+
+// Top-k of NR rows at once in one wave (their radix searches interleave).
+// Row r's logits come from LDS (lg, [T][E]) or, with lg == nullptr, from
+// global memory.  Returns, in lanes k < K, row r's k-th expert and weight.
+template <int NR>
+__device__ __forceinline__ void topk_rows(KParams& p, const SHARED float* lg, const int (&t)[NR],
+                                          int (&out_e)[NR], float (&out_w)[NR]) {
+  const int lane = lane_id();
+  const int K = p.K;
+  uint32_t uk[NR][4];
+#pragma unroll
+  for (int r = 0; r < NR; ++r)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = lane + kWave * j;
+      const float v = e < p.E ? (lg ? lg[t[r] * p.E + e] : ld_coh(p.logits + (size_t)t[r] * p.E + e)) : 0.f;
+      uk[r][j] = e < p.E ? order_ukey(v) : 0u;
+    }
+  // radix select: thr[r] = the K-th largest key of row r
+  uint32_t thr[NR];
+#pragma unroll
+  for (int r = 0; r < NR; ++r) thr[r] = 0;
+  for (int bit = 31; bit >= 0; --bit) {
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      const uint32_t cand = thr[r] | (1u << bit);
+      int c = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) c += __popcll(__ballot(uk[r][j] >= cand));
+      thr[r] = c >= K ? cand : thr[r];
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    // selection: every key above the threshold, then the lowest ids equal to it
+    int need = K;
+    unsigned long long sel[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      sel[j] = __ballot(uk[r][j] > thr[r]);
+      need -= __popcll(sel[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      unsigned long long m = __ballot(uk[r][j] == thr[r]);
+      while (need > 0 && m) {
+        const unsigned long long low = m & (~m + 1ull);
+        sel[j] |= low;
+        m ^= low;
+        --need;
       }
     }
+    // move the K picks to lanes 0..K-1 (in id order): pick i of the wave goes
+    // to lane i through a readlane from its owner
+    uint32_t my_k = 0, my_e = 0;
+    int base = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      unsigned long long m = sel[j];
+      while (m) {
+        const int src = __ffsll((long long)m) - 1;
+        m &= m - 1;
+        const uint32_t kk = (uint32_t)__builtin_amdgcn_readlane((int)uk[r][j], src);
+        if (lane == base) { my_k = kk; my_e = (uint32_t)(src + kWave * j); }
+        ++base;
+      }
+    }
+    // rank among the picks: key descending, id ascending
+    int rank = 0;
+#pragma unroll
+    for (int i = 0; i < kMaxTopK; ++i) {
+      if (i < K) {
+        const uint32_t ki = (uint32_t)__builtin_amdgcn_readlane((int)my_k, i);
+        const uint32_t ei = (uint32_t)__builtin_amdgcn_readlane((int)my_e, i);
+        rank += (ki > my_k) || (ki == my_k && ei < my_e);
+      }
+    }
+    // lane k takes the pick of rank k
+    uint32_t out_k = 0, oe = 0;
+#pragma unroll
+    for (int i = 0; i < kMaxTopK; ++i) {
+      if (i < K) {
+        const int ri = __builtin_amdgcn_readlane(rank, i);
+        const uint32_t ki = (uint32_t)__builtin_amdgcn_readlane((int)my_k, i);
+        const uint32_t ei = (uint32_t)__builtin_amdgcn_readlane((int)my_e, i);
+        if (lane == ri) { out_k = ki; oe = ei; }
+      }
+    }
+    const float s = lane < K ? 1.0f / (1.0f + __expf(-ukey_value(out_k))) : 0.f;
+    const float sum = wave_sum(s);
+    out_e[r] = (int)oe;
+    out_w[r] = s / sum;
   }
 }
 
-// ----------------------------------------------------------------------------
-// Top-k: one row per wave.  Lane l holds experts l, l+64, l+128, l+192.
-// Ranking by logit equals ranking by sigmoid score (monotone); ties go to the
-// lower expert id.  Weights: sigmoid of the selected logits over their sum.
-// ----------------------------------------------------------------------------
-__device__ __forceinline__ int order_key(float v) {
-  // order-preserving map of a float to an int; NaN sorts just above the
-  // "unavailable" key so it can never displace a real score
-  const int b = __float_as_int(v);
-  if (v != v) return INT_MIN + 1;
-  return b >= 0 ? b : (b ^ 0x7fffffff);
+// One row (distributed top-k items).
+__device__ __forceinline__ void topk_row(KParams& p, const Lds& L, int t, int* out_e, float* out_w) {
+  const int tr[1] = {t};
+  int e[1];
+  float w[1];
+  topk_rows<1>(p, nullptr, tr, e, w);
+  *out_e = e[0];
+  *out_w = w[0];
 }
 
-__device__ void topk_item(const Params& p, int item) {
-  const int w = wave_id(), lane = lane_id();
-  const int t = item * kWaves + w;
+// Distributed top-k item: rows 4 item .. 4 item + 3, one per wave, to global.
+__device__ __forceinline__ void topk_item(KParams& p, const Lds& L, int item) {
+  const int t = item * kWaves + wave_id();
   if (t >= p.T) return;
-  float v[4];
-  int key[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int e = lane + kWave * j;
-    v[j] = e < p.E ? p.logits[(size_t)t * p.E + e] : 0.f;
-    key[j] = e < p.E ? order_key(v[j]) : INT_MIN;   // INT_MIN: not selectable
+  int e;
+  float wk;
+  topk_row(p, L, t, &e, &wk);
+  if (lane_id() < p.K) {
+    st_coh(p.topk_idx + t * p.K + lane_id(), e);
+    st_coh(p.topk_w + t * p.K + lane_id(), wk);
   }
-  int my_idx = 0;
-  float my_logit = 0.f;
-  for (int k = 0; k < p.K; ++k) {
-    int bk = key[0], be = lane;
-    float bv = v[0];
+}
+
+// A down item's h rows (nrows x I bf16, written by other workgroups) into LDS.
+__device__ __forceinline__ void stage_h_rows(KParams& p, const Lds& L, int row0, int nrows) {
+  const int per_row = p.I / 4;                // 8-byte words per row
+  batched_copy<uint64_t>(
+      nrows * per_row,
+      [&](int i) {
+        return __hip_atomic_load((GLOBAL uint64_t*)(p.h_scr + (size_t)(row0 + i / per_row) * p.I) + i % per_row,
+                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      },
+      [&](int i, uint64_t v) { *(SHARED uint64_t*)(L.hs + (size_t)(i / per_row) * p.hs_stride + 4 * (i % per_row)) = v; });
+}
+
+// ----------------------------------------------------------------------------
+// Down-item epilogue of one wave: after its o rows are stored, the wave counts
+// itself in for each of its rows t at (t, row group rg); the wave that
+// completes a (t, rg) -- all K+S expert outputs times the waves covering the
+// group -- combines it: y[t][rg*128 .. +128) = bf16(o_shared + sum_k w_k o_k),
+// summed in that fixed order.
+// ----------------------------------------------------------------------------
+__device__ __forceinline__ void wave_arrive_combine(KParams& p, const Lds& L, int sbase, int r0,
+                                                    int nrows, int rg, bool shared) {
+  const int lane = lane_id();
+  const int K = p.K;
+  const int c0 = rg * kDownRows;
+  const int nc = min(kDownRows, p.H - c0);
+  const int waves_in_group = min(kWaves, (nc + 2 * kTileRows - 1) / (2 * kTileRows));
+  const int target = (K + p.S) * waves_in_group;
+  wait_stores();
+  int t = 0;
+  bool last = false;
+  if (lane < nrows) {
+    t = shared ? (r0 + lane) : (int)L.rows[sbase + r0 + lane];
+    last = atomic_add_agent(p.pair_done + t * p.n_rg + rg, 1) == target - 1;
+  }
+  unsigned long long todo = __ballot(last);
+  while (todo) {
+    const int src = __ffsll((long long)todo) - 1;
+    todo &= todo - 1;
+    const int tt = __shfl(t, src, kWave);
+    constexpr int kCols = kDownRows / kWave;   // columns per lane
+    // all K+S expert outputs are requested before any is summed (one round trip)
+    float o[kMaxTopK + 1][kCols];
+    float wk[kMaxTopK];
 #pragma unroll
-    for (int j = 1; j < 4; ++j) {
-      if (key[j] > bk) { bk = key[j]; be = lane + kWave * j; bv = v[j]; }   // strict: lower id on ties
+    for (int k = 0; k < kMaxTopK; ++k) {
+      if (k < K) {
+        const int e = L.tki[tt * K + k];
+        const int row = L.base[e] + pair_rank(p, L, tt, e);
+        wk[k] = L.tkw[tt * K + k];
+#pragma unroll
+        for (int i = 0; i < kCols; ++i)
+          o[k][i] = ld_coh(p.o_scr + (size_t)row * p.H + c0 + min(lane + kWave * i, nc - 1));
+      }
     }
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-      const int ok = __shfl_xor(bk, o, kWave);
-      const int oe = __shfl_xor(be, o, kWave);
-      const float ov = __shfl_xor(bv, o, kWave);
-      if (ok > bk || (ok == bk && oe < be)) { bk = ok; be = oe; bv = ov; }
-    }
-    if (lane == k) { my_idx = be; my_logit = bv; }
+    for (int i = 0; i < kCols; ++i)
+      o[kMaxTopK][i] = p.S ? ld_coh(p.o_scr + (size_t)(p.T * K + tt) * p.H + c0 + min(lane + kWave * i, nc - 1)) : 0.f;
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      if (be == lane + kWave * j) key[j] = INT_MIN;
-  }
-  const float s = lane < p.K ? 1.0f / (1.0f + __expf(-my_logit)) : 0.f;
-  const float sum = wave_sum(s);
-  if (lane < p.K) {
-    const float wk = s / sum;
-    p.topk_idx[t * p.K + lane] = my_idx;
-    p.topk_w[t * p.K + lane] = wk;
-    if (p.dbg_idx) p.dbg_idx[t * p.K + lane] = my_idx;
-    if (p.dbg_w) p.dbg_w[t * p.K + lane] = wk;
+    for (int i = 0; i < kCols; ++i) {
+      float v = o[kMaxTopK][i];
+#pragma unroll
+      for (int k = 0; k < kMaxTopK; ++k)
+        if (k < K) v += wk[k] * o[k][i];
+      const int c = lane + kWave * i;
+      if (c < nc) st(p.y + (size_t)tt * p.H + c0 + c, f32_to_bf16(v));
+    }
+    if (lane == 0) store_agent(p.pair_done + tt * p.n_rg + rg, 0);
   }
 }
 
 // ----------------------------------------------------------------------------
 // Expert gate/up: one 16-row block (8 gate rows + 8 up rows) of one expert for
-// up to 64 of its rows; the 4 waves split the H/64 tiles (wave w takes tiles
-// q = w, w+4, ...); partial sums meet in LDS; then h = bf16(silu(g) * u).
+// up to 64 of its rows.  The 4 waves split the H/64 tiles (wave w takes tiles
+// w, w+4, ...); weight loads run up to two stages ahead of the MFMAs; partial
+// sums meet in LDS; then h = bf16(silu(g) * u) for the block's 8 intermediate
+// columns.  XL: the activation rows are read from LDS (small batches),
+// otherwise from global memory in the same pipeline as the weights.
 // ----------------------------------------------------------------------------
-template <int NMB>
-__device__ void gu_item(const Params& p, const Lds& L, int slot, int sbase, int r0, int nrows,
-                        int rb, bool shared) {
+template <int NMB, bool XL>
+struct GuStage {
+  static constexpr int D = XL ? 4 : (NMB == 1 ? 2 : 1);   // tiles per stage
+  u32x4 w[D];
+  f32x2 s[D];
+  u32x4 a[XL ? 1 : D][2][NMB];
+};
+
+template <int NMB, bool XL, int NMBMAX>
+__device__ __forceinline__ void gu_item(KParams& p, const Lds& L, int slot, int sbase, int r0, int nrows,
+                        int rb, bool shared, int parity) {
+  using Stage = GuStage<NMB, XL>;
+  constexpr int D = Stage::D;
   const int w = wave_id(), lane = lane_id();
   const int n = lane & 15, kq = lane >> 4;
   const int nq = p.n_q13;
+  const int nj = (nq - w + kWaves - 1) / kWaves;     // tiles of this wave
   const size_t blk = (size_t)slot * p.n_rb13 + rb;
   const u32x4* wt = p.w13p + blk * nq * kWave + lane;
-  const float2* sc = (const float2*)p.s13p + blk * nq * kTileRows + n;
+  const f32x2* sc = (const f32x2*)p.s13p + blk * nq * kTileRows + n;
 
-  // A operand rows: token of expert row r0 + mb*16 + n (zero when past nrows)
+  // A operand rows: token of expert row r0 + mb*16 + n.  Rows past nrows read
+  // row r0 (always valid) and are zeroed before the MFMA, so every load is
+  // issued by every lane and the loads stay in order behind one counter.
   const uint16_t* arow[NMB];
+  const SHARED uint16_t* arow_l[NMB];
   bool aval[NMB];
 #pragma unroll
   for (int mb = 0; mb < NMB; ++mb) {
     const int r = mb * kMBlock + n;
     aval[mb] = r < nrows;
-    int tok = 0;
-    if (aval[mb]) tok = shared ? (r0 + r) : (int)L.rows[sbase + r0 + r];
+    const int rr = aval[mb] ? r : 0;
+    const int tok = shared ? (r0 + rr) : (int)L.rows[sbase + r0 + rr];
     arow[mb] = p.x + (size_t)tok * p.H + 8 * kq;
+    arow_l[mb] = L.xs + (size_t)tok * p.xs_stride + 8 * kq;
   }
 
-  f32x4 acc[NMB];
+  auto load = [&](Stage& S, int j0) __attribute__((always_inline)) {
 #pragma unroll
-  for (int mb = 0; mb < NMB; ++mb) acc[mb] = (f32x4){0.f, 0.f, 0.f, 0.f};
-
-  constexpr int U = NMB == 1 ? 4 : 2;
-  for (int q0 = w; q0 < nq; q0 += kWaves * U) {
-    u32x4 wv[U];
-    float2 sv[U];
-    u32x4 av[U][2][NMB];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int q = q0 + kWaves * u;
-      if (q < nq) {
-        wv[u] = load_nt(wt + (size_t)q * kWave);
-        sv[u] = sc[(size_t)q * kTileRows];
+    for (int u = 0; u < D; ++u) {
+      const int j = min(j0 + u, nj - 1);               // past the end: reload the last tile
+      const int q = w + kWaves * j;
+      S.w[u] = ld_stream(wt + (size_t)q * kWave);
+      S.s[u] = ld(sc + (size_t)q * kTileRows);
+      if (!XL) {
 #pragma unroll
         for (int g = 0; g < 2; ++g)
 #pragma unroll
           for (int mb = 0; mb < NMB; ++mb)
-            av[u][g][mb] = aval[mb] ? *(const u32x4*)(arow[mb] + kTileK * q + kGroup * g)
-                                    : (u32x4){0u, 0u, 0u, 0u};
+            S.a[XL ? 0 : u][g][mb] = ld((const u32x4*)(arow[mb] + kTileK * q + kGroup * g));
       }
     }
+  };
+  f32x4 acc[NMB];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int q = q0 + kWaves * u;
-      if (q < nq) {
+  for (int mb = 0; mb < NMB; ++mb) acc[mb] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  const u32x4 zero4 = {0u, 0u, 0u, 0u};
+  auto compute = [&](const Stage& S, int j0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < D; ++u) {
+      if (j0 + u < nj) {
+        const int q = w + kWaves * (j0 + u);
 #pragma unroll
         for (int g = 0; g < 2; ++g) {
-          const bf16x8 b = fp8x8_to_bf16(wv[u][2 * g], wv[u][2 * g + 1]);
-          const float s = g ? sv[u].y : sv[u].x;
+          const bf16x8 b = fp8x8_to_bf16(S.w[u][2 * g], S.w[u][2 * g + 1]);
+          const float s = g ? S.s[u].y : S.s[u].x;
 #pragma unroll
           for (int mb = 0; mb < NMB; ++mb) {
-            const f32x4 t = mfma16(as_bf16x8(av[u][g][mb]), b);
-            acc[mb] += s * t;
+            u32x4 a;
+            if (XL) a = *(const SHARED u32x4*)(arow_l[mb] + kTileK * q + kGroup * g);
+            else a = S.a[XL ? 0 : u][g][mb];
+            acc[mb] += s * mfma16(as_bf16x8(aval[mb] ? a : zero4), b);
           }
         }
       }
     }
+  };
+  // two register stages in turn; a stage is only loaded if it holds tiles
+  // (the branches are uniform across the wave)
+  Stage A, B;
+  load(A, 0);
+  for (int j0 = 0; j0 < nj; j0 += 2 * D) {
+    if (j0 + D < nj) load(B, j0 + D);
+    compute(A, j0);
+    if (j0 + 2 * D < nj) load(A, j0 + 2 * D);
+    if (j0 + D < nj) compute(B, j0 + D);
   }
 
-  // cross-wave sum in fixed order (wave 0 + 1 + 2 + 3)
-  f32x4* red = (f32x4*)L.red;
+  // cross-wave sum in fixed order (wave 0 + 1 + 2 + 3); the partials area
+  // alternates between items, so the waves need no second barrier
+  SHARED f32x4* red = (SHARED f32x4*)L.red + (parity & 1) * kWaves * NMBMAX * kWave;
 #pragma unroll
-  for (int mb = 0; mb < NMB; ++mb) red[(w * 4 + mb) * kWave + lane] = acc[mb];
+  for (int mb = 0; mb < NMB; ++mb) red[(w * NMB + mb) * kWave + lane] = acc[mb];
   __syncthreads();
-  if (w < NMB) {
+  if (w < NMB && w * kMBlock < nrows) {
     const int mb = w;
-    f32x4 s = red[(0 * 4 + mb) * kWave + lane];
+    f32x4 s = red[(0 * NMB + mb) * kWave + lane];
 #pragma unroll
-    for (int ww = 1; ww < kWaves; ++ww) s += red[(ww * 4 + mb) * kWave + lane];
+    for (int ww = 1; ww < kWaves; ++ww) s += red[(ww * NMB + mb) * kWave + lane];
     // column n < 8 is gate row 8 rb + n, column n + 8 the matching up row
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const float g = s[i];
-      const float u = __shfl_down(s[i], 8, 16);
+      const float u = dpp<kDppRowRor8>(s[i]);
+      const uint32_t hb = f32_to_bf16(g / (1.0f + __expf(-g)) * u);
+      const uint32_t hb_next = dpp<kDppRowShl1>(hb);          // column n + 1
       const int r = mb * kMBlock + 4 * kq + i;
-      if (n < 8 && r < nrows) {
-        const float hv = g / (1.0f + __expf(-g)) * u;
-        p.h_scr[(size_t)(sbase + r0 + r) * p.I + 8 * rb + n] = f32_to_bf16(hv);
-      }
+      if (n < 8 && (n & 1) == 0 && r < nrows)
+        st_coh((uint32_t*)(p.h_scr + (size_t)(sbase + r0 + r) * p.I + 8 * rb + n), hb | (hb_next << 16));
     }
+    // each wave that stored h rows publishes them (one count per 16-row block)
+    wait_stores();
+    if (lane == 0) atomic_add_agent(p.ctr + kCtrHReady + slot, 1);
   }
 }
 
 // ----------------------------------------------------------------------------
 // Expert down projection: 128 output rows (8 row blocks, 2 per wave, full K =
-// I) of one expert for up to 64 of its rows.  Output rows go to o_scr.
+// I) of one expert for up to 64 of its rows.  Output rows go to o_scr.  HL:
+// the item's h rows (<= 16) are staged in LDS first; otherwise they are read
+// from global memory in the weight pipeline.
 // ----------------------------------------------------------------------------
-template <int NMB>
-__device__ void down_item(const Params& p, int slot, int sbase, int r0, int nrows, int rg) {
+template <int NMB, bool HL>
+struct DnStage {
+  static constexpr int D = HL ? 4 : (NMB == 1 ? 2 : 1);
+  u32x4 w[D][2];
+  f32x2 s[D][2];
+  u32x4 a[HL ? 1 : D][2][NMB];
+};
+
+template <int NMB, bool HL>
+__device__ __forceinline__ void down_item(KParams& p, const Lds& L, int slot, int sbase, int r0, int nrows,
+                          int rg, bool shared) {
+  using Stage = DnStage<NMB, HL>;
+  constexpr int D = Stage::D;
   const int w = wave_id(), lane = lane_id();
   const int n = lane & 15, kq = lane >> 4;
   const int nq = p.n_q2;
   const int rb0 = rg * (kDownRows / kTileRows) + 2 * w;
+  const int nrb = min(2, p.n_rb2 - rb0);      // row blocks of this wave (0..2)
+
+  const int nrb_eff = max(nrb, 1);            // waves past the last block idle after staging
 
   const uint16_t* arow[NMB];
+  const SHARED uint16_t* arow_l[NMB];
   bool aval[NMB];
 #pragma unroll
   for (int mb = 0; mb < NMB; ++mb) {
     const int r = mb * kMBlock + n;
     aval[mb] = r < nrows;
-    arow[mb] = p.h_scr + (size_t)(sbase + r0 + (aval[mb] ? r : 0)) * p.I + 8 * kq;
+    const int rr = aval[mb] ? r : 0;
+    arow[mb] = p.h_scr + (size_t)(sbase + r0 + rr) * p.I + 8 * kq;
+    arow_l[mb] = L.hs + (size_t)rr * p.hs_stride + 8 * kq;
   }
-
+  // a wave with a single row block (last group of a ragged H) loads that
+  // block twice and stores only the first copy
+  const u32x4* wt[2];
+  const f32x2* sc[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    const int rb = rb0 + j;
-    if (rb >= p.n_rb2) break;
-    const size_t blk = (size_t)slot * p.n_rb2 + rb;
-    const u32x4* wt = p.w2p + blk * nq * kWave + lane;
-    const float2* sc = (const float2*)p.s2p + blk * nq * kTileRows + n;
-    f32x4 acc[NMB];
+    const size_t blk = (size_t)slot * p.n_rb2 + min(rb0 + min(j, nrb_eff - 1), p.n_rb2 - 1);
+    wt[j] = p.w2p + blk * nq * kWave + lane;
+    sc[j] = (const f32x2*)p.s2p + blk * nq * kTileRows + n;
+  }
+  auto load = [&](Stage& S, int q0) __attribute__((always_inline)) {
 #pragma unroll
-    for (int mb = 0; mb < NMB; ++mb) acc[mb] = (f32x4){0.f, 0.f, 0.f, 0.f};
-    constexpr int U = NMB == 1 ? 8 : 4;
-    for (int q0 = 0; q0 < nq; q0 += U) {
-      u32x4 wv[U];
-      float2 sv[U];
-      u32x4 av[U][2][NMB];
+    for (int u = 0; u < D; ++u) {
+      const int q = min(q0 + u, nq - 1);
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int q = q0 + u;
-        if (q < nq) {
-          wv[u] = load_nt(wt + (size_t)q * kWave);
-          sv[u] = sc[(size_t)q * kTileRows];
-#pragma unroll
-          for (int g = 0; g < 2; ++g)
-#pragma unroll
-            for (int mb = 0; mb < NMB; ++mb)
-              av[u][g][mb] = aval[mb] ? *(const u32x4*)(arow[mb] + kTileK * q + kGroup * g)
-                                      : (u32x4){0u, 0u, 0u, 0u};
-        }
+      for (int j = 0; j < 2; ++j) {
+        S.w[u][j] = ld_stream(wt[j] + (size_t)q * kWave);
+        S.s[u][j] = ld(sc[j] + (size_t)q * kTileRows);
       }
+      if (!HL) {
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
+        for (int g = 0; g < 2; ++g)
+#pragma unroll
+          for (int mb = 0; mb < NMB; ++mb)
+            S.a[HL ? 0 : u][g][mb] = ld_coh16(arow[mb] + kTileK * q + kGroup * g);
+      }
+    }
+  };
+  f32x4 acc[2][NMB];
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb) acc[j][mb] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  const u32x4 zero4 = {0u, 0u, 0u, 0u};
+  auto compute = [&](const Stage& S, int q0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < D; ++u) {
+      if (q0 + u < nq) {
         const int q = q0 + u;
-        if (q < nq) {
 #pragma unroll
-          for (int g = 0; g < 2; ++g) {
-            const bf16x8 b = fp8x8_to_bf16(wv[u][2 * g], wv[u][2 * g + 1]);
-            const float s = g ? sv[u].y : sv[u].x;
+        for (int g = 0; g < 2; ++g) {
+          u32x4 a[NMB];
 #pragma unroll
-            for (int mb = 0; mb < NMB; ++mb) {
-              const f32x4 t = mfma16(as_bf16x8(av[u][g][mb]), b);
-              acc[mb] += s * t;
-            }
+          for (int mb = 0; mb < NMB; ++mb) {
+            if (HL) a[mb] = *(const SHARED u32x4*)(arow_l[mb] + kTileK * q + kGroup * g);
+            else a[mb] = S.a[HL ? 0 : u][g][mb];
+            a[mb] = aval[mb] ? a[mb] : zero4;
+          }
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            const bf16x8 b = fp8x8_to_bf16(S.w[u][j][2 * g], S.w[u][j][2 * g + 1]);
+            const float s = g ? S.s[u][j].y : S.s[u][j].x;
+#pragma unroll
+            for (int mb = 0; mb < NMB; ++mb) acc[j][mb] += s * mfma16(as_bf16x8(a[mb]), b);
           }
         }
       }
     }
+  };
+  Stage A, B;
+  load(A, 0);                                 // weights first: they need no input
+  if (HL) {
+    // stage the h rows of this item: nrows x I bf16, 8 bytes per thread-step
+    __syncthreads();
+    stage_h_rows(p, L, sbase + r0, nrows);
+    __syncthreads();
+  }
+  if (nrb <= 0) return;
+  for (int q0 = 0; q0 < nq; q0 += 2 * D) {
+    if (q0 + D < nq) load(B, q0 + D);
+    compute(A, q0);
+    if (q0 + 2 * D < nq) load(A, q0 + 2 * D);
+    if (q0 + D < nq) compute(B, q0 + D);
+  }
 #pragma unroll
-    for (int mb = 0; mb < NMB; ++mb)
+  for (int j = 0; j < 2; ++j) {
+    if (j < nrb) {
+      const int rb = rb0 + j;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = mb * kMBlock + 4 * kq + i;
-        if (r < nrows) p.o_scr[(size_t)(sbase + r0 + r) * p.H + rb * kTileRows + n] = acc[mb][i];
-      }
+      for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = mb * kMBlock + 4 * kq + i;
+          if (r < nrows) st_coh(p.o_scr + (size_t)(sbase + r0 + r) * p.H + rb * kTileRows + n, acc[j][mb][i]);
+        }
+    }
+  }
+  wave_arrive_combine(p, L, sbase, r0, nrows, rg, shared);
+}
+
+// ----------------------------------------------------------------------------
+// Fully unrolled gate/up and down items for the common shapes (x and h in LDS,
+// one MFMA block): every weight tile of the wave's share is requested at the
+// start of the item (16 KiB in flight per wave), then consumed in order, so
+// each MFMA waits only for its own tile.
+// ----------------------------------------------------------------------------
+template <int NJ>
+__device__ __forceinline__ void gu_item_full(KParams& p, const Lds& L, int slot, int sbase, int r0, int nrows,
+                             int rb, bool shared, int parity) {
+  const int w = wave_id(), lane = lane_id();
+  const int n = lane & 15, kq = lane >> 4;
+  const int nq = p.n_q13;                            // == 4 * NJ
+  const size_t blk = (size_t)slot * p.n_rb13 + rb;
+  const u32x4* wt = p.w13p + (blk * nq + w) * kWave + lane;
+  const f32x2* sc = (const f32x2*)p.s13p + (blk * nq + w) * kTileRows + n;
+  u32x4 wv[NJ];
+  f32x2 sv[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    wv[j] = ld_stream(wt + (size_t)j * kWaves * kWave);
+    sv[j] = ld(sc + (size_t)j * kWaves * kTileRows);
+  }
+  const bool aval = n < nrows;
+  const int tok = shared ? (r0 + (aval ? n : 0)) : (int)L.rows[sbase + r0 + (aval ? n : 0)];
+  const SHARED uint16_t* arow = L.xs + (size_t)tok * p.xs_stride + 8 * kq + kTileK * w;
+  const u32x4 zero4 = {0u, 0u, 0u, 0u};
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      u32x4 a = *(const SHARED u32x4*)(arow + kTileK * kWaves * j + kGroup * g);
+      a = aval ? a : zero4;
+      const bf16x8 b = fp8x8_to_bf16(wv[j][2 * g], wv[j][2 * g + 1]);
+      acc += (g ? sv[j].y : sv[j].x) * mfma16(as_bf16x8(a), b);
+    }
+  }
+  SHARED f32x4* red = (SHARED f32x4*)L.red + (parity & 1) * kWaves * kWave;
+  red[w * kWave + lane] = acc;
+  __syncthreads();
+  if (w == 0) {
+    f32x4 s = red[lane];
+#pragma unroll
+    for (int ww = 1; ww < kWaves; ++ww) s += red[ww * kWave + lane];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float g = s[i];
+      const float u = dpp<kDppRowRor8>(s[i]);
+      const uint32_t hb = f32_to_bf16(g / (1.0f + __expf(-g)) * u);
+      const uint32_t hb_next = dpp<kDppRowShl1>(hb);
+      const int r = 4 * kq + i;
+      if (n < 8 && (n & 1) == 0 && r < nrows)
+        st_coh((uint32_t*)(p.h_scr + (size_t)(sbase + r0 + r) * p.I + 8 * rb + n), hb | (hb_next << 16));
+    }
+    wait_stores();
+    if (lane == 0) atomic_add_agent(p.ctr + kCtrHReady + slot, 1);
   }
 }
 
-// y[t][rg*128 .. +128) = bf16(o_shared + sum_k w_k o_k), in that order.
-__device__ void combine_rows(const Params& p, const Lds& L, int ncomb, int rg) {
-  const int tid = threadIdx.x;
-  const int K = p.K;
-  int* ctok = L.comb;                          // [64]
-  int* crow = L.comb + kMRange;                // [64][K]
-  float* cw = (float*)(L.comb + kMRange + kMRange * kMaxTopK);   // [64][K]
-  for (int i = tid; i < ncomb * K; i += kThreads) {
-    const int j = i / K, k = i % K;
-    const int t = ctok[j];
-    const int e = p.topk_idx[t * K + k];
-    crow[j * kMaxTopK + k] = pair_row(p, L, t, e);
-    cw[j * kMaxTopK + k] = p.topk_w[t * K + k];
+template <int NQ>
+__device__ __forceinline__ void down_item_full(KParams& p, const Lds& L, int slot, int sbase, int r0, int nrows,
+                               int rg, bool shared) {
+  const int w = wave_id(), lane = lane_id();
+  const int n = lane & 15, kq = lane >> 4;
+  const int rb0 = rg * (kDownRows / kTileRows) + 2 * w;
+  const int nrb = min(2, p.n_rb2 - rb0);
+  u32x4 wv[2][NQ];
+  f32x2 sv[2][NQ];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const size_t blk = (size_t)slot * p.n_rb2 + min(rb0 + j, p.n_rb2 - 1);
+    const u32x4* wt = p.w2p + blk * NQ * kWave + lane;
+    const f32x2* sc = (const f32x2*)p.s2p + blk * NQ * kTileRows + n;
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      wv[j][q] = ld_stream(wt + (size_t)q * kWave);
+      sv[j][q] = ld(sc + (size_t)q * kTileRows);
+    }
   }
+  // stage the item's h rows (nrows x I bf16) while the weights are in flight;
+  // the first barrier keeps the previous item's readers of the area safe
   __syncthreads();
-  const int c0 = rg * kDownRows;
-  const int nc = min(kDownRows, p.H - c0);
-  for (int i = tid; i < ncomb * kDownRows; i += kThreads) {
-    const int j = i / kDownRows, c = i % kDownRows;
-    if (c >= nc) continue;
-    const int t = ctok[j];
-    float v = p.S ? p.o_scr[(size_t)(p.T * K + t) * p.H + c0 + c] : 0.f;
-    for (int k = 0; k < K; ++k)
-      v += cw[j * kMaxTopK + k] * p.o_scr[(size_t)crow[j * kMaxTopK + k] * p.H + c0 + c];
-    p.y[(size_t)t * p.H + c0 + c] = f32_to_bf16(v);
+  stage_h_rows(p, L, sbase + r0, nrows);
+  __syncthreads();
+  if (nrb <= 0) return;
+  const bool aval = n < nrows;
+  const SHARED uint16_t* arow = L.hs + (size_t)(aval ? n : 0) * p.hs_stride + 8 * kq;
+  const u32x4 zero4 = {0u, 0u, 0u, 0u};
+  f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) {
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      u32x4 a = *(const SHARED u32x4*)(arow + kTileK * q + kGroup * g);
+      a = aval ? a : zero4;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const bf16x8 b = fp8x8_to_bf16(wv[j][q][2 * g], wv[j][q][2 * g + 1]);
+        acc[j] += (g ? sv[j][q].y : sv[j][q].x) * mfma16(as_bf16x8(a), b);
+      }
+    }
   }
-  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    if (j < nrb) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 4 * kq + i;
+        if (r < nrows)
+          st_coh(p.o_scr + (size_t)(sbase + r0 + r) * p.H + (rb0 + j) * kTileRows + n, acc[j][i]);
+      }
+    }
+  }
+  wave_arrive_combine(p, L, sbase, r0, nrows, rg, shared);
 }
 
 // ----------------------------------------------------------------------------
 // The persistent kernel
 // ----------------------------------------------------------------------------
-template <int NMBMAX>
-__global__ void __launch_bounds__(kThreads) moe_decode_kernel(Params p) {
+template <int NMBMAX, bool XL>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(NMBMAX == 1 ? 2 : 1))) moe_decode_kernel(Params arg) {
+  KParams& p = *(const CONSTANT Params*)__builtin_amdgcn_kernarg_segment_ptr();
+  (void)arg;
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  const Lds L = lds_view(p, smem);
+  const Lds L = lds_view(p, (SHARED char*)smem);
   const int tid = threadIdx.x;
-  bool placed = false;
-  int t_rgu_end = 0, t_total = 0;
-
-  auto ensure_placement = [&]() -> bool {
-    if (placed) return true;
-    if (!wait_geq(p, p.ctr + kCtrTopkDone, p.n_topk, L.misc + 1)) return false;
-    build_placement(p, L);
-    const int n_mr = L.misc[2];
-    t_rgu_end = p.t_sdn_end + n_mr * p.n_rb13;
-    t_total = t_rgu_end + n_mr * p.n_rg;
-    placed = true;
-    return true;
-  };
-
-  // dispatch on the number of 16-row MFMA blocks an item covers
-  auto run_gu = [&](int slot, int sbase, int r0, int nrows, int rb, bool shared) {
-    const int nmb = (nrows + kMBlock - 1) / kMBlock;
-    if (NMBMAX == 1 || nmb <= 1) gu_item<1>(p, L, slot, sbase, r0, nrows, rb, shared);
-    else if (nmb == 2) gu_item<NMBMAX >= 2 ? 2 : 1>(p, L, slot, sbase, r0, nrows, rb, shared);
-    else if (nmb == 3) gu_item<NMBMAX >= 3 ? 3 : 1>(p, L, slot, sbase, r0, nrows, rb, shared);
-    else gu_item<NMBMAX >= 4 ? 4 : 1>(p, L, slot, sbase, r0, nrows, rb, shared);
-  };
-  auto run_down = [&](int slot, int sbase, int r0, int nrows, int rg) {
-    const int nmb = (nrows + kMBlock - 1) / kMBlock;
-    if (NMBMAX == 1 || nmb <= 1) down_item<1>(p, slot, sbase, r0, nrows, rg);
-    else if (nmb == 2) down_item<NMBMAX >= 2 ? 2 : 1>(p, slot, sbase, r0, nrows, rg);
-    else if (nmb == 3) down_item<NMBMAX >= 3 ? 3 : 1>(p, slot, sbase, r0, nrows, rg);
-    else down_item<NMBMAX >= 4 ? 4 : 1>(p, slot, sbase, r0, nrows, rg);
-  };
-
-  // After a down item: count its rows in for (row, chunk); the last arriver
-  // for a (row, chunk) combines it.
-  auto arrive_and_combine = [&](int sbase, int r0, int nrows, int rg, bool shared) -> bool {
+  const int G = gridDim.x;
+  // Small batch: the whole layer input is kept in LDS, loaded before the
+  // first item that reads it (the router reads x from global memory, so the
+  // copy overlaps the routing wait).
+  bool x_staged = !XL;
+  auto ensure_x = [&]() __attribute__((always_inline)) {
+    if (x_staged) return;
+    const int per_row = p.H / 8;
+    batched_copy<u32x4>(
+        p.T * per_row, [&](int i) { return ld((const u32x4*)(p.x + (size_t)(i / per_row) * p.H) + i % per_row); },
+        [&](int i, u32x4 v) { *(SHARED u32x4*)(L.xs + (size_t)(i / per_row) * p.xs_stride + 8 * (i % per_row)) = v; });
     __syncthreads();
-    if (tid == 0) L.misc[8] = 0;
-    __syncthreads();
-    if (tid < nrows) {
-      const int t = shared ? (r0 + tid) : (int)L.rows[sbase + r0 + tid];
-      fence_release_agent();
-      const int old = atomic_add_agent(p.pair_done + t * p.n_rg + rg, 1);
-      if (old == p.K + p.S - 1) {
-        const int j = atomicAdd(L.misc + 8, 1);
-        L.comb[j] = t;
+    x_staged = true;
+  };
+  bool routed = false;          // routing and placement are in LDS
+  int i_rgu_end = 0, i_sdn_end = 0, i_total = 0;
+
+  // optional timeline of this workgroup (thread 0 writes it)
+  long long* trace = (p.trace && (int)blockIdx.x < p.trace_blocks)
+                         ? p.trace + (size_t)blockIdx.x * (1 + p.trace_cap) * 4 : nullptr;
+  const long long t_entry = wall_clock64();
+  int n_ev = 0;
+  long long t_got = 0, t_ready = 0;
+  int kind = 0, it = 0;
+  auto record = [&]() __attribute__((always_inline)) {
+    if (trace && tid == 0 && n_ev < p.trace_cap) {
+      long long* r = trace + (size_t)(1 + n_ev) * 4;
+      st(r + 0, (long long)it | ((long long)kind << 32));
+      st(r + 1, t_got);
+      st(r + 2, t_ready);
+      st(r + 3, (long long)wall_clock64());
+    }
+    ++n_ev;
+  };
+
+  // Routing in this workgroup: top-k (selected here for small batches, else
+  // copied from the distributed top-k items) and the bitmap placement.
+  auto ensure_routing = [&]() __attribute__((always_inline)) -> bool {
+    if (routed) return true;
+    const long long r_start = wall_clock64();
+    long long r_go = 0, r_lg = 0, r_row0 = 0, c_lg = 0;
+    if (p.local_topk) {
+      if (!wait_geq(p, go_flag(p.ctr + kCtrRouterGo), 1, L.misc + 1)) return false;
+      r_go = wall_clock64();
+      // all T x E logits into LDS with one round of coherent loads
+      batched_copy<float>(p.T * p.E, [&](int i) { return ld_coh(p.logits + i); },
+                          [&](int i, float v) { L.lg[i] = v; });
+      __syncthreads();
+      r_lg = wall_clock64();
+      c_lg = (long long)__builtin_amdgcn_s_memtime();
+      // rows w, w+4 | w+8, w+12 | ... two at a time per wave
+      for (int t0 = wave_id(); t0 < p.T; t0 += 2 * kWaves) {
+        const int t1 = t0 + kWaves;
+        const int tr[2] = {t0, min(t1, p.T - 1)};
+        int e[2];
+        float wk[2];
+        topk_rows<2>(p, L.lg, tr, e, wk);
+        if (t0 == 0) r_row0 = wall_clock64();
+        if (lane_id() < p.K) {
+          L.tki[t0 * p.K + lane_id()] = (int16_t)e[0];
+          L.tkw[t0 * p.K + lane_id()] = wk[0];
+          if (t1 < p.T) {
+            L.tki[t1 * p.K + lane_id()] = (int16_t)e[1];
+            L.tkw[t1 * p.K + lane_id()] = wk[1];
+          }
+        }
+      }
+    } else {
+      if (!wait_geq(p, go_flag(p.ctr + kCtrTopkGo), 1, L.misc + 1)) return false;
+      for (int i = tid; i < p.T * p.K; i += kThreads) {
+        L.tki[i] = (int16_t)ld_coh(p.topk_idx + i);
+        L.tkw[i] = ld_coh(p.topk_w + i);
       }
     }
+    const long long r_rows = wall_clock64();
+    const long long c_rows = (long long)__builtin_amdgcn_s_memtime();
     __syncthreads();
-    const int ncomb = L.misc[8];
-    if (ncomb == 0) return true;
-    if (!ensure_placement()) return false;
-    if (tid == 0) fence_acquire_agent();
-    __syncthreads();
-    combine_rows(p, L, ncomb, rg);
-    for (int j = tid; j < ncomb; j += kThreads) store_agent(p.pair_done + L.comb[j] * p.n_rg + rg, 0);
+    const long long r_topk = wall_clock64();
+    build_placement(p, L);
+    const long long r_place = wall_clock64();
+    if (blockIdx.x == 0) write_routing_debug(p, L);
+    if (trace && tid == 0 && n_ev + 1 < p.trace_cap) {   // routing phases: kinds 7, 8
+      long long* r = trace + (size_t)(1 + n_ev) * 4;
+      st(r + 0, (long long)7 << 32 | (long long)((r_place - r_topk) & 0xffffffff));
+      st(r + 1, r_start);
+      st(r + 2, r_go);
+      st(r + 3, r_topk);
+      r += 4;
+      st(r + 0, (long long)8 << 32 | (long long)((c_rows - c_lg) & 0xffffffff));
+      st(r + 1, r_lg);
+      st(r + 2, r_row0);
+      st(r + 3, r_rows);
+      n_ev += 2;
+    }
+    const int n_mr = L.misc[0];
+    i_rgu_end = p.i_topk_end + n_mr * p.n_rb13;
+    i_sdn_end = i_rgu_end + p.n_sdn;
+    i_total = i_sdn_end + n_mr * p.n_rg;
+    routed = true;
     return true;
+  };
+
+  int gu_count = 0;             // parity of the gate/up partial-sum area
+  auto run_gu = [&](int slot, int sbase, int r0, int nrows, int rb, bool shared) __attribute__((always_inline)) {
+    const int nmb = (nrows + kMBlock - 1) / kMBlock;
+    const int par = gu_count++;
+    if (XL && p.n_q13 == 4 * kFullTiles) gu_item_full<kFullTiles>(p, L, slot, sbase, r0, nrows, rb, shared, par);
+    else if (NMBMAX == 1 || nmb <= 1) gu_item<1, XL, NMBMAX>(p, L, slot, sbase, r0, nrows, rb, shared, par);
+    else if (nmb == 2) gu_item<NMBMAX >= 2 ? 2 : 1, XL, NMBMAX>(p, L, slot, sbase, r0, nrows, rb, shared, par);
+    else if (nmb == 3) gu_item<NMBMAX >= 3 ? 3 : 1, XL, NMBMAX>(p, L, slot, sbase, r0, nrows, rb, shared, par);
+    else gu_item<NMBMAX >= 4 ? 4 : 1, XL, NMBMAX>(p, L, slot, sbase, r0, nrows, rb, shared, par);
+  };
+  auto run_down = [&](int slot, int sbase, int r0, int nrows, int rg, bool shared) __attribute__((always_inline)) {
+    const int nmb = (nrows + kMBlock - 1) / kMBlock;
+    if (XL && p.hs_stride > 0 && p.n_q2 == kFullTiles / 2)
+      down_item_full<kFullTiles / 2>(p, L, slot, sbase, r0, nrows, rg, shared);
+    else if (XL && p.hs_stride > 0) down_item<1, XL>(p, L, slot, sbase, r0, nrows, rg, shared);
+    else if (NMBMAX == 1 || nmb <= 1) down_item<1, false>(p, L, slot, sbase, r0, nrows, rg, shared);
+    else if (nmb == 2) down_item<NMBMAX >= 2 ? 2 : 1, false>(p, L, slot, sbase, r0, nrows, rg, shared);
+    else if (nmb == 3) down_item<NMBMAX >= 3 ? 3 : 1, false>(p, L, slot, sbase, r0, nrows, rg, shared);
+    else down_item<NMBMAX >= 4 ? 4 : 1, false>(p, L, slot, sbase, r0, nrows, rg, shared);
+  };
+  // gate/up publications an expert's down items wait for: one per 16-row
+  // MFMA block per gate/up row block
+  auto h_target = [&](int rows) __attribute__((always_inline)) {
+    return p.n_rb13 * ((rows + kMBlock - 1) / kMBlock);
   };
 
   bool router_seen = false;
-  while (true) {
-    if (tid == 0) {
-      L.misc[0] = atomic_add_agent(p.ctr + kCtrTicket, 1);
-      L.misc[1] = load_agent(p.ctr + kCtrStatus);
-    }
-    __syncthreads();
-    const int tk = L.misc[0];
-    const int st = L.misc[1];
-    __syncthreads();
-    if (st != 0) break;
-
-    if (tk < p.t_router_end) {
-      router_item(p, tk);
-      publish_done(p.ctr + kCtrRouterDone);
-    } else if (tk < p.t_sgu_end) {
-      const int i = tk - p.t_router_end;
+  for (it = blockIdx.x;; it += G) {
+    t_got = t_ready = wall_clock64();
+    if (it < p.i_router_end) {
+      kind = 0;
+      router_item(p, L, it);
+      t_ready = wall_clock64();
+      publish_done(p.ctr + kCtrRouterDone, p.n_router, p.ctr + kCtrRouterGo);
+    } else if (it < p.i_sgu_end) {
+      kind = 1;
+      ensure_x();
+      const int i = it - p.i_router_end;
       const int mr = i / p.n_rb13, rb = i % p.n_rb13;
       const int r0 = mr * kMRange;
       run_gu(p.E, p.T * p.K, r0, min(kMRange, p.T - r0), rb, true);
-      publish_done(p.ctr + kCtrHReady + p.E);
-    } else if (tk < p.t_topk_end) {
+    } else if (it < p.i_topk_end) {
+      kind = 2;
       if (!router_seen) {
-        if (!wait_geq(p, p.ctr + kCtrRouterDone, p.n_router, L.misc + 1)) break;
+        if (!wait_geq(p, go_flag(p.ctr + kCtrRouterGo), 1, L.misc + 1)) break;
         router_seen = true;
       }
-      topk_item(p, tk - p.t_sgu_end);
-      publish_done(p.ctr + kCtrTopkDone);
-    } else if (tk < p.t_sdn_end) {
-      const int i = tk - p.t_topk_end;
-      const int mr = i / p.n_rg, rg = i % p.n_rg;
-      const int r0 = mr * kMRange;
-      const int nrows = min(kMRange, p.T - r0);
-      if (!wait_geq(p, p.ctr + kCtrHReady + p.E, p.n_mr_sh * p.n_rb13, L.misc + 1)) break;
-      run_down(p.E, p.T * p.K, r0, nrows, rg);
-      if (!arrive_and_combine(p.T * p.K, r0, nrows, rg, true)) break;
+      t_ready = wall_clock64();
+      topk_item(p, L, it - p.i_sgu_end);
+      publish_done(p.ctr + kCtrTopkDone, p.n_topk, p.ctr + kCtrTopkGo);
     } else {
-      if (!ensure_placement()) break;
-      if (tk >= t_total) break;
-      if (tk == p.t_sdn_end) write_placement_debug(p, L);
-      if (tk < t_rgu_end) {
-        const int i = tk - p.t_sdn_end;
+      kind = 6;
+      ensure_x();
+      if (!ensure_routing()) break;
+      t_ready = wall_clock64();
+      if (it >= i_total) break;
+      if (it < i_rgu_end) {
+        kind = 4;
+        const int i = it - p.i_topk_end;
         const int m = i / p.n_rb13, rb = i % p.n_rb13;
         const int e = L.mrlist[m];
         const int r0 = (m - L.nmrb[e]) * kMRange;
         run_gu(e, L.base[e], r0, min(kMRange, L.cnt[e] - r0), rb, false);
-        publish_done(p.ctr + kCtrHReady + e);
+      } else if (it < i_sdn_end) {
+        kind = 3;
+        const int i = it - i_rgu_end;
+        const int mr = i / p.n_rg, rg = i % p.n_rg;
+        const int r0 = mr * kMRange;
+        const int nrows = min(kMRange, p.T - r0);
+        if (!wait_geq(p, p.ctr + kCtrHReady + p.E, h_target(p.T), L.misc + 1)) break;
+        t_ready = wall_clock64();
+        run_down(p.E, p.T * p.K, r0, nrows, rg, true);
       } else {
-        const int i = tk - t_rgu_end;
+        kind = 5;
+        const int i = it - i_sdn_end;
         const int m = i / p.n_rg, rg = i % p.n_rg;
         const int e = L.mrlist[m];
         const int r0 = (m - L.nmrb[e]) * kMRange;
         const int nrows = min(kMRange, L.cnt[e] - r0);
-        const int need = (L.nmrb[e + 1] - L.nmrb[e]) * p.n_rb13;
-        if (!wait_geq(p, p.ctr + kCtrHReady + e, need, L.misc + 1)) break;
-        run_down(e, L.base[e], r0, nrows, rg);
-        if (!arrive_and_combine(L.base[e], r0, nrows, rg, false)) break;
+        if (!wait_geq(p, p.ctr + kCtrHReady + e, h_target(L.cnt[e]), L.misc + 1)) break;
+        t_ready = wall_clock64();
+        run_down(e, L.base[e], r0, nrows, rg, false);
       }
     }
+    record();
+  }
+  if (trace && tid == 0) {
+    st(trace + 0, t_entry);
+    st(trace + 1, (long long)wall_clock64());
+    st(trace + 2, (long long)n_ev);
+    st(trace + 3, (long long)G);
   }
 
   // The last workgroup out resets the counters for the next run.
+  wait_stores();
   __syncthreads();
   if (tid == 0) {
-    fence_release_agent();
     const int old = atomic_add_agent(p.ctr + kCtrExit, 1);
-    if (old == (int)gridDim.x - 1) {
-      fence_acquire_agent();
+    if (old == G - 1) {
       const bool failed = load_agent(p.ctr + kCtrStatus) != 0;
-      store_agent(p.ctr + kCtrTicket, 0);
       store_agent(p.ctr + kCtrRouterDone, 0);
       store_agent(p.ctr + kCtrTopkDone, 0);
+      for (int i = 0; i < kGoLines; ++i) {
+        store_agent(p.ctr + kCtrRouterGo + i * kGoStride, 0);
+        store_agent(p.ctr + kCtrTopkGo + i * kGoStride, 0);
+      }
       for (int e = 0; e < p.E + p.S; ++e) store_agent(p.ctr + kCtrHReady + e, 0);
       if (failed)
         for (int i = 0; i < p.T * p.n_rg; ++i) store_agent(p.pair_done + i, 0);
@@ -824,6 +1372,7 @@ struct moe_decode_handle {
   moe_decode_config cfg;
   int device;
   int n_cu;
+  int coop;
   float* router_w = nullptr;
   float* router_b = nullptr;
   u32x4* w13p = nullptr;
@@ -840,8 +1389,8 @@ struct moe_decode_handle {
   hipStream_t last_stream = nullptr;
   std::mutex mu;
   // occupancy cache, by (kernel variant, LDS bytes)
-  int occ_lds[2] = {-1, -1};
-  int occ_blocks[2] = {0, 0};
+  int occ_lds[3] = {-1, -1, -1};
+  int occ_blocks[3] = {0, 0, 0};
 };
 
 namespace {
@@ -860,6 +1409,8 @@ moe_status check_config(const moe_decode_config* c) {
   if (c->num_shared > 1) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
+
+constexpr size_t ctr_head_words(size_t) { return kCtrHead; }
 
 Params make_params(const moe_decode_handle* h, int T) {
   const moe_decode_config& c = h->cfg;
@@ -886,7 +1437,7 @@ Params make_params(const moe_decode_handle* h, int T) {
   p.pair_done = h->pair_done;
   const long long dl = c.deadline_us > 0 ? c.deadline_us : 1000000;
   p.deadline_ticks = dl * 100;   // wall clock runs at 100 MHz
-  p.n_eb = (p.E + kWaves - 1) / kWaves;
+  p.local_topk = T <= kLocalTopkRows ? 1 : 0;
   p.n_rb13 = p.I / 8;
   p.n_q13 = p.H / kTileK;
   p.n_rb2 = p.H / kTileRows;
@@ -894,17 +1445,18 @@ Params make_params(const moe_decode_handle* h, int T) {
   p.n_rg = (p.H + kDownRows - 1) / kDownRows;
   p.nch = (T + 63) / 64;
   p.n_mr_sh = p.S ? (T + kMRange - 1) / kMRange : 0;
-  p.n_router = p.n_eb * ((T + kRouterRows - 1) / kRouterRows);
-  p.n_topk = (T + kWaves - 1) / kWaves;
-  p.t_router_end = p.n_router;
-  p.t_sgu_end = p.t_router_end + p.n_mr_sh * p.n_rb13;
-  p.t_topk_end = p.t_sgu_end + p.n_topk;
-  p.t_sdn_end = p.t_topk_end + p.n_mr_sh * p.n_rg;
+  p.n_router = p.E * ((T + kRouterRows - 1) / kRouterRows);
+  p.n_topk = p.local_topk ? 0 : (T + kWaves - 1) / kWaves;
+  p.i_router_end = p.n_router;
+  p.i_sgu_end = p.i_router_end + p.n_mr_sh * p.n_rb13;
+  p.i_topk_end = p.i_sgu_end + p.n_topk;
+  p.n_sdn = p.n_mr_sh * p.n_rg;
   // LDS layout
   const int E = p.E, K = p.K;
   const int max_mr = E + (T * K + kMRange - 1) / kMRange;
+  const int nmb = T > kMBlock ? 4 : 1;
   size_t off = 0;
-  auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes, 16); return (int)o; };
+  auto take = [&](size_t bytes) __attribute__((always_inline)) { size_t o = off; off = align_up(off + bytes, 16); return (int)o; };
   p.lds_bm = take((size_t)E * p.nch * 8);
   p.lds_cp = take((size_t)E * p.nch * 4);
   p.lds_cnt = take((size_t)E * 4);
@@ -912,10 +1464,25 @@ Params make_params(const moe_decode_handle* h, int T) {
   p.lds_nmrb = take((size_t)(E + 1) * 4);
   p.lds_mrlist = take((size_t)max_mr * 4);
   p.lds_rows = take((size_t)T * K * 2);
-  const int nmb = T > kMBlock ? 4 : 1;
-  p.lds_red = take((size_t)kWaves * 4 * kWave * 16 * (nmb == 1 ? 1 : 1));
-  p.lds_comb = take((size_t)(kMRange + 2 * kMRange * kMaxTopK) * 4);
+  p.lds_tki = take((size_t)T * K * 2);
+  p.lds_tkw = take((size_t)T * K * 4);
   p.lds_misc = take(16 * 4);
+  p.lds_tks = take((size_t)kWaves * kWave * 4);
+  // small batches (every expert then has at most 16 rows: one MFMA block) keep
+  // x in LDS (rows padded by 16 bytes against bank conflicts) and stage each
+  // down item's h rows there as well
+  const size_t xs_stride = (size_t)p.H + 8;
+  if (T <= kMBlock && (size_t)T * xs_stride * 2 <= kXsMaxBytes) {
+    p.xs_stride = (int)xs_stride;
+    p.lds_xs = take((size_t)T * xs_stride * 2);
+    if (p.I <= kHsMaxI) p.hs_stride = p.I + 8;
+  }
+  // partial sums of the router and of gate/up items (two alternating halves)
+  p.lds_red = take((size_t)2 * kWaves * nmb * kWave * 16);
+  // one region used in turn by the routing logits and a down item's h rows
+  const size_t hs_bytes = p.hs_stride ? (size_t)std::min(T, kMBlock) * p.hs_stride * 2 : 0;
+  const size_t lg_bytes = p.local_topk ? (size_t)T * E * 4 : 0;
+  p.lds_hs = p.lds_lg = take(std::max(hs_bytes, lg_bytes));
   p.lds_bytes = (int)off;
   return p;
 }
@@ -988,11 +1555,13 @@ moe_status moe_decode_create(const moe_decode_config* cfg, const moe_decode_weig
     hipDeviceProp_t prop;
     if (hipGetDeviceProperties(&prop, device) != hipSuccess) { rc = MOE_ERR_HIP; break; }
     h->n_cu = prop.multiProcessorCount;
+    h->coop = prop.cooperativeLaunch;
     const size_t E = cfg->num_experts, S = cfg->num_shared, H = cfg->hidden,
                  I = cfg->intermediate, K = cfg->top_k, Tm = cfg->max_tokens;
     const size_t slots = E + S;
     const size_t n_rg = (H + kDownRows - 1) / kDownRows;
     const size_t scr_rows = Tm * K + Tm * S;
+    const size_t ctr_words = ctr_head_words(slots) + Tm * n_rg;
     struct A { void** p; size_t bytes; } allocs[] = {
         {(void**)&h->router_w, E * H * 4},
         {(void**)&h->router_b, w->router_bias ? E * 4 : 0},
@@ -1005,15 +1574,15 @@ moe_status moe_decode_create(const moe_decode_config* cfg, const moe_decode_weig
         {(void**)&h->topk_w, Tm * K * 4},
         {(void**)&h->h_scr, scr_rows * I * 2},
         {(void**)&h->o_scr, scr_rows * H * 4},
-        {(void**)&h->ctr, (kCtrHReady + slots + Tm * n_rg) * 4},
+        {(void**)&h->ctr, ctr_words * 4},
     };
     for (auto& a : allocs) {
       if (a.bytes == 0) continue;
       if (hipMalloc(a.p, a.bytes) != hipSuccess) { rc = MOE_ERR_OUT_OF_MEMORY; break; }
     }
     if (rc != MOE_OK) break;
-    h->pair_done = h->ctr + kCtrHReady + slots;
-    if (hipMemset(h->ctr, 0, (kCtrHReady + slots + Tm * n_rg) * 4) != hipSuccess) { rc = MOE_ERR_HIP; break; }
+    h->pair_done = h->ctr + ctr_head_words(slots);
+    if (hipMemset(h->ctr, 0, ctr_words * 4) != hipSuccess) { rc = MOE_ERR_HIP; break; }
     if (hipMemcpy(h->router_w, w->router_w, E * H * 4, hipMemcpyDeviceToDevice) != hipSuccess) { rc = MOE_ERR_HIP; break; }
     if (w->router_bias &&
         hipMemcpy(h->router_b, w->router_bias, E * 4, hipMemcpyDeviceToDevice) != hipSuccess) { rc = MOE_ERR_HIP; break; }
@@ -1054,14 +1623,22 @@ moe_status moe_decode_run(moe_decode_handle* h, const void* x, int32_t T, void* 
     p.dbg_rank = dbg->pair_rank;
     p.dbg_count = dbg->expert_count;
     p.dbg_logits = dbg->logits;
+    if (dbg->trace && dbg->trace_blocks > 0 && dbg->trace_cap > 0) {
+      p.trace = (long long*)dbg->trace;
+      p.trace_blocks = dbg->trace_blocks;
+      p.trace_cap = dbg->trace_cap;
+    }
   }
   hipStream_t stream = (hipStream_t)hip_stream;
   std::lock_guard<std::mutex> lock(h->mu);
   int prev = 0;
   HIP_TRY(hipGetDevice(&prev));
   if (prev != h->device) HIP_TRY(hipSetDevice(h->device));
-  const int variant = T > kMBlock ? 1 : 0;
-  const void* fn = variant ? (const void*)moe_decode_kernel<4> : (const void*)moe_decode_kernel<1>;
+  // variants: 0 = x in LDS, 1 = up to 16 rows, 2 = more rows (4 MFMA blocks per item)
+  const int variant = p.xs_stride > 0 ? 0 : (T > kMBlock ? 2 : 1);
+  const void* fn = variant == 0 ? (const void*)moe_decode_kernel<1, true>
+                 : variant == 1 ? (const void*)moe_decode_kernel<1, false>
+                                : (const void*)moe_decode_kernel<4, false>;
   if (h->occ_lds[variant] != p.lds_bytes) {
     int nb = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fn, kThreads, p.lds_bytes) != hipSuccess ||
@@ -1073,11 +1650,11 @@ moe_status moe_decode_run(moe_decode_handle* h, const void* x, int32_t T, void* 
     h->occ_blocks[variant] = nb;
   }
   const int grid = h->n_cu * h->occ_blocks[variant];
-  if (variant)
-    hipLaunchKernelGGL(moe_decode_kernel<4>, dim3(grid), dim3(kThreads), p.lds_bytes, stream, p);
-  else
-    hipLaunchKernelGGL(moe_decode_kernel<1>, dim3(grid), dim3(kThreads), p.lds_bytes, stream, p);
-  const hipError_t err = hipGetLastError();
+  // The grid is sized to what the device holds at once, so all workgroups
+  // are resident together on an otherwise idle device; every wait has a
+  // deadline for the case where they are not.
+  void* args[] = {&p};
+  const hipError_t err = hipLaunchKernel(fn, dim3(grid), dim3(kThreads), args, p.lds_bytes, stream);
   h->last_stream = stream;
   if (prev != h->device) (void)hipSetDevice(prev);
   return err == hipSuccess ? MOE_OK : MOE_ERR_HIP;
