@@ -112,7 +112,9 @@ typedef struct moe_decode_debug {
    * items recorded, workgroups in the grid}; row 1 + i: {ticket | kind << 32,
    * ticket granted, inputs ready (after any wait), item done}.  Times are
    * the 100 MHz device wall clock.  kind: 0 router, 1 shared gate/up,
-   * 2 top-k, 3 shared down, 4 routed gate/up, 5 routed down, 6 exit ticket.
+   * 2 top-k, 3 shared down, 4 routed gate/up, 5 routed down, 6 exit ticket,
+   * 7 combine; 8 and 9 time the phases of the workgroup's own routing
+   * (logits, top-k, placement).
    */
   int64_t* trace;
   int32_t trace_blocks;

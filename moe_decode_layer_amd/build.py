@@ -20,10 +20,14 @@ SYNTH_LIB = os.path.join(PKG, "synth", "_synth.so")
 HIP_SRCS = [os.path.join(PKG, "csrc", "moe_decode.hip")]
 HIP_LIB = os.path.join(PKG, "_moe_decode.so")
 
-# Packed fp32 instructions are kept out of every device build.
+# Packed fp32 instructions are kept out of every device build.  The device
+# compiler's atomic optimizer is off: it rewrites a one-lane fetch-add into a
+# wave-wide form that waits for the result right away, which would stall the
+# kernel's prefetched work claims.
 HIP_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Xarch_device", "-mllvm=-amdgpu-atomic-optimizer-strategy=None",
     "-Wall", "-Wno-unused-function",
     "-I", os.path.join(ROOT, "include"),
 ]

@@ -4,7 +4,7 @@
 // One launch runs the whole layer.  Every workgroup stays resident and walks
 // its own share of one global list of work items (item i belongs to
 // workgroup i mod G, taken in order); an item that needs earlier results
-// waits on a counter the producing items bump when done.  Blocks that stay
+// for a counter the producing items bump, then for the tags of its inputs.  Blocks that stay
 // resident across stages, pass ready results on through tagged buffers and
 // load weights while earlier stages still compute follow "FlyDSL Mono
 // Kernels for High-Interactivity LLM Serving in ATOM" (sections "What FlyDSL
@@ -23,10 +23,12 @@
 //   routed gate/up  : 16 weight rows of one routed expert      -- waits: routing
 //   shared down     : 128 output rows of the shared expert     -- waits: its gate/up
 //   routed down     : 128 output rows of one routed expert     -- waits: its gate/up
-// The weighted combine runs in whichever down item arrives last for a
-// (row, 128-column chunk).  A gate/up or down item covers up to 64 rows of
-// its expert (four 16-row MFMA blocks); experts with more rows get one item
-// per 64 rows.
+//   combine         : 4 rows x 128 columns of y                -- waits: the down
+//                                                                 items of those columns
+// A gate/up or down item covers up to 64 rows of its expert (four 16-row
+// MFMA blocks); experts with more rows get one item per 64 rows.  Results
+// handed between workgroups carry the run's epoch (tagged words), so a
+// producer never waits for its own stores: it bumps a counter and moves on.
 //
 // Expert weights are re-laid out once, at create time, into 1 KiB tiles of
 // 16 weight rows x 64 K: lane l of a wave reads bytes [16 l, 16 l + 16) of a
@@ -75,17 +77,24 @@ constexpr size_t kXsMaxBytes = 64 * 1024;   // x kept in LDS up to this size
 constexpr int kHsMaxI = 1024;               // h staged in LDS up to this intermediate width
 constexpr int kFullTiles = 16;              // tiles per wave of the fully unrolled items (H 4096, I 512)
 
-// counter block (int32 words)
-constexpr int kCtrRouterDone = 0;
-constexpr int kCtrTopkDone = 16;
-constexpr int kCtrExit = 32;
-constexpr int kCtrStatus = 48;
-constexpr int kCtrHReady = 64;              // [E+S] (E+S <= 257)
-// "go" flags raised once by the last producer and polled by many workgroups:
-// kGoLines copies, 1 KiB apart, so the pollers spread over memory channels
+constexpr int kCombineRows = 4;             // rows per combine item
+// Counter block (int32 words).  Every counter sits on a 256-byte line of its
+// own (kLine words apart): a line many workgroups poll or bump must not also
+// carry another hot word.
+constexpr int kLine = 64;
+constexpr int kCtrRouterDone = 0 * kLine;   // router items done
+constexpr int kCtrTopkDone = 1 * kLine;     // distributed top-k items done
+constexpr int kCtrExit = 2 * kLine;
+constexpr int kCtrStatus = 3 * kLine;
+constexpr int kCtrTicket = 4 * kLine;       // next unclaimed item of the list
+constexpr int kCtrHReady = 5 * kLine;       // [E+S] gate/up publications per expert (E+S <= 257)
+constexpr int kCtrRgDone = kCtrHReady + 257 * kLine;   // [H/128] down-wave publications (<= 128)
+// "go" flags raised once by the last router item and by the last
+// distributed top-k item, polled by every workgroup: kGoLines copies, 1 KiB
+// apart, so the pollers spread over memory channels
 constexpr int kGoLines = 64;
 constexpr int kGoStride = 256;              // words
-constexpr int kCtrRouterGo = 512;
+constexpr int kCtrRouterGo = kCtrRgDone + 128 * kLine;
 constexpr int kCtrTopkGo = kCtrRouterGo + kGoLines * kGoStride;
 constexpr int kCtrHead = kCtrTopkGo + kGoLines * kGoStride;
 
@@ -111,14 +120,15 @@ struct Params {
   const float* s13p;   // [E+S][2I/16][H/64][16][2]
   const u32x4* w2p;    // [E+S][H/16][I/64][64]
   const float* s2p;    // [E+S][H/16][I/64][16][2]
-  // workspace
-  float* logits;       // [T][E]
+  // workspace.  Words handed between workgroups carry the run's epoch in
+  // their high half (see "Tagged hand-offs" below).
+  uint64_t* lgt;       // [T][E] router logits (fp32 bits | epoch)
   int* topk_idx;       // [T][K]  (distributed top-k only)
   float* topk_w;       // [T][K]
-  uint16_t* h_scr;     // [T*K + T*S][I] bf16, rows grouped by expert
-  float* o_scr;        // [T*K + T*S][H]
+  uint64_t* h_scr;     // [T*K + T*S][I/2] two bf16 of h | epoch, rows grouped by expert
+  uint64_t* o_scr;     // [T*K + T*S][H] expert outputs (fp32 bits | epoch)
   int* ctr;            // counters
-  int* pair_done;      // [T][n_rg]
+  uint32_t epoch;      // this run's tag, never 0 (the workspace starts zeroed)
   // debug copies (nullable)
   int* dbg_idx;
   float* dbg_w;
@@ -141,8 +151,9 @@ struct Params {
   int n_router, n_topk;
   int i_router_end, i_sgu_end, i_topk_end;
   int n_sdn;           // shared down items
+  int n_cmb;           // combine items: ceil(T / kCombineRows) * n_rg
   // LDS offsets (bytes)
-  int lds_bm, lds_cp, lds_cnt, lds_base, lds_nmrb, lds_mrlist, lds_rows, lds_tki, lds_tkw,
+  int lds_bm, lds_cp, lds_cnt, lds_base, lds_nmrb, lds_mrlist, lds_rows, lds_tki, lds_prow, lds_tkw,
       lds_red, lds_misc, lds_tks, lds_xs, lds_hs, lds_lg;
   int lds_bytes;
   int xs_stride;       // x rows in LDS (bf16 elements per row), 0 when x stays in global memory
@@ -263,6 +274,54 @@ __device__ __forceinline__ u32x4 ld_coh16(const void* p) {
 // Wait until this wave's outstanding memory operations are acknowledged.
 __device__ __forceinline__ void wait_stores() { __builtin_amdgcn_s_waitcnt(0); }
 
+// Tagged hand-offs.  Logits, h and expert outputs travel as 64-bit words:
+// 32 bits of payload, and the run's epoch in the high half.  A 64-bit store
+// is single-copy atomic, so a reader that sees the current epoch sees the
+// payload written with it.  The producer therefore never waits for its
+// stores before it counts itself done (the count only tells readers when to
+// look); a reader that finds a stale tag reads the word again.
+__device__ __forceinline__ void st_tag(uint64_t* p, uint32_t v, uint32_t epoch) {
+  __hip_atomic_store((GLOBAL uint64_t*)p, (uint64_t)epoch << 32 | v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t ld_tag(const uint64_t* p) {
+  return __hip_atomic_load((GLOBAL uint64_t*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ bool tag_ok(uint64_t v, uint32_t epoch) { return (uint32_t)(v >> 32) == epoch; }
+// Counter bump whose result is not needed (no return trip is waited for).
+__device__ __forceinline__ void count_done(int* p) {
+  __hip_atomic_fetch_add((GLOBAL int*)p, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// s_waitcnt vmcnt(n) (n <= 63), leaving the LDS and export counters alone:
+// every vector memory operation of this wave except the n most recent is done.
+template <int N>
+__device__ __forceinline__ void wait_vm_older_than() {
+  static_assert(N >= 0 && N <= 63, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// A down wave counts itself in for its column group only once its output
+// stores have landed, so a combine that sees the count finds the outputs
+// tagged on its first read.  To keep the wave from stalling on that, the
+// count is deferred ("pending") to the next item, right after that item has
+// issued its own loads (N of them): waiting then for everything older costs
+// nothing.  Items that issue no loads first flush with a full wait.
+template <int N>
+__device__ __forceinline__ void flush_pending(KParams& p, int& pend) {
+  if (pend >= 0) {
+    wait_vm_older_than<N>();
+    if (lane_id() == 0) count_done(p.ctr + kCtrRgDone + pend * kLine);
+    pend = -1;
+  }
+}
+__device__ __forceinline__ void flush_pending_now(KParams& p, int& pend) {
+  if (pend >= 0) {
+    wait_stores();
+    if (lane_id() == 0) count_done(p.ctr + kCtrRgDone + pend * kLine);
+    pend = -1;
+  }
+}
+
 // The copy of a go flag this workgroup polls.
 __device__ __forceinline__ int* go_flag(int* base) { return base + (blockIdx.x % kGoLines) * kGoStride; }
 
@@ -280,11 +339,13 @@ __device__ void publish_done(int* ctr, int target = 0, int* flag = nullptr) {
   }
 }
 
-// Workgroup-wide wait until *ctr >= target.  Thread 0 spins (with a pause
-// that grows to ~0.4 us) under a deadline; the result is broadcast through
-// LDS, and the barrier orders every wave's later (coherent) loads after it.
-// false: deadline passed or another workgroup reported an error.
-__device__ bool wait_geq(KParams& p, int* ctr, int target, SHARED int* lds_flag) {
+// Workgroup-wide wait until *ctr >= target.  Thread 0 polls under a
+// deadline; the pause between polls starts at ~0.05 us and, after max_fast
+// short ones, doubles up to ~0.9 us, so long waits load the polled line
+// lightly.  The result is broadcast through LDS, and the barrier orders
+// every wave's later loads after it.  false: deadline passed or another
+// workgroup reported an error.
+__device__ bool wait_geq(KParams& p, int* ctr, int target, SHARED int* lds_flag, int max_fast = 8) {
   if (threadIdx.x == 0) {
     int ok = 1;
     if (load_agent(ctr) < target) {
@@ -301,11 +362,18 @@ __device__ bool wait_geq(KParams& p, int* ctr, int target, SHARED int* lds_flag)
           ok = 0;
           break;
         }
-        __builtin_amdgcn_s_sleep(8);
+        const int step = spins - max_fast;
+        if (step < 0) __builtin_amdgcn_s_sleep(2);
+        else if (step < 2) __builtin_amdgcn_s_sleep(4);
+        else if (step < 4) __builtin_amdgcn_s_sleep(8);
+        else if (step < 6) __builtin_amdgcn_s_sleep(16);
+        else __builtin_amdgcn_s_sleep(32);
         ++spins;
       }
     }
     *lds_flag = ok;
+    // when the last wait ended (read back by the same thread for the timeline)
+    *(SHARED long long*)(lds_flag + 11) = (long long)wall_clock64();
   }
   __syncthreads();
   const int ok = *lds_flag;
@@ -332,6 +400,42 @@ __device__ __forceinline__ void batched_copy(int n, LoadFn load, StoreFn store) 
       if (i < n) store(i, v[b]);
     }
   }
+}
+
+// Workgroup-wide OR of one predicate per thread (slots: kWaves LDS words).
+__device__ __forceinline__ bool block_any(bool v, SHARED int* slots) {
+  const unsigned long long b = __ballot(v);
+  if (lane_id() == 0) slots[wave_id()] = b != 0ull;
+  __syncthreads();
+  int any = 0;
+#pragma unroll
+  for (int i = 0; i < kWaves; ++i) any |= slots[i];
+  __syncthreads();
+  return any != 0;
+}
+
+// Thread 0 checks the deadline (started at *t_end == 0) and the error status
+// between polling rounds, then pauses; the verdict is broadcast through LDS.
+__device__ bool poll_round(KParams& p, long long* t_end, SHARED int* lds_flag) {
+  if (threadIdx.x == 0) {
+    int ok = 1;
+    const long long now = (long long)wall_clock64();
+    if (*t_end == 0) *t_end = now + p.deadline_ticks;
+    if (now > *t_end) {
+      int expected = 0;
+      __hip_atomic_compare_exchange_strong((GLOBAL int*)(p.ctr + kCtrStatus), &expected, MOE_ERR_TIMEOUT,
+                                           __ATOMIC_RELAXED, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      ok = 0;
+    } else if (load_agent(p.ctr + kCtrStatus) != 0) {
+      ok = 0;
+    }
+    __builtin_amdgcn_s_sleep(4);
+    *lds_flag = ok;
+  }
+  __syncthreads();
+  const int ok = *lds_flag;
+  __syncthreads();
+  return ok != 0;
 }
 
 // Block-wide exclusive prefix sum of one int per thread (kThreads values).
@@ -376,9 +480,11 @@ struct Lds {
   SHARED int* mrlist;             // [n_mr] expert of each routed M-range
   SHARED int16_t* rows;           // [T*K] scratch row -> token, grouped by expert
   SHARED int16_t* tki;            // [T][K] selected experts
+  SHARED int* prow;               // [T][K] scratch row of each pair (its expert output row)
   SHARED float* tkw;              // [T][K] their weights
   SHARED float* red;              // partial sums of the 4 waves
-  SHARED int* misc;               // [0] n_mr, [1] flag, [3..7) scan scratch
+  SHARED int* misc;               // [0] n_mr, [1] flag, [3..7) scan scratch, [8..12) block_any,
+                                  // [2] claimed item, [12..14) end of the last wait (thread 0)
   SHARED uint32_t* tks;           // [kWaves][64] top-k scratch of each wave
   SHARED uint16_t* xs;            // [T][xs_stride] the layer input (small batches)
   SHARED uint16_t* hs;            // [16][hs_stride] h rows of the current down item
@@ -395,6 +501,7 @@ __device__ Lds lds_view(KParams& p, SHARED char* smem) {
   L.mrlist = (SHARED int*)(smem + p.lds_mrlist);
   L.rows = (SHARED int16_t*)(smem + p.lds_rows);
   L.tki = (SHARED int16_t*)(smem + p.lds_tki);
+  L.prow = (SHARED int*)(smem + p.lds_prow);
   L.tkw = (SHARED float*)(smem + p.lds_tkw);
   L.red = (SHARED float*)(smem + p.lds_red);
   L.misc = (SHARED int*)(smem + p.lds_misc);
@@ -403,6 +510,34 @@ __device__ Lds lds_view(KParams& p, SHARED char* smem) {
   L.hs = (SHARED uint16_t*)(smem + p.lds_hs);
   L.lg = (SHARED float*)(smem + p.lds_lg);
   return L;
+}
+
+// Gather n tagged words of this run with the whole workgroup: take(i, payload)
+// is called for every i whose word carries the current epoch (possibly more
+// than once); stale words are read again, round by round, until none is.
+// kBatch loads per thread are in flight before any is examined.  false: the
+// deadline passed or another workgroup reported an error.
+template <typename LoadFn, typename TakeFn>
+__device__ __forceinline__ bool gather_tagged(KParams& p, const Lds& L, int n, LoadFn load, TakeFn take) {
+  long long t_end = 0;
+  while (true) {
+    bool stale = false;
+    for (int i0 = threadIdx.x; i0 < n; i0 += kBatch * kThreads) {
+      uint64_t v[kBatch];
+#pragma unroll
+      for (int b = 0; b < kBatch; ++b) v[b] = load(min(i0 + b * kThreads, n - 1));
+#pragma unroll
+      for (int b = 0; b < kBatch; ++b) {
+        const int i = i0 + b * kThreads;
+        if (i < n) {
+          if (tag_ok(v[b], p.epoch)) take(i, (uint32_t)v[b]);
+          else stale = true;
+        }
+      }
+    }
+    if (!block_any(stale, L.misc + 8)) return true;
+    if (!poll_round(p, &t_end, L.misc + 1)) return false;
+  }
 }
 
 // Sort-free placement ("routing without sorting": each expert's rows go to
@@ -450,6 +585,7 @@ __device__ __forceinline__ void build_placement(KParams& p, const Lds& L) {
     const unsigned long long below = L.bm[e * nch + (t >> 6)] & ((1ull << (t & 63)) - 1ull);
     const int rank = L.cp[e * nch + (t >> 6)] + __popcll(below);
     L.rows[L.base[e] + rank] = (int16_t)t;
+    L.prow[i] = L.base[e] + rank;
   }
   __syncthreads();
 }
@@ -479,29 +615,46 @@ __device__ __forceinline__ void router_item(KParams& p, const Lds& L, int item) 
   const int e = item % p.E;
   const int t0 = (item / p.E) * kRouterRows;
   const int nt = min(kRouterRows, p.T - t0);
-  const int nc = p.H / 4;                      // 4-element chunks
-  const int c_lo = w * (nc / kWaves), c_hi = c_lo + nc / kWaves;
+  const int n16 = p.H / 16;                    // 16-element chunks
   float acc[kRouterRows];
 #pragma unroll
   for (int j = 0; j < kRouterRows; ++j) acc[j] = 0.f;
   const f32x4* wr = (const f32x4*)(p.router_w + (size_t)e * p.H);
-  const bool xl = false;                       // x in LDS is staged after the router
-  const u32x2* xg[kRouterRows];                // rows past nt reread the last row
-  const SHARED u32x2* xsh[kRouterRows];
+  const u32x4* xg[kRouterRows];                // rows past nt reread the last row
 #pragma unroll
-  for (int j = 0; j < kRouterRows; ++j) {
-    const int t = t0 + min(j, nt - 1);
-    xg[j] = (const u32x2*)(p.x + (size_t)t * p.H);
-    xsh[j] = (const SHARED u32x2*)(L.xs + (size_t)t * p.xs_stride);
-  }
-#pragma unroll 4
-  for (int c = c_lo + lane; c < c_hi; c += kWave) {
-    const f32x4 wv = ld(wr + c);
+  for (int j = 0; j < kRouterRows; ++j) xg[j] = (const u32x4*)(p.x + (size_t)(t0 + min(j, nt - 1)) * p.H);
+  // each thread owns 16 consecutive elements per pass; a pass issues all of
+  // its loads (4 x 16 B of weights, 2 x 16 B per row) before the first use
+  for (int c0 = 0; c0 < n16; c0 += kThreads) {
+    const int c = min(c0 + (int)threadIdx.x, n16 - 1);
+    const bool live = c0 + (int)threadIdx.x < n16;
+    f32x4 wv[4];
+    u32x4 xv[kRouterRows][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) wv[i] = ld(wr + 4 * c + i);
 #pragma unroll
     for (int j = 0; j < kRouterRows; ++j) {
-      const u32x2 xv = xl ? xsh[j][c] : ld(xg[j] + c);
-      acc[j] += wv.x * bf16_to_f32(xv.x & 0xffffu) + wv.y * bf16_to_f32(xv.x >> 16) +
-                wv.z * bf16_to_f32(xv.y & 0xffffu) + wv.w * bf16_to_f32(xv.y >> 16);
+      xv[j][0] = ld(xg[j] + 2 * c);
+      xv[j][1] = ld(xg[j] + 2 * c + 1);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+      wv[i] = live ? wv[i] : z;
+    }
+#pragma unroll
+    for (int j = 0; j < kRouterRows; ++j) {
+      float a = acc[j];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const u32x4 xw = xv[j][h];
+        const f32x4 w0 = wv[2 * h], w1 = wv[2 * h + 1];
+        a += w0.x * bf16_to_f32(xw.x & 0xffffu) + w0.y * bf16_to_f32(xw.x >> 16) +
+             w0.z * bf16_to_f32(xw.y & 0xffffu) + w0.w * bf16_to_f32(xw.y >> 16);
+        a += w1.x * bf16_to_f32(xw.z & 0xffffu) + w1.y * bf16_to_f32(xw.z >> 16) +
+             w1.z * bf16_to_f32(xw.w & 0xffffu) + w1.w * bf16_to_f32(xw.w >> 16);
+      }
+      acc[j] = a;
     }
   }
   SHARED float* part = L.red;                  // [kWaves][8]
@@ -511,27 +664,37 @@ __device__ __forceinline__ void router_item(KParams& p, const Lds& L, int item) 
     if (lane == 0) part[w * kRouterRows + j] = s;
   }
   __syncthreads();
+  float s = 0.f;
   if (threadIdx.x < nt) {
     const int j = threadIdx.x;
-    float s = part[j];
+    s = part[j];
 #pragma unroll
     for (int ww = 1; ww < kWaves; ++ww) s += part[ww * kRouterRows + j];
     s += p.router_b ? ld(p.router_b + e) : 0.f;
-    st_coh(p.logits + (size_t)(t0 + j) * p.E + e, s);
+  }
+  __syncthreads();                             // the partials area is free again
+  if (threadIdx.x < nt) {
+    const int j = threadIdx.x;
+    st_tag(p.lgt + (size_t)(t0 + j) * p.E + e, __float_as_uint(s), p.epoch);
     if (p.dbg_logits) st(p.dbg_logits + (size_t)(t0 + j) * p.E + e, s);
   }
+  // the last router item raises the go flags (no store needs to be waited
+  // for first: the readers check the tags)
+  if (threadIdx.x == 0 && atomic_add_agent(p.ctr + kCtrRouterDone, 1) == p.n_router - 1)
+    for (int i = 0; i < kGoLines; ++i) store_agent(p.ctr + kCtrRouterGo + i * kGoStride, 1);
 }
 
 // ----------------------------------------------------------------------------
-// Top-k of one row (one wave).  Lane l holds experts l, l+64, l+128, l+192 as
+// Top-k of a row in one wave.  Lane l holds experts 4l .. 4l+3 as
 // order-preserving unsigned keys of their logits (ranking by logit equals
-// ranking by sigmoid score).  A 32-step radix select over ballots finds the
-// K-th largest key; every larger key is selected, then the lowest-id keys
-// equal to it.  The K picks are ordered by (key desc, id asc) through LDS.
+// ranking by sigmoid score).  K rounds each take the wave maximum key and,
+// among its holders, the lowest expert id (the lowest lane, then its lowest
+// slot), then retire it: the picks come out in (score desc, id asc) order.
 // Weights: sigmoid of the selected logits over their sum.
 // ----------------------------------------------------------------------------
 __device__ __forceinline__ uint32_t order_ukey(float v) {
-  // NaN maps to 1, just above absent experts (0), so it never displaces a score
+  // NaN maps to 1, just above absent and retired experts (0), so it never
+  // displaces a score
   if (v != v) return 1u;
   const int b = __float_as_int(v);
   const int k = b >= 0 ? b : (b ^ 0x7fffffff);
@@ -541,192 +704,213 @@ __device__ __forceinline__ float ukey_value(uint32_t u) {
   const int k = (int)(u ^ 0x80000000u);
   return __int_as_float(k >= 0 ? k : (k ^ 0x7fffffff));
 }
+// Maximum / minimum over the 64 lanes, returned in every lane, all in vector
+// registers: DPP within each 16-lane row, then the gfx950 lane swaps across
+// rows (32 apart, then 16 apart).  No scalar register carries the result, so
+// independent reductions of one wave overlap.
+__device__ __forceinline__ uint32_t wave_max_v(uint32_t v) {
+  v = max(v, dpp<kDppXor1>(v));
+  v = max(v, dpp<kDppXor2>(v));
+  v = max(v, dpp<kDppHalfMirror>(v));
+  v = max(v, dpp<kDppMirror>(v));
+  const auto a = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  v = max(a[0], a[1]);
+  const auto b = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  return max(b[0], b[1]);
+}
+__device__ __forceinline__ uint32_t wave_min_v(uint32_t v) {
+  v = min(v, dpp<kDppXor1>(v));
+  v = min(v, dpp<kDppXor2>(v));
+  v = min(v, dpp<kDppHalfMirror>(v));
+  v = min(v, dpp<kDppMirror>(v));
+  const auto a = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  v = min(a[0], a[1]);
+  const auto b = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  return min(b[0], b[1]);
+}
 
-// Top-k of NR rows at once in one wave (their radix searches interleave).
-// Row r's logits come from LDS (lg, [T][E]) or, with lg == nullptr, from
-// global memory.  Returns, in lanes k < K, row r's k-th expert and weight.
+// Top-k of NR rows at once in one wave (their rounds interleave).  Row r's
+// logits are lg[t[r]][0..E) in LDS.  Returns, in lanes k < K, row r's k-th
+// expert and weight.
 template <int NR>
 __device__ __forceinline__ void topk_rows(KParams& p, const SHARED float* lg, const int (&t)[NR],
                                           int (&out_e)[NR], float (&out_w)[NR]) {
-  const int lane = lane_id();
+  const uint32_t lane = lane_id();
   const int K = p.K;
   uint32_t uk[NR][4];
 #pragma unroll
   for (int r = 0; r < NR; ++r)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int e = lane + kWave * j;
-      const float v = e < p.E ? (lg ? lg[t[r] * p.E + e] : ld_coh(p.logits + (size_t)t[r] * p.E + e)) : 0.f;
+      const int e = 4 * lane + j;
+      const float v = lg[t[r] * p.E + min(e, p.E - 1)];
       uk[r][j] = e < p.E ? order_ukey(v) : 0u;
     }
-  // radix select: thr[r] = the K-th largest key of row r
-  uint32_t thr[NR];
+  uint32_t sel_k[NR], sel_e[NR];
 #pragma unroll
-  for (int r = 0; r < NR; ++r) thr[r] = 0;
-  for (int bit = 31; bit >= 0; --bit) {
+  for (int r = 0; r < NR; ++r) sel_k[r] = sel_e[r] = 0;
+  for (int k = 0; k < K; ++k) {
+    uint32_t M[NR], W[NR];
 #pragma unroll
     for (int r = 0; r < NR; ++r) {
-      const uint32_t cand = thr[r] | (1u << bit);
-      int c = 0;
+      const uint32_t m = max(max(uk[r][0], uk[r][1]), max(uk[r][2], uk[r][3]));
+      M[r] = wave_max_v(m);
+      // lowest expert id holding the maximum: ids 4 lane + j grow with lane, then j
+      const uint32_t fj = uk[r][0] == M[r] ? 0u : uk[r][1] == M[r] ? 1u : uk[r][2] == M[r] ? 2u : 3u;
+      W[r] = wave_min_v(m == M[r] ? 4 * lane + fj : 0xffffu);
+    }
 #pragma unroll
-      for (int j = 0; j < 4; ++j) c += __popcll(__ballot(uk[r][j] >= cand));
-      thr[r] = c >= K ? cand : thr[r];
+    for (int r = 0; r < NR; ++r) {
+      sel_k[r] = lane == (uint32_t)k ? M[r] : sel_k[r];
+      sel_e[r] = lane == (uint32_t)k ? W[r] : sel_e[r];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) uk[r][j] = 4 * lane + j == W[r] ? 0u : uk[r][j];
     }
   }
 #pragma unroll
   for (int r = 0; r < NR; ++r) {
-    // selection: every key above the threshold, then the lowest ids equal to it
-    int need = K;
-    unsigned long long sel[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      sel[j] = __ballot(uk[r][j] > thr[r]);
-      need -= __popcll(sel[j]);
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      unsigned long long m = __ballot(uk[r][j] == thr[r]);
-      while (need > 0 && m) {
-        const unsigned long long low = m & (~m + 1ull);
-        sel[j] |= low;
-        m ^= low;
-        --need;
-      }
-    }
-    // move the K picks to lanes 0..K-1 (in id order): pick i of the wave goes
-    // to lane i through a readlane from its owner
-    uint32_t my_k = 0, my_e = 0;
-    int base = 0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      unsigned long long m = sel[j];
-      while (m) {
-        const int src = __ffsll((long long)m) - 1;
-        m &= m - 1;
-        const uint32_t kk = (uint32_t)__builtin_amdgcn_readlane((int)uk[r][j], src);
-        if (lane == base) { my_k = kk; my_e = (uint32_t)(src + kWave * j); }
-        ++base;
-      }
-    }
-    // rank among the picks: key descending, id ascending
-    int rank = 0;
-#pragma unroll
-    for (int i = 0; i < kMaxTopK; ++i) {
-      if (i < K) {
-        const uint32_t ki = (uint32_t)__builtin_amdgcn_readlane((int)my_k, i);
-        const uint32_t ei = (uint32_t)__builtin_amdgcn_readlane((int)my_e, i);
-        rank += (ki > my_k) || (ki == my_k && ei < my_e);
-      }
-    }
-    // lane k takes the pick of rank k
-    uint32_t out_k = 0, oe = 0;
-#pragma unroll
-    for (int i = 0; i < kMaxTopK; ++i) {
-      if (i < K) {
-        const int ri = __builtin_amdgcn_readlane(rank, i);
-        const uint32_t ki = (uint32_t)__builtin_amdgcn_readlane((int)my_k, i);
-        const uint32_t ei = (uint32_t)__builtin_amdgcn_readlane((int)my_e, i);
-        if (lane == ri) { out_k = ki; oe = ei; }
-      }
-    }
-    const float s = lane < K ? 1.0f / (1.0f + __expf(-ukey_value(out_k))) : 0.f;
+    const float s = (int)lane < K ? 1.0f / (1.0f + __expf(-ukey_value(sel_k[r]))) : 0.f;
     const float sum = wave_sum(s);
-    out_e[r] = (int)oe;
+    out_e[r] = (int)sel_e[r];
     out_w[r] = s / sum;
   }
 }
 
-// One row (distributed top-k items).
-__device__ __forceinline__ void topk_row(KParams& p, const Lds& L, int t, int* out_e, float* out_w) {
-  const int tr[1] = {t};
-  int e[1];
-  float w[1];
-  topk_rows<1>(p, nullptr, tr, e, w);
-  *out_e = e[0];
-  *out_w = w[0];
+// Copy rows [t0, t0 + nt) of this run's router logits into LDS lg (row-major,
+// from row 0) once every one of them carries the current epoch.
+__device__ __forceinline__ bool gather_logits(KParams& p, const Lds& L, int t0, int nt) {
+  return gather_tagged(p, L, nt * p.E, [&](int i) { return ld_tag(p.lgt + (size_t)t0 * p.E + i); },
+                       [&](int i, uint32_t v) { L.lg[i] = __uint_as_float(v); });
 }
 
-// Distributed top-k item: rows 4 item .. 4 item + 3, one per wave, to global.
-__device__ __forceinline__ void topk_item(KParams& p, const Lds& L, int item) {
-  const int t = item * kWaves + wave_id();
-  if (t >= p.T) return;
-  int e;
-  float wk;
-  topk_row(p, L, t, &e, &wk);
-  if (lane_id() < p.K) {
-    st_coh(p.topk_idx + t * p.K + lane_id(), e);
-    st_coh(p.topk_w + t * p.K + lane_id(), wk);
+// Distributed top-k item (large batches): rows 4 item .. 4 item + 3, one per
+// wave, to global memory.
+__device__ __forceinline__ bool topk_item(KParams& p, const Lds& L, int item) {
+  const int t0 = item * kWaves;
+  const int nt = min(kWaves, p.T - t0);
+  __syncthreads();                             // earlier readers of the lg area are done
+  if (!gather_logits(p, L, t0, nt)) return false;
+  __syncthreads();
+  const int w = wave_id();
+  if (w < nt) {
+    const int tr[1] = {w};
+    int e[1];
+    float wk[1];
+    topk_rows<1>(p, L.lg, tr, e, wk);
+    if (lane_id() < p.K) {
+      st_coh(p.topk_idx + (t0 + w) * p.K + lane_id(), e[0]);
+      st_coh(p.topk_w + (t0 + w) * p.K + lane_id(), wk[0]);
+    }
   }
+  return true;
 }
 
-// A down item's h rows (nrows x I bf16, written by other workgroups) into LDS.
-__device__ __forceinline__ void stage_h_rows(KParams& p, const Lds& L, int row0, int nrows) {
-  const int per_row = p.I / 4;                // 8-byte words per row
-  batched_copy<uint64_t>(
-      nrows * per_row,
-      [&](int i) {
-        return __hip_atomic_load((GLOBAL uint64_t*)(p.h_scr + (size_t)(row0 + i / per_row) * p.I) + i % per_row,
-                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      },
-      [&](int i, uint64_t v) { *(SHARED uint64_t*)(L.hs + (size_t)(i / per_row) * p.hs_stride + 4 * (i % per_row)) = v; });
+// A down item's h rows (nrows x I bf16, written by other workgroups) into
+// LDS, once each word carries this run's epoch.
+__device__ __forceinline__ bool stage_h_rows(KParams& p, const Lds& L, int row0, int nrows) {
+  const int per_row = p.I / 2;                // tagged words per row
+  return gather_tagged(
+      p, L, nrows * per_row, [&](int i) { return ld_tag(p.h_scr + (size_t)row0 * per_row + i); },
+      [&](int i, uint32_t v) { *(SHARED uint32_t*)(L.hs + (size_t)(i / per_row) * p.hs_stride + 2 * (i % per_row)) = v; });
+}
+
+// Wait until every word of h rows [row0, row0 + nrows) carries this run's
+// epoch (down items that read h straight from global memory).
+__device__ __forceinline__ bool verify_h_rows(KParams& p, const Lds& L, int row0, int nrows) {
+  const int per_row = p.I / 2;
+  return gather_tagged(p, L, nrows * per_row, [&](int i) { return ld_tag(p.h_scr + (size_t)row0 * per_row + i); },
+                       [&](int, uint32_t) {});
+}
+
+// 8 consecutive bf16 of a tagged h row (4 words): the payload halves.
+__device__ __forceinline__ u32x4 ld_h8(const uint64_t* w) {
+  const u32x4 a = ld_coh16(w), b = ld_coh16(w + 2);
+  return (u32x4){a.x, a.z, b.x, b.z};
 }
 
 // ----------------------------------------------------------------------------
-// Down-item epilogue of one wave: after its o rows are stored, the wave counts
-// itself in for each of its rows t at (t, row group rg); the wave that
-// completes a (t, rg) -- all K+S expert outputs times the waves covering the
-// group -- combines it: y[t][rg*128 .. +128) = bf16(o_shared + sum_k w_k o_k),
-// summed in that fixed order.
+// Down-wave epilogue: each wave stores its output rows as tagged words and
+// counts itself in for its 128-column group (no wait for the stores).
 // ----------------------------------------------------------------------------
-__device__ __forceinline__ void wave_arrive_combine(KParams& p, const Lds& L, int sbase, int r0,
-                                                    int nrows, int rg, bool shared) {
-  const int lane = lane_id();
+__device__ __forceinline__ int down_waves_in_group(KParams& p, int rg) {
+  const int nc = min(kDownRows, p.H - rg * kDownRows);
+  return min(kWaves, (nc + 2 * kTileRows - 1) / (2 * kTileRows));
+}
+
+// ----------------------------------------------------------------------------
+// Combine item: rows [4 rc, 4 rc + 4) x columns [128 rg, 128 rg + 128) of
+//   y[t] = bf16( o_shared[t] + sum_k w[t][k] o_{idx[t][k]}[t] ),
+// summed in exactly that order, once every down wave of column group rg has
+// counted in and every expert output read carries this run's epoch.
+// ----------------------------------------------------------------------------
+__device__ __forceinline__ bool combine_item(KParams& p, const Lds& L, int rc, int rg, int n_mr) {
+  constexpr int kOut = kCombineRows * kDownRows / kThreads;   // outputs per thread (2)
+  constexpr int kIn = kMaxTopK + 1;                           // inputs per output: K routed, shared last
   const int K = p.K;
   const int c0 = rg * kDownRows;
   const int nc = min(kDownRows, p.H - c0);
-  const int waves_in_group = min(kWaves, (nc + 2 * kTileRows - 1) / (2 * kTileRows));
-  const int target = (K + p.S) * waves_in_group;
-  wait_stores();
-  int t = 0;
-  bool last = false;
-  if (lane < nrows) {
-    t = shared ? (r0 + lane) : (int)L.rows[sbase + r0 + lane];
-    last = atomic_add_agent(p.pair_done + t * p.n_rg + rg, 1) == target - 1;
+  const int t0 = rc * kCombineRows;
+  const int nt = min(kCombineRows, p.T - t0);
+  long long t_end = 0;
+  // Many combine items (large batches) first wait for the column group's
+  // count, so they do not poll expert outputs that are still far from done;
+  // a few items poll the outputs' tags directly, re-reading only stale words.
+  if (p.n_cmb > 128) {
+    const int target = (n_mr + p.n_mr_sh) * down_waves_in_group(p, rg);
+    if (!wait_geq(p, p.ctr + kCtrRgDone + rg * kLine, target, L.misc + 1)) return false;
   }
-  unsigned long long todo = __ballot(last);
-  while (todo) {
-    const int src = __ffsll((long long)todo) - 1;
-    todo &= todo - 1;
-    const int tt = __shfl(t, src, kWave);
-    constexpr int kCols = kDownRows / kWave;   // columns per lane
-    // all K+S expert outputs are requested before any is summed (one round trip)
-    float o[kMaxTopK + 1][kCols];
-    float wk[kMaxTopK];
+  int tt[kOut];
+  bool live[kOut];
+  const uint64_t* src[kOut];
 #pragma unroll
-    for (int k = 0; k < kMaxTopK; ++k) {
-      if (k < K) {
-        const int e = L.tki[tt * K + k];
-        const int row = L.base[e] + pair_rank(p, L, tt, e);
-        wk[k] = L.tkw[tt * K + k];
+  for (int j = 0; j < kOut; ++j) {
+    const int o = threadIdx.x + kThreads * j;
+    const int r = o / kDownRows, c = o % kDownRows;
+    live[j] = r < nt && c < nc;
+    tt[j] = t0 + min(r, nt - 1);
+    src[j] = p.o_scr + c0 + min(c, nc - 1);
+  }
+  const uint64_t fresh = (uint64_t)p.epoch << 32;   // tag-only stand-in for a missing shared expert
+  uint64_t v[kOut][kIn];
 #pragma unroll
-        for (int i = 0; i < kCols; ++i)
-          o[k][i] = ld_coh(p.o_scr + (size_t)row * p.H + c0 + min(lane + kWave * i, nc - 1));
+  for (int j = 0; j < kOut; ++j)
+#pragma unroll
+    for (int k = 0; k < kIn; ++k) v[j][k] = 0;
+  while (true) {
+    bool stale = false;
+#pragma unroll
+    for (int j = 0; j < kOut; ++j) {
+#pragma unroll
+      for (int k = 0; k < kIn; ++k) {
+        if (k < K || k == kMaxTopK) {
+          if (!tag_ok(v[j][k], p.epoch)) {
+            if (k == kMaxTopK)
+              v[j][k] = p.S ? ld_tag(src[j] + (size_t)(p.T * K + tt[j]) * p.H) : fresh;
+            else
+              v[j][k] = ld_tag(src[j] + (size_t)L.prow[tt[j] * K + k] * p.H);
+          }
+        }
       }
     }
 #pragma unroll
-    for (int i = 0; i < kCols; ++i)
-      o[kMaxTopK][i] = p.S ? ld_coh(p.o_scr + (size_t)(p.T * K + tt) * p.H + c0 + min(lane + kWave * i, nc - 1)) : 0.f;
+    for (int j = 0; j < kOut; ++j)
 #pragma unroll
-    for (int i = 0; i < kCols; ++i) {
-      float v = o[kMaxTopK][i];
-#pragma unroll
-      for (int k = 0; k < kMaxTopK; ++k)
-        if (k < K) v += wk[k] * o[k][i];
-      const int c = lane + kWave * i;
-      if (c < nc) st(p.y + (size_t)tt * p.H + c0 + c, f32_to_bf16(v));
-    }
-    if (lane == 0) store_agent(p.pair_done + tt * p.n_rg + rg, 0);
+      for (int k = 0; k < kIn; ++k)
+        if ((k < K || k == kMaxTopK) && live[j] && !tag_ok(v[j][k], p.epoch)) stale = true;
+    if (!block_any(stale, L.misc + 8)) break;
+    if (!poll_round(p, &t_end, L.misc + 1)) return false;
   }
+#pragma unroll
+  for (int j = 0; j < kOut; ++j) {
+    float acc = p.S ? __uint_as_float((uint32_t)v[j][kMaxTopK]) : 0.f;
+#pragma unroll
+    for (int k = 0; k < kMaxTopK; ++k)
+      if (k < K) acc += L.tkw[tt[j] * K + k] * __uint_as_float((uint32_t)v[j][k]);
+    const int o = threadIdx.x + kThreads * j;
+    if (live[j]) st(p.y + (size_t)tt[j] * p.H + c0 + o % kDownRows, f32_to_bf16(acc));
+  }
+  if (threadIdx.x == 0) *(SHARED long long*)(L.misc + 12) = (long long)wall_clock64();   // timeline
+  return true;
 }
 
 // ----------------------------------------------------------------------------
@@ -747,7 +931,8 @@ struct GuStage {
 
 template <int NMB, bool XL, int NMBMAX>
 __device__ __forceinline__ void gu_item(KParams& p, const Lds& L, int slot, int sbase, int r0, int nrows,
-                        int rb, bool shared, int parity) {
+                        int rb, bool shared, int parity, int& pend) {
+  flush_pending_now(p, pend);
   using Stage = GuStage<NMB, XL>;
   constexpr int D = Stage::D;
   const int w = wave_id(), lane = lane_id();
@@ -845,11 +1030,10 @@ __device__ __forceinline__ void gu_item(KParams& p, const Lds& L, int slot, int 
       const uint32_t hb_next = dpp<kDppRowShl1>(hb);          // column n + 1
       const int r = mb * kMBlock + 4 * kq + i;
       if (n < 8 && (n & 1) == 0 && r < nrows)
-        st_coh((uint32_t*)(p.h_scr + (size_t)(sbase + r0 + r) * p.I + 8 * rb + n), hb | (hb_next << 16));
+        st_tag(p.h_scr + (size_t)(sbase + r0 + r) * (p.I / 2) + (8 * rb + n) / 2, hb | (hb_next << 16), p.epoch);
     }
-    // each wave that stored h rows publishes them (one count per 16-row block)
-    wait_stores();
-    if (lane == 0) atomic_add_agent(p.ctr + kCtrHReady + slot, 1);
+    // each wave that stored h rows counts them in (one per 16-row block)
+    if (lane == 0) count_done(p.ctr + kCtrHReady + slot * kLine);
   }
 }
 
@@ -868,8 +1052,9 @@ struct DnStage {
 };
 
 template <int NMB, bool HL>
-__device__ __forceinline__ void down_item(KParams& p, const Lds& L, int slot, int sbase, int r0, int nrows,
-                          int rg, bool shared) {
+__device__ __forceinline__ bool down_item(KParams& p, const Lds& L, int slot, int sbase, int r0, int nrows,
+                          int rg, int h_target, int& pend) {
+  flush_pending_now(p, pend);
   using Stage = DnStage<NMB, HL>;
   constexpr int D = Stage::D;
   const int w = wave_id(), lane = lane_id();
@@ -880,7 +1065,7 @@ __device__ __forceinline__ void down_item(KParams& p, const Lds& L, int slot, in
 
   const int nrb_eff = max(nrb, 1);            // waves past the last block idle after staging
 
-  const uint16_t* arow[NMB];
+  const uint64_t* arow[NMB];                  // tagged h words: 2 bf16 each
   const SHARED uint16_t* arow_l[NMB];
   bool aval[NMB];
 #pragma unroll
@@ -888,7 +1073,7 @@ __device__ __forceinline__ void down_item(KParams& p, const Lds& L, int slot, in
     const int r = mb * kMBlock + n;
     aval[mb] = r < nrows;
     const int rr = aval[mb] ? r : 0;
-    arow[mb] = p.h_scr + (size_t)(sbase + r0 + rr) * p.I + 8 * kq;
+    arow[mb] = p.h_scr + (size_t)(sbase + r0 + rr) * (p.I / 2) + 4 * kq;
     arow_l[mb] = L.hs + (size_t)rr * p.hs_stride + 8 * kq;
   }
   // a wave with a single row block (last group of a ragged H) loads that
@@ -915,7 +1100,7 @@ __device__ __forceinline__ void down_item(KParams& p, const Lds& L, int slot, in
         for (int g = 0; g < 2; ++g)
 #pragma unroll
           for (int mb = 0; mb < NMB; ++mb)
-            S.a[HL ? 0 : u][g][mb] = ld_coh16(arow[mb] + kTileK * q + kGroup * g);
+            S.a[HL ? 0 : u][g][mb] = ld_h8(arow[mb] + (kTileK * q + kGroup * g) / 2);
       }
     }
   };
@@ -951,14 +1136,20 @@ __device__ __forceinline__ void down_item(KParams& p, const Lds& L, int slot, in
     }
   };
   Stage A, B;
+  if (!HL) {
+    // h is read in the pipeline below: it must be complete first
+    if (!wait_geq(p, p.ctr + kCtrHReady + slot * kLine, h_target, L.misc + 1)) return false;
+    if (!verify_h_rows(p, L, sbase + r0, nrows)) return false;
+  }
   load(A, 0);                                 // weights first: they need no input
   if (HL) {
-    // stage the h rows of this item: nrows x I bf16, 8 bytes per thread-step
-    __syncthreads();
-    stage_h_rows(p, L, sbase + r0, nrows);
+    // stage the item's h rows while the first weights are in flight (the
+    // barrier inside the wait keeps the previous item's readers safe)
+    if (!wait_geq(p, p.ctr + kCtrHReady + slot * kLine, h_target, L.misc + 1)) return false;
+    if (!stage_h_rows(p, L, sbase + r0, nrows)) return false;
     __syncthreads();
   }
-  if (nrb <= 0) return;
+  if (nrb <= 0) return true;
   for (int q0 = 0; q0 < nq; q0 += 2 * D) {
     if (q0 + D < nq) load(B, q0 + D);
     compute(A, q0);
@@ -974,11 +1165,13 @@ __device__ __forceinline__ void down_item(KParams& p, const Lds& L, int slot, in
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int r = mb * kMBlock + 4 * kq + i;
-          if (r < nrows) st_coh(p.o_scr + (size_t)(sbase + r0 + r) * p.H + rb * kTileRows + n, acc[j][mb][i]);
+          if (r < nrows)
+            st_tag(p.o_scr + (size_t)(sbase + r0 + r) * p.H + rb * kTileRows + n, __float_as_uint(acc[j][mb][i]), p.epoch);
         }
     }
   }
-  wave_arrive_combine(p, L, sbase, r0, nrows, rg, shared);
+  pend = rg;
+  return true;
 }
 
 // ----------------------------------------------------------------------------
@@ -989,7 +1182,7 @@ __device__ __forceinline__ void down_item(KParams& p, const Lds& L, int slot, in
 // ----------------------------------------------------------------------------
 template <int NJ>
 __device__ __forceinline__ void gu_item_full(KParams& p, const Lds& L, int slot, int sbase, int r0, int nrows,
-                             int rb, bool shared, int parity) {
+                             int rb, bool shared, int parity, int& pend) {
   const int w = wave_id(), lane = lane_id();
   const int n = lane & 15, kq = lane >> 4;
   const int nq = p.n_q13;                            // == 4 * NJ
@@ -1003,6 +1196,7 @@ __device__ __forceinline__ void gu_item_full(KParams& p, const Lds& L, int slot,
     wv[j] = ld_stream(wt + (size_t)j * kWaves * kWave);
     sv[j] = ld(sc + (size_t)j * kWaves * kTileRows);
   }
+  flush_pending<2 * NJ>(p, pend);
   const bool aval = n < nrows;
   const int tok = shared ? (r0 + (aval ? n : 0)) : (int)L.rows[sbase + r0 + (aval ? n : 0)];
   const SHARED uint16_t* arow = L.xs + (size_t)tok * p.xs_stride + 8 * kq + kTileK * w;
@@ -1033,20 +1227,32 @@ __device__ __forceinline__ void gu_item_full(KParams& p, const Lds& L, int slot,
       const uint32_t hb_next = dpp<kDppRowShl1>(hb);
       const int r = 4 * kq + i;
       if (n < 8 && (n & 1) == 0 && r < nrows)
-        st_coh((uint32_t*)(p.h_scr + (size_t)(sbase + r0 + r) * p.I + 8 * rb + n), hb | (hb_next << 16));
+        st_tag(p.h_scr + (size_t)(sbase + r0 + r) * (p.I / 2) + (8 * rb + n) / 2, hb | (hb_next << 16), p.epoch);
     }
-    wait_stores();
-    if (lane == 0) atomic_add_agent(p.ctr + kCtrHReady + slot, 1);
+    if (lane == 0) count_done(p.ctr + kCtrHReady + slot * kLine);
   }
 }
 
 template <int NQ>
-__device__ __forceinline__ void down_item_full(KParams& p, const Lds& L, int slot, int sbase, int r0, int nrows,
-                               int rg, bool shared) {
+__device__ __forceinline__ bool down_item_full(KParams& p, const Lds& L, int slot, int sbase, int r0, int nrows,
+                               int rg, int h_target, int& pend) {
   const int w = wave_id(), lane = lane_id();
   const int n = lane & 15, kq = lane >> 4;
   const int rb0 = rg * (kDownRows / kTileRows) + 2 * w;
   const int nrb = min(2, p.n_rb2 - rb0);
+  // The item's h rows (tagged words) are requested first, so they return
+  // before the weights; when every tag is current (h complete, the usual
+  // case) no counter needs to be polled at all.
+  constexpr int kHFast = 8;                   // h words per thread on the fast path
+  const int per_row = p.I / 2;
+  const int nh = nrows * per_row;
+  const bool fast = nh <= kHFast * kThreads;
+  const uint64_t* hsrc = p.h_scr + (size_t)(sbase + r0) * per_row;
+  uint64_t hv[kHFast];
+  if (fast) {
+#pragma unroll
+    for (int b = 0; b < kHFast; ++b) hv[b] = ld_tag(hsrc + min((int)threadIdx.x + b * kThreads, nh - 1));
+  }
   u32x4 wv[2][NQ];
   f32x2 sv[2][NQ];
 #pragma unroll
@@ -1060,12 +1266,32 @@ __device__ __forceinline__ void down_item_full(KParams& p, const Lds& L, int slo
       sv[j][q] = ld(sc + (size_t)q * kTileRows);
     }
   }
-  // stage the item's h rows (nrows x I bf16) while the weights are in flight;
-  // the first barrier keeps the previous item's readers of the area safe
+  if (fast) flush_pending<4 * NQ + kHFast>(p, pend);
+  else flush_pending<4 * NQ>(p, pend);
+  // the previous item's readers of the h area are done past this barrier
   __syncthreads();
-  stage_h_rows(p, L, sbase + r0, nrows);
+  bool stale = !fast;
+  if (fast) {
+#pragma unroll
+    for (int b = 0; b < kHFast; ++b) {
+      const int i = threadIdx.x + b * kThreads;
+      if (i < nh) {
+        if (tag_ok(hv[b], p.epoch))
+          *(SHARED uint32_t*)(L.hs + (size_t)(i / per_row) * p.hs_stride + 2 * (i % per_row)) = (uint32_t)hv[b];
+        else
+          stale = true;
+      }
+    }
+  }
+  if (block_any(stale, L.misc + 8)) {
+    // h not complete yet (or too many rows): wait for the count, then gather
+    if (!wait_geq(p, p.ctr + kCtrHReady + slot * kLine, h_target, L.misc + 1)) return false;
+    if (!stage_h_rows(p, L, sbase + r0, nrows)) return false;
+  } else if (threadIdx.x == 0) {
+    *(SHARED long long*)(L.misc + 12) = (long long)wall_clock64();   // inputs ready (timeline)
+  }
   __syncthreads();
-  if (nrb <= 0) return;
+  if (nrb <= 0) return true;
   const bool aval = n < nrows;
   const SHARED uint16_t* arow = L.hs + (size_t)(aval ? n : 0) * p.hs_stride + 8 * kq;
   const u32x4 zero4 = {0u, 0u, 0u, 0u};
@@ -1090,11 +1316,12 @@ __device__ __forceinline__ void down_item_full(KParams& p, const Lds& L, int slo
       for (int i = 0; i < 4; ++i) {
         const int r = 4 * kq + i;
         if (r < nrows)
-          st_coh(p.o_scr + (size_t)(sbase + r0 + r) * p.H + (rb0 + j) * kTileRows + n, acc[j][i]);
+          st_tag(p.o_scr + (size_t)(sbase + r0 + r) * p.H + (rb0 + j) * kTileRows + n, __float_as_uint(acc[j][i]), p.epoch);
       }
     }
   }
-  wave_arrive_combine(p, L, sbase, r0, nrows, rg, shared);
+  pend = rg;
+  return true;
 }
 
 // ----------------------------------------------------------------------------
@@ -1122,7 +1349,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
     x_staged = true;
   };
   bool routed = false;          // routing and placement are in LDS
-  int i_rgu_end = 0, i_sdn_end = 0, i_total = 0;
+  int i_rgu_end = 0, i_sdn_end = 0, i_rdn_end = 0, i_total = 0, n_mr = 0;
 
   // optional timeline of this workgroup (thread 0 writes it)
   long long* trace = (p.trace && (int)blockIdx.x < p.trace_blocks)
@@ -1149,11 +1376,11 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
     const long long r_start = wall_clock64();
     long long r_go = 0, r_lg = 0, r_row0 = 0, c_lg = 0;
     if (p.local_topk) {
-      if (!wait_geq(p, go_flag(p.ctr + kCtrRouterGo), 1, L.misc + 1)) return false;
+      // the wait's barrier also keeps earlier readers of the lg area safe
+      if (!wait_geq(p, go_flag(p.ctr + kCtrRouterGo), 1, L.misc + 1, 1 << 20)) return false;
       r_go = wall_clock64();
-      // all T x E logits into LDS with one round of coherent loads
-      batched_copy<float>(p.T * p.E, [&](int i) { return ld_coh(p.logits + i); },
-                          [&](int i, float v) { L.lg[i] = v; });
+      // all T x E logits into LDS (one round of loads unless some are late)
+      if (!gather_logits(p, L, 0, p.T)) return false;
       __syncthreads();
       r_lg = wall_clock64();
       c_lg = (long long)__builtin_amdgcn_s_memtime();
@@ -1175,7 +1402,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
         }
       }
     } else {
-      if (!wait_geq(p, go_flag(p.ctr + kCtrTopkGo), 1, L.misc + 1)) return false;
+      if (!wait_geq(p, go_flag(p.ctr + kCtrTopkGo), 1, L.misc + 1, 1 << 20)) return false;
       for (int i = tid; i < p.T * p.K; i += kThreads) {
         L.tki[i] = (int16_t)ld_coh(p.topk_idx + i);
         L.tkw[i] = ld_coh(p.topk_w + i);
@@ -1188,46 +1415,50 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
     build_placement(p, L);
     const long long r_place = wall_clock64();
     if (blockIdx.x == 0) write_routing_debug(p, L);
-    if (trace && tid == 0 && n_ev + 1 < p.trace_cap) {   // routing phases: kinds 7, 8
+    if (trace && tid == 0 && n_ev + 1 < p.trace_cap) {   // routing phases: kinds 8, 9
       long long* r = trace + (size_t)(1 + n_ev) * 4;
-      st(r + 0, (long long)7 << 32 | (long long)((r_place - r_topk) & 0xffffffff));
+      st(r + 0, (long long)8 << 32 | (long long)((r_place - r_topk) & 0xffffffff));
       st(r + 1, r_start);
       st(r + 2, r_go);
       st(r + 3, r_topk);
       r += 4;
-      st(r + 0, (long long)8 << 32 | (long long)((c_rows - c_lg) & 0xffffffff));
+      st(r + 0, (long long)9 << 32 | (long long)((c_rows - c_lg) & 0xffffffff));
       st(r + 1, r_lg);
       st(r + 2, r_row0);
       st(r + 3, r_rows);
       n_ev += 2;
     }
-    const int n_mr = L.misc[0];
+    n_mr = L.misc[0];
     i_rgu_end = p.i_topk_end + n_mr * p.n_rb13;
     i_sdn_end = i_rgu_end + p.n_sdn;
-    i_total = i_sdn_end + n_mr * p.n_rg;
+    i_rdn_end = i_sdn_end + n_mr * p.n_rg;
+    i_total = i_rdn_end + p.n_cmb;
     routed = true;
     return true;
   };
 
   int gu_count = 0;             // parity of the gate/up partial-sum area
+  int pend_rg = -1;             // this wave's deferred column-group count (-1: none)
   auto run_gu = [&](int slot, int sbase, int r0, int nrows, int rb, bool shared) __attribute__((always_inline)) {
     const int nmb = (nrows + kMBlock - 1) / kMBlock;
     const int par = gu_count++;
-    if (XL && p.n_q13 == 4 * kFullTiles) gu_item_full<kFullTiles>(p, L, slot, sbase, r0, nrows, rb, shared, par);
-    else if (NMBMAX == 1 || nmb <= 1) gu_item<1, XL, NMBMAX>(p, L, slot, sbase, r0, nrows, rb, shared, par);
-    else if (nmb == 2) gu_item<NMBMAX >= 2 ? 2 : 1, XL, NMBMAX>(p, L, slot, sbase, r0, nrows, rb, shared, par);
-    else if (nmb == 3) gu_item<NMBMAX >= 3 ? 3 : 1, XL, NMBMAX>(p, L, slot, sbase, r0, nrows, rb, shared, par);
-    else gu_item<NMBMAX >= 4 ? 4 : 1, XL, NMBMAX>(p, L, slot, sbase, r0, nrows, rb, shared, par);
+    if (XL && p.n_q13 == 4 * kFullTiles) gu_item_full<kFullTiles>(p, L, slot, sbase, r0, nrows, rb, shared, par, pend_rg);
+    else if (NMBMAX == 1 || nmb <= 1) gu_item<1, XL, NMBMAX>(p, L, slot, sbase, r0, nrows, rb, shared, par, pend_rg);
+    else if (nmb == 2) gu_item<NMBMAX >= 2 ? 2 : 1, XL, NMBMAX>(p, L, slot, sbase, r0, nrows, rb, shared, par, pend_rg);
+    else if (nmb == 3) gu_item<NMBMAX >= 3 ? 3 : 1, XL, NMBMAX>(p, L, slot, sbase, r0, nrows, rb, shared, par, pend_rg);
+    else gu_item<NMBMAX >= 4 ? 4 : 1, XL, NMBMAX>(p, L, slot, sbase, r0, nrows, rb, shared, par, pend_rg);
   };
-  auto run_down = [&](int slot, int sbase, int r0, int nrows, int rg, bool shared) __attribute__((always_inline)) {
+  // a down item waits (after issuing its first weight loads) until its
+  // expert's gate/up items have counted in ht publications
+  auto run_down = [&](int slot, int sbase, int r0, int nrows, int rg, int ht) __attribute__((always_inline)) -> bool {
     const int nmb = (nrows + kMBlock - 1) / kMBlock;
     if (XL && p.hs_stride > 0 && p.n_q2 == kFullTiles / 2)
-      down_item_full<kFullTiles / 2>(p, L, slot, sbase, r0, nrows, rg, shared);
-    else if (XL && p.hs_stride > 0) down_item<1, XL>(p, L, slot, sbase, r0, nrows, rg, shared);
-    else if (NMBMAX == 1 || nmb <= 1) down_item<1, false>(p, L, slot, sbase, r0, nrows, rg, shared);
-    else if (nmb == 2) down_item<NMBMAX >= 2 ? 2 : 1, false>(p, L, slot, sbase, r0, nrows, rg, shared);
-    else if (nmb == 3) down_item<NMBMAX >= 3 ? 3 : 1, false>(p, L, slot, sbase, r0, nrows, rg, shared);
-    else down_item<NMBMAX >= 4 ? 4 : 1, false>(p, L, slot, sbase, r0, nrows, rg, shared);
+      return down_item_full<kFullTiles / 2>(p, L, slot, sbase, r0, nrows, rg, ht, pend_rg);
+    else if (XL && p.hs_stride > 0) return down_item<1, XL>(p, L, slot, sbase, r0, nrows, rg, ht, pend_rg);
+    else if (NMBMAX == 1 || nmb <= 1) return down_item<1, false>(p, L, slot, sbase, r0, nrows, rg, ht, pend_rg);
+    else if (nmb == 2) return down_item<NMBMAX >= 2 ? 2 : 1, false>(p, L, slot, sbase, r0, nrows, rg, ht, pend_rg);
+    else if (nmb == 3) return down_item<NMBMAX >= 3 ? 3 : 1, false>(p, L, slot, sbase, r0, nrows, rg, ht, pend_rg);
+    else return down_item<NMBMAX >= 4 ? 4 : 1, false>(p, L, slot, sbase, r0, nrows, rg, ht, pend_rg);
   };
   // gate/up publications an expert's down items wait for: one per 16-row
   // MFMA block per gate/up row block
@@ -1235,14 +1466,38 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
     return p.n_rb13 * ((rows + kMBlock - 1) / kMBlock);
   };
 
-  bool router_seen = false;
-  for (it = blockIdx.x;; it += G) {
+  // Schedule.  Items [0, S) are static: workgroup g takes g, g + G, ... in
+  // order.  The last G items, [S, i_total), are claimed in list order from
+  // one counter, so the tail balances itself across workgroups; a claim is
+  // issued when an item starts and read when it ends, so its round trip hides
+  // behind the item (claims from one counter are costly, hence only the
+  // tail).  An item waits only on items earlier in the list, each workgroup's
+  // items increase, and a workgroup claims only after its static items: the
+  // earliest unfinished item is always being worked on, so every wait ends
+  // while all workgroups are resident.  S needs the routing (i_total).
+  bool dyn = false;
+  int i_dyn = INT_MAX;          // S, once routed
+  it = blockIdx.x;
+  for (;;) {
+    if (!dyn && it >= p.i_topk_end) {
+      ensure_x();
+      if (!ensure_routing()) break;
+      i_dyn = max(p.i_topk_end, i_total - G);
+      if (it >= i_dyn) {        // past the static part: claim (blocking, once)
+        dyn = true;
+        if (tid == 0) L.misc[2] = i_dyn + atomic_add_agent(p.ctr + kCtrTicket, 1);
+        __syncthreads();
+        it = __builtin_amdgcn_readfirstlane(L.misc[2]);
+        __syncthreads();
+      }
+    }
+    const bool claim = routed && (dyn || it + G >= i_dyn);
+    int next = 0;
+    if (tid == 0 && claim) next = i_dyn + atomic_add_agent(p.ctr + kCtrTicket, 1);
     t_got = t_ready = wall_clock64();
     if (it < p.i_router_end) {
       kind = 0;
       router_item(p, L, it);
-      t_ready = wall_clock64();
-      publish_done(p.ctr + kCtrRouterDone, p.n_router, p.ctr + kCtrRouterGo);
     } else if (it < p.i_sgu_end) {
       kind = 1;
       ensure_x();
@@ -1252,12 +1507,9 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
       run_gu(p.E, p.T * p.K, r0, min(kMRange, p.T - r0), rb, true);
     } else if (it < p.i_topk_end) {
       kind = 2;
-      if (!router_seen) {
-        if (!wait_geq(p, go_flag(p.ctr + kCtrRouterGo), 1, L.misc + 1)) break;
-        router_seen = true;
-      }
+      if (!wait_geq(p, go_flag(p.ctr + kCtrRouterGo), 1, L.misc + 1, 1 << 20)) break;
       t_ready = wall_clock64();
-      topk_item(p, L, it - p.i_sgu_end);
+      if (!topk_item(p, L, it - p.i_sgu_end)) break;
       publish_done(p.ctr + kCtrTopkDone, p.n_topk, p.ctr + kCtrTopkGo);
     } else {
       kind = 6;
@@ -1277,23 +1529,34 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
         const int i = it - i_rgu_end;
         const int mr = i / p.n_rg, rg = i % p.n_rg;
         const int r0 = mr * kMRange;
-        const int nrows = min(kMRange, p.T - r0);
-        if (!wait_geq(p, p.ctr + kCtrHReady + p.E, h_target(p.T), L.misc + 1)) break;
-        t_ready = wall_clock64();
-        run_down(p.E, p.T * p.K, r0, nrows, rg, true);
-      } else {
+        if (!run_down(p.E, p.T * p.K, r0, min(kMRange, p.T - r0), rg, h_target(p.T))) break;
+        t_ready = *(SHARED long long*)(L.misc + 12);
+      } else if (it < i_rdn_end) {
         kind = 5;
         const int i = it - i_sdn_end;
         const int m = i / p.n_rg, rg = i % p.n_rg;
         const int e = L.mrlist[m];
         const int r0 = (m - L.nmrb[e]) * kMRange;
-        const int nrows = min(kMRange, L.cnt[e] - r0);
-        if (!wait_geq(p, p.ctr + kCtrHReady + e, h_target(L.cnt[e]), L.misc + 1)) break;
-        t_ready = wall_clock64();
-        run_down(e, L.base[e], r0, nrows, rg, false);
+        if (!run_down(e, L.base[e], r0, min(kMRange, L.cnt[e] - r0), rg, h_target(L.cnt[e]))) break;
+        t_ready = *(SHARED long long*)(L.misc + 12);
+      } else {
+        kind = 7;
+        flush_pending_now(p, pend_rg);
+        const int c = it - i_rdn_end;
+        if (!combine_item(p, L, c / p.n_rg, c % p.n_rg, n_mr)) break;
+        t_ready = *(SHARED long long*)(L.misc + 12);
       }
     }
     record();
+    if (claim) {
+      // every item has a barrier after its last read of misc[2]
+      if (tid == 0) L.misc[2] = next;
+      __syncthreads();
+      it = __builtin_amdgcn_readfirstlane(L.misc[2]);
+      dyn = true;
+    } else {
+      it += G;
+    }
   }
   if (trace && tid == 0) {
     st(trace + 0, t_entry);
@@ -1303,21 +1566,21 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
   }
 
   // The last workgroup out resets the counters for the next run.
+  flush_pending_now(p, pend_rg);
   wait_stores();
   __syncthreads();
   if (tid == 0) {
     const int old = atomic_add_agent(p.ctr + kCtrExit, 1);
     if (old == G - 1) {
-      const bool failed = load_agent(p.ctr + kCtrStatus) != 0;
       store_agent(p.ctr + kCtrRouterDone, 0);
       store_agent(p.ctr + kCtrTopkDone, 0);
+      store_agent(p.ctr + kCtrTicket, 0);
       for (int i = 0; i < kGoLines; ++i) {
         store_agent(p.ctr + kCtrRouterGo + i * kGoStride, 0);
         store_agent(p.ctr + kCtrTopkGo + i * kGoStride, 0);
       }
-      for (int e = 0; e < p.E + p.S; ++e) store_agent(p.ctr + kCtrHReady + e, 0);
-      if (failed)
-        for (int i = 0; i < p.T * p.n_rg; ++i) store_agent(p.pair_done + i, 0);
+      for (int e = 0; e < p.E + p.S; ++e) store_agent(p.ctr + kCtrHReady + e * kLine, 0);
+      for (int rg = 0; rg < p.n_rg; ++rg) store_agent(p.ctr + kCtrRgDone + rg * kLine, 0);
       store_agent(p.ctr + kCtrExit, 0);
     }
   }
@@ -1379,13 +1642,13 @@ struct moe_decode_handle {
   float* s13p = nullptr;
   u32x4* w2p = nullptr;
   float* s2p = nullptr;
-  float* logits = nullptr;
+  uint64_t* lgt = nullptr;
   int* topk_idx = nullptr;
   float* topk_w = nullptr;
-  uint16_t* h_scr = nullptr;
-  float* o_scr = nullptr;
+  uint64_t* h_scr = nullptr;
+  uint64_t* o_scr = nullptr;
   int* ctr = nullptr;
-  int* pair_done = nullptr;
+  uint32_t epoch = 0;            // tag of the last run (0: none yet)
   hipStream_t last_stream = nullptr;
   std::mutex mu;
   // occupancy cache, by (kernel variant, LDS bytes)
@@ -1410,8 +1673,6 @@ moe_status check_config(const moe_decode_config* c) {
   return MOE_OK;
 }
 
-constexpr size_t ctr_head_words(size_t) { return kCtrHead; }
-
 Params make_params(const moe_decode_handle* h, int T) {
   const moe_decode_config& c = h->cfg;
   Params p;
@@ -1428,13 +1689,12 @@ Params make_params(const moe_decode_handle* h, int T) {
   p.s13p = h->s13p;
   p.w2p = h->w2p;
   p.s2p = h->s2p;
-  p.logits = h->logits;
+  p.lgt = h->lgt;
   p.topk_idx = h->topk_idx;
   p.topk_w = h->topk_w;
   p.h_scr = h->h_scr;
   p.o_scr = h->o_scr;
   p.ctr = h->ctr;
-  p.pair_done = h->pair_done;
   const long long dl = c.deadline_us > 0 ? c.deadline_us : 1000000;
   p.deadline_ticks = dl * 100;   // wall clock runs at 100 MHz
   p.local_topk = T <= kLocalTopkRows ? 1 : 0;
@@ -1451,6 +1711,7 @@ Params make_params(const moe_decode_handle* h, int T) {
   p.i_sgu_end = p.i_router_end + p.n_mr_sh * p.n_rb13;
   p.i_topk_end = p.i_sgu_end + p.n_topk;
   p.n_sdn = p.n_mr_sh * p.n_rg;
+  p.n_cmb = (T + kCombineRows - 1) / kCombineRows * p.n_rg;
   // LDS layout
   const int E = p.E, K = p.K;
   const int max_mr = E + (T * K + kMRange - 1) / kMRange;
@@ -1465,6 +1726,7 @@ Params make_params(const moe_decode_handle* h, int T) {
   p.lds_mrlist = take((size_t)max_mr * 4);
   p.lds_rows = take((size_t)T * K * 2);
   p.lds_tki = take((size_t)T * K * 2);
+  p.lds_prow = take((size_t)T * K * 4);
   p.lds_tkw = take((size_t)T * K * 4);
   p.lds_misc = take(16 * 4);
   p.lds_tks = take((size_t)kWaves * kWave * 4);
@@ -1481,7 +1743,7 @@ Params make_params(const moe_decode_handle* h, int T) {
   p.lds_red = take((size_t)2 * kWaves * nmb * kWave * 16);
   // one region used in turn by the routing logits and a down item's h rows
   const size_t hs_bytes = p.hs_stride ? (size_t)std::min(T, kMBlock) * p.hs_stride * 2 : 0;
-  const size_t lg_bytes = p.local_topk ? (size_t)T * E * 4 : 0;
+  const size_t lg_bytes = (size_t)(p.local_topk ? T : kWaves) * E * 4;
   p.lds_hs = p.lds_lg = take(std::max(hs_bytes, lg_bytes));
   p.lds_bytes = (int)off;
   return p;
@@ -1524,7 +1786,7 @@ void moe_decode_destroy(moe_decode_handle* h) {
   (void)hipGetDevice(&prev);
   (void)hipSetDevice(h->device);
   (void)hipDeviceSynchronize();
-  void* ptrs[] = {h->router_w, h->router_b, h->w13p, h->s13p, h->w2p, h->s2p, h->logits,
+  void* ptrs[] = {h->router_w, h->router_b, h->w13p, h->s13p, h->w2p, h->s2p, h->lgt,
                   h->topk_idx, h->topk_w, h->h_scr, h->o_scr, h->ctr};
   for (void* q : ptrs)
     if (q) (void)hipFree(q);
@@ -1559,9 +1821,8 @@ moe_status moe_decode_create(const moe_decode_config* cfg, const moe_decode_weig
     const size_t E = cfg->num_experts, S = cfg->num_shared, H = cfg->hidden,
                  I = cfg->intermediate, K = cfg->top_k, Tm = cfg->max_tokens;
     const size_t slots = E + S;
-    const size_t n_rg = (H + kDownRows - 1) / kDownRows;
     const size_t scr_rows = Tm * K + Tm * S;
-    const size_t ctr_words = ctr_head_words(slots) + Tm * n_rg;
+    const size_t ctr_words = kCtrHead;
     struct A { void** p; size_t bytes; } allocs[] = {
         {(void**)&h->router_w, E * H * 4},
         {(void**)&h->router_b, w->router_bias ? E * 4 : 0},
@@ -1569,11 +1830,11 @@ moe_status moe_decode_create(const moe_decode_config* cfg, const moe_decode_weig
         {(void**)&h->s13p, slots * 2 * I * (H / 32) * 4},
         {(void**)&h->w2p, slots * H * I},
         {(void**)&h->s2p, slots * H * (I / 32) * 4},
-        {(void**)&h->logits, Tm * E * 4},
+        {(void**)&h->lgt, Tm * E * 8},
         {(void**)&h->topk_idx, Tm * K * 4},
         {(void**)&h->topk_w, Tm * K * 4},
-        {(void**)&h->h_scr, scr_rows * I * 2},
-        {(void**)&h->o_scr, scr_rows * H * 4},
+        {(void**)&h->h_scr, scr_rows * (I / 2) * 8},
+        {(void**)&h->o_scr, scr_rows * H * 8},
         {(void**)&h->ctr, ctr_words * 4},
     };
     for (auto& a : allocs) {
@@ -1581,8 +1842,11 @@ moe_status moe_decode_create(const moe_decode_config* cfg, const moe_decode_weig
       if (hipMalloc(a.p, a.bytes) != hipSuccess) { rc = MOE_ERR_OUT_OF_MEMORY; break; }
     }
     if (rc != MOE_OK) break;
-    h->pair_done = h->ctr + ctr_head_words(slots);
-    if (hipMemset(h->ctr, 0, ctr_words * 4) != hipSuccess) { rc = MOE_ERR_HIP; break; }
+    // counters and every tagged word start at zero (no run has epoch 0)
+    if (hipMemset(h->ctr, 0, ctr_words * 4) != hipSuccess ||
+        hipMemset(h->lgt, 0, Tm * E * 8) != hipSuccess ||
+        hipMemset(h->h_scr, 0, scr_rows * (I / 2) * 8) != hipSuccess ||
+        hipMemset(h->o_scr, 0, scr_rows * H * 8) != hipSuccess) { rc = MOE_ERR_HIP; break; }
     if (hipMemcpy(h->router_w, w->router_w, E * H * 4, hipMemcpyDeviceToDevice) != hipSuccess) { rc = MOE_ERR_HIP; break; }
     if (w->router_bias &&
         hipMemcpy(h->router_b, w->router_bias, E * 4, hipMemcpyDeviceToDevice) != hipSuccess) { rc = MOE_ERR_HIP; break; }
@@ -1631,6 +1895,9 @@ moe_status moe_decode_run(moe_decode_handle* h, const void* x, int32_t T, void* 
   }
   hipStream_t stream = (hipStream_t)hip_stream;
   std::lock_guard<std::mutex> lock(h->mu);
+  // a new tag for this run (0 is skipped: the workspace starts zeroed)
+  h->epoch = h->epoch + 1 == 0 ? 1 : h->epoch + 1;
+  p.epoch = h->epoch;
   int prev = 0;
   HIP_TRY(hipGetDevice(&prev));
   if (prev != h->device) HIP_TRY(hipSetDevice(h->device));
