@@ -64,7 +64,9 @@ constexpr int kWaves = 4;                   // waves per workgroup
 constexpr int kThreads = kWave * kWaves;
 constexpr int kMBlock = 16;                 // rows per MFMA block
 constexpr int kMRange = 64;                 // rows per expert item (<= 4 MFMA blocks)
-constexpr int kRouterRows = 8;              // rows per router item
+constexpr int kRouterRows = 8;              // rows per router item (small batches)
+constexpr int kRouterTile = 16;             // rows and experts per router tile (larger batches)
+constexpr int kRouterKsMax = 8;             // a router tile's H may be split over up to 8 items
 constexpr int kDownRows = 128;              // output rows per down item (8 row blocks)
 constexpr int kTileRows = 16;               // weight rows per tile
 constexpr int kTileK = 64;                  // K elements per tile (two scale groups)
@@ -72,7 +74,6 @@ constexpr int kGroup = 32;
 constexpr int kMaxTokens = 512;
 constexpr int kMaxExperts = 256;
 constexpr int kMaxTopK = 16;
-constexpr int kLocalTopkRows = 32;          // at most this many rows: top-k in every workgroup
 constexpr size_t kXsMaxBytes = 64 * 1024;   // x kept in LDS up to this size
 constexpr int kHsMaxI = 1024;               // h staged in LDS up to this intermediate width
 constexpr int kFullTiles = 16;              // tiles per wave of the fully unrolled items (H 4096, I 512)
@@ -86,8 +87,9 @@ constexpr int kCtrRouterDone = 0 * kLine;   // router items done
 constexpr int kCtrTopkDone = 1 * kLine;     // distributed top-k items done
 constexpr int kCtrExit = 2 * kLine;
 constexpr int kCtrStatus = 3 * kLine;
-constexpr int kCtrTicket = 4 * kLine;       // next unclaimed item of the list
-constexpr int kCtrHReady = 5 * kLine;       // [E+S] gate/up publications per expert (E+S <= 257)
+constexpr int kClaimGroups = 8;             // claim counters (workgroup index mod 8)
+constexpr int kCtrTicket = 4 * kLine;       // [kClaimGroups] next unclaimed dynamic item of each group
+constexpr int kCtrHReady = (4 + kClaimGroups) * kLine;   // [E+S] gate/up publications per expert (E+S <= 257)
 constexpr int kCtrRgDone = kCtrHReady + 257 * kLine;   // [H/128] down-wave publications (<= 128)
 // "go" flags raised once by the last router item and by the last
 // distributed top-k item, polled by every workgroup: kGoLines copies, 1 KiB
@@ -122,7 +124,7 @@ struct Params {
   const float* s2p;    // [E+S][H/16][I/64][16][2]
   // workspace.  Words handed between workgroups carry the run's epoch in
   // their high half (see "Tagged hand-offs" below).
-  uint64_t* lgt;       // [T][E] router logits (fp32 bits | epoch)
+  uint64_t* lgt;       // [T][E] router logits (fp32 bits | epoch); tiles: [router_ks][T][E] partials
   int* topk_idx;       // [T][K]  (distributed top-k only)
   float* topk_w;       // [T][K]
   uint64_t* h_scr;     // [T*K + T*S][I/2] two bf16 of h | epoch, rows grouped by expert
@@ -149,6 +151,8 @@ struct Params {
   int nch;             // 64-row chunks: ceil(T/64)
   // item list boundaries
   int n_router, n_topk;
+  int router_tiles;    // 1: router items are 16 x 16 MFMA tiles (batches above 16 rows)
+  int router_ks;       // H split of a tile: item (tile, ks) writes partial logits ks
   int i_router_end, i_sgu_end, i_topk_end;
   int n_sdn;           // shared down items
   int n_cmb;           // combine items: ceil(T / kCombineRows) * n_rg
@@ -610,6 +614,88 @@ __device__ __forceinline__ void write_routing_debug(KParams& p, const Lds& L) {
 // Router: logits of expert e for up to 8 rows; the 4 waves split H.  x comes
 // from LDS when the batch is small enough to keep it there.
 // ----------------------------------------------------------------------------
+// The last router item raises the go flags (no store needs to be waited for
+// first: the readers check the tags).
+__device__ __forceinline__ void router_done(KParams& p) {
+  if (threadIdx.x == 0 && atomic_add_agent(p.ctr + kCtrRouterDone, 1) == p.n_router - 1)
+    for (int i = 0; i < kGoLines; ++i) store_agent(p.ctr + kCtrRouterGo + i * kGoStride, 1);
+}
+
+// Router tile (batches above 16 rows): logits of rows [16 rt, +16) x experts
+// [16 et, +16) with v_mfma_f32_16x16x4_f32; the 4 waves split H.  Lane l =
+// (n, kq), n = l % 16, kq = l / 16, loads 4 consecutive K of row n of x and
+// of expert n's router row; its i-th value feeds the i-th of 4 MFMAs, so the
+// 4 instructions together cover 16 consecutive K (any split of a sum's terms
+// over the instructions gives the same sum up to rounding order).  The fp32
+// partial tiles of the waves are added in LDS in wave order.
+__device__ __forceinline__ void router_tile_item(KParams& p, const Lds& L, int item) {
+  const int w = wave_id(), lane = lane_id();
+  const int n = lane & 15, kq = lane >> 4;
+  const int n_et = (p.E + kRouterTile - 1) / kRouterTile;
+  const int tile = item / p.router_ks, ks = item % p.router_ks;
+  const int t0 = (tile / n_et) * kRouterTile, e0 = (tile % n_et) * kRouterTile;
+  const int nt = min(kRouterTile, p.T - t0), ne = min(kRouterTile, p.E - e0);
+  const int kw = p.H / p.router_ks / kWaves;   // K per wave (a multiple of 16)
+  const int kbase = ks * (p.H / p.router_ks) + w * kw;
+  const uint16_t* xr = p.x + (size_t)(t0 + min(n, nt - 1)) * p.H + kbase + 4 * kq;
+  const float* wr = p.router_w + (size_t)(e0 + min(n, ne - 1)) * p.H + kbase + 4 * kq;
+  // one accumulator per MFMA slot i, so consecutive MFMAs do not depend on
+  // each other; the four are added in a fixed order at the end
+  f32x4 acc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) acc[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  // two register stages of kU 16-K steps each, loaded a stage ahead
+  constexpr int kU = 8;
+  struct Stage { u32x2 xa[kU]; f32x4 wb[kU]; };
+  auto load = [&](Stage& S, int k0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int k = min(k0 + 16 * u, kw - 16);  // past the end: reread the last step (unused)
+      S.xa[u] = ld((const u32x2*)(xr + k));
+      S.wb[u] = ld((const f32x4*)(wr + k));
+    }
+  };
+  auto compute = [&](const Stage& S, int k0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      if (k0 + 16 * u < kw) {
+        acc[0] = __builtin_amdgcn_mfma_f32_16x16x4f32(bf16_to_f32(S.xa[u].x & 0xffffu), S.wb[u].x, acc[0], 0, 0, 0);
+        acc[1] = __builtin_amdgcn_mfma_f32_16x16x4f32(bf16_to_f32(S.xa[u].x >> 16), S.wb[u].y, acc[1], 0, 0, 0);
+        acc[2] = __builtin_amdgcn_mfma_f32_16x16x4f32(bf16_to_f32(S.xa[u].y & 0xffffu), S.wb[u].z, acc[2], 0, 0, 0);
+        acc[3] = __builtin_amdgcn_mfma_f32_16x16x4f32(bf16_to_f32(S.xa[u].y >> 16), S.wb[u].w, acc[3], 0, 0, 0);
+      }
+    }
+  };
+  constexpr int kStep = 16 * kU;
+  Stage A, B;
+  load(A, 0);
+  for (int k0 = 0; k0 < kw; k0 += 2 * kStep) {
+    if (k0 + kStep < kw) load(B, k0 + kStep);
+    compute(A, k0);
+    if (k0 + 2 * kStep < kw) load(A, k0 + 2 * kStep);
+    if (k0 + kStep < kw) compute(B, k0 + kStep);
+  }
+  // D layout: lane l holds rows 4 kq + i (x rows) of column n (expert)
+  SHARED f32x4* part = (SHARED f32x4*)L.red;   // [kWaves][64]
+  part[w * kWave + lane] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+  __syncthreads();
+  if (w == 0) {
+    f32x4 s = part[lane];
+#pragma unroll
+    for (int ww = 1; ww < kWaves; ++ww) s += part[ww * kWave + lane];
+    // the bias goes with part 0; the top-k items add the parts in order
+    const float b = (ks == 0 && p.router_b && n < ne) ? ld(p.router_b + e0 + n) : 0.f;
+    uint64_t* out = p.lgt + (size_t)ks * p.T * p.E;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 4 * kq + i;
+      if (r < nt && n < ne) st_tag(out + (size_t)(t0 + r) * p.E + e0 + n, __float_as_uint(s[i] + b), p.epoch);
+    }
+  }
+  __syncthreads();                             // the partials area is free again
+  router_done(p);
+}
+
 __device__ __forceinline__ void router_item(KParams& p, const Lds& L, int item) {
   const int w = wave_id(), lane = lane_id();
   const int e = item % p.E;
@@ -678,10 +764,7 @@ __device__ __forceinline__ void router_item(KParams& p, const Lds& L, int item) 
     st_tag(p.lgt + (size_t)(t0 + j) * p.E + e, __float_as_uint(s), p.epoch);
     if (p.dbg_logits) st(p.dbg_logits + (size_t)(t0 + j) * p.E + e, s);
   }
-  // the last router item raises the go flags (no store needs to be waited
-  // for first: the readers check the tags)
-  if (threadIdx.x == 0 && atomic_add_agent(p.ctr + kCtrRouterDone, 1) == p.n_router - 1)
-    for (int i = 0; i < kGoLines; ++i) store_agent(p.ctr + kCtrRouterGo + i * kGoStride, 1);
+  router_done(p);
 }
 
 // ----------------------------------------------------------------------------
@@ -784,12 +867,27 @@ __device__ __forceinline__ bool gather_logits(KParams& p, const Lds& L, int t0, 
 }
 
 // Distributed top-k item (large batches): rows 4 item .. 4 item + 3, one per
-// wave, to global memory.
+// wave, to global memory.  The logits arrive as router_ks partial sums
+// (gathered as [ks][row][E]) and are added in ks order.
 __device__ __forceinline__ bool topk_item(KParams& p, const Lds& L, int item) {
   const int t0 = item * kWaves;
   const int nt = min(kWaves, p.T - t0);
+  const int KS = p.router_ks;
+  const int per_part = nt * p.E;
   __syncthreads();                             // earlier readers of the lg area are done
-  if (!gather_logits(p, L, t0, nt)) return false;
+  if (!gather_tagged(p, L, KS * per_part,
+                     [&](int i) {
+                       return ld_tag(p.lgt + (size_t)(i / per_part) * p.T * p.E + (size_t)t0 * p.E + i % per_part);
+                     },
+                     [&](int i, uint32_t v) { L.lg[i] = __uint_as_float(v); }))
+    return false;
+  __syncthreads();
+  for (int i = threadIdx.x; i < per_part; i += kThreads) {
+    float v = L.lg[i];
+    for (int k = 1; k < KS; ++k) v += L.lg[k * per_part + i];
+    L.lg[i] = v;
+    if (p.dbg_logits) st(p.dbg_logits + (size_t)t0 * p.E + i, v);
+  }
   __syncthreads();
   const int w = wave_id();
   if (w < nt) {
@@ -1467,16 +1565,20 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
   };
 
   // Schedule.  Items [0, S) are static: workgroup g takes g, g + G, ... in
-  // order.  The last G items, [S, i_total), are claimed in list order from
-  // one counter, so the tail balances itself across workgroups; a claim is
-  // issued when an item starts and read when it ends, so its round trip hides
-  // behind the item (claims from one counter are costly, hence only the
-  // tail).  An item waits only on items earlier in the list, each workgroup's
-  // items increase, and a workgroup claims only after its static items: the
-  // earliest unfinished item is always being worked on, so every wait ends
-  // while all workgroups are resident.  S needs the routing (i_total).
+  // order.  The last G items, [S, i_total), are claimed, so the tail
+  // balances itself: claim group c = g mod 8 owns items S + c, S + c + 8, ...
+  // and hands them out in order from its own counter (eight counters on
+  // separate lines, so simultaneous claims do not queue on one address).  A
+  // claim is issued when an item starts and read when it ends, so its round
+  // trip hides behind the item.  An item waits only on items earlier in the
+  // list, each workgroup's items increase, a group's claims come in order
+  // and a workgroup claims only after its static items: the earliest
+  // unfinished item is always being worked on, so every wait ends while all
+  // workgroups are resident.  S needs the routing (i_total).
   bool dyn = false;
   int i_dyn = INT_MAX;          // S, once routed
+  const int cgroup = blockIdx.x % kClaimGroups;
+  int* const claim_ctr = p.ctr + kCtrTicket + cgroup * kLine;
   it = blockIdx.x;
   for (;;) {
     if (!dyn && it >= p.i_topk_end) {
@@ -1485,19 +1587,20 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
       i_dyn = max(p.i_topk_end, i_total - G);
       if (it >= i_dyn) {        // past the static part: claim (blocking, once)
         dyn = true;
-        if (tid == 0) L.misc[2] = i_dyn + atomic_add_agent(p.ctr + kCtrTicket, 1);
+        if (tid == 0) L.misc[2] = i_dyn + cgroup + kClaimGroups * atomic_add_agent(claim_ctr, 1);
         __syncthreads();
         it = __builtin_amdgcn_readfirstlane(L.misc[2]);
         __syncthreads();
       }
     }
     const bool claim = routed && (dyn || it + G >= i_dyn);
-    int next = 0;
-    if (tid == 0 && claim) next = i_dyn + atomic_add_agent(p.ctr + kCtrTicket, 1);
+    int claimed = 0;              // raw counter value; read only after the item
+    if (tid == 0 && claim) claimed = atomic_add_agent(claim_ctr, 1);
     t_got = t_ready = wall_clock64();
     if (it < p.i_router_end) {
       kind = 0;
-      router_item(p, L, it);
+      if (p.router_tiles) router_tile_item(p, L, it);
+      else router_item(p, L, it);
     } else if (it < p.i_sgu_end) {
       kind = 1;
       ensure_x();
@@ -1549,8 +1652,12 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
     }
     record();
     if (claim) {
-      // every item has a barrier after its last read of misc[2]
-      if (tid == 0) L.misc[2] = next;
+      // the claim's result is first read here, so the wait for its round
+      // trip lands after the item (the empty asm keeps the compiler from
+      // using it earlier); every item has a barrier after its last read of
+      // misc[2]
+      asm volatile("" : "+v"(claimed));
+      if (tid == 0) L.misc[2] = i_dyn + cgroup + kClaimGroups * claimed;
       __syncthreads();
       it = __builtin_amdgcn_readfirstlane(L.misc[2]);
       dyn = true;
@@ -1574,7 +1681,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
     if (old == G - 1) {
       store_agent(p.ctr + kCtrRouterDone, 0);
       store_agent(p.ctr + kCtrTopkDone, 0);
-      store_agent(p.ctr + kCtrTicket, 0);
+      for (int c = 0; c < kClaimGroups; ++c) store_agent(p.ctr + kCtrTicket + c * kLine, 0);
       for (int i = 0; i < kGoLines; ++i) {
         store_agent(p.ctr + kCtrRouterGo + i * kGoStride, 0);
         store_agent(p.ctr + kCtrTopkGo + i * kGoStride, 0);
@@ -1697,7 +1804,8 @@ Params make_params(const moe_decode_handle* h, int T) {
   p.ctr = h->ctr;
   const long long dl = c.deadline_us > 0 ? c.deadline_us : 1000000;
   p.deadline_ticks = dl * 100;   // wall clock runs at 100 MHz
-  p.local_topk = T <= kLocalTopkRows ? 1 : 0;
+  p.router_tiles = T > kMBlock ? 1 : 0;
+  p.local_topk = p.router_tiles ? 0 : 1;
   p.n_rb13 = p.I / 8;
   p.n_q13 = p.H / kTileK;
   p.n_rb2 = p.H / kTileRows;
@@ -1705,7 +1813,15 @@ Params make_params(const moe_decode_handle* h, int T) {
   p.n_rg = (p.H + kDownRows - 1) / kDownRows;
   p.nch = (T + 63) / 64;
   p.n_mr_sh = p.S ? (T + kMRange - 1) / kMRange : 0;
-  p.n_router = p.E * ((T + kRouterRows - 1) / kRouterRows);
+  {
+    const int n_tiles = ((T + kRouterTile - 1) / kRouterTile) * ((p.E + kRouterTile - 1) / kRouterTile);
+    // split H so that the tiles fill about one item per CU; each wave's share
+    // of H must stay a multiple of 16
+    int ks = 1;
+    while (2 * ks <= kRouterKsMax && n_tiles * 2 * ks <= 256 && (p.H / kTileK) % (2 * ks) == 0) ks *= 2;
+    p.router_ks = p.router_tiles ? ks : 1;
+    p.n_router = p.router_tiles ? n_tiles * p.router_ks : p.E * ((T + kRouterRows - 1) / kRouterRows);
+  }
   p.n_topk = p.local_topk ? 0 : (T + kWaves - 1) / kWaves;
   p.i_router_end = p.n_router;
   p.i_sgu_end = p.i_router_end + p.n_mr_sh * p.n_rb13;
@@ -1743,7 +1859,7 @@ Params make_params(const moe_decode_handle* h, int T) {
   p.lds_red = take((size_t)2 * kWaves * nmb * kWave * 16);
   // one region used in turn by the routing logits and a down item's h rows
   const size_t hs_bytes = p.hs_stride ? (size_t)std::min(T, kMBlock) * p.hs_stride * 2 : 0;
-  const size_t lg_bytes = (size_t)(p.local_topk ? T : kWaves) * E * 4;
+  const size_t lg_bytes = (size_t)(p.local_topk ? T : kWaves * p.router_ks) * E * 4;
   p.lds_hs = p.lds_lg = take(std::max(hs_bytes, lg_bytes));
   p.lds_bytes = (int)off;
   return p;
@@ -1830,7 +1946,7 @@ moe_status moe_decode_create(const moe_decode_config* cfg, const moe_decode_weig
         {(void**)&h->s13p, slots * 2 * I * (H / 32) * 4},
         {(void**)&h->w2p, slots * H * I},
         {(void**)&h->s2p, slots * H * (I / 32) * 4},
-        {(void**)&h->lgt, Tm * E * 8},
+        {(void**)&h->lgt, Tm * E * 8 * kRouterKsMax},
         {(void**)&h->topk_idx, Tm * K * 4},
         {(void**)&h->topk_w, Tm * K * 4},
         {(void**)&h->h_scr, scr_rows * (I / 2) * 8},
@@ -1844,7 +1960,7 @@ moe_status moe_decode_create(const moe_decode_config* cfg, const moe_decode_weig
     if (rc != MOE_OK) break;
     // counters and every tagged word start at zero (no run has epoch 0)
     if (hipMemset(h->ctr, 0, ctr_words * 4) != hipSuccess ||
-        hipMemset(h->lgt, 0, Tm * E * 8) != hipSuccess ||
+        hipMemset(h->lgt, 0, Tm * E * 8 * kRouterKsMax) != hipSuccess ||
         hipMemset(h->h_scr, 0, scr_rows * (I / 2) * 8) != hipSuccess ||
         hipMemset(h->o_scr, 0, scr_rows * H * 8) != hipSuccess) { rc = MOE_ERR_HIP; break; }
     if (hipMemcpy(h->router_w, w->router_w, E * H * 4, hipMemcpyDeviceToDevice) != hipSuccess) { rc = MOE_ERR_HIP; break; }
