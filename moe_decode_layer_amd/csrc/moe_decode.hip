@@ -16,10 +16,12 @@
 // each workgroup takes its items in list order and all workgroups are
 // resident together, so every wait is eventually satisfied -- and if they
 // were not all resident, the deadline turns the stall into an error):
-//   router          : logits of one expert for up to 8 rows
+//   router          : logits of one expert for up to 8 rows (batches above
+//                     16 rows: a 16-row x 16-expert MFMA tile, or part of
+//                     its H)
+//   top-k           : 4 rows, one per wave (only for batches above 16 rows;
+//                     smaller batches select top-k in every workgroup)
 //   shared gate/up  : 16 weight rows (8 gate + 8 up) of the shared expert
-//   top-k           : 4 rows, one per wave (only for batches of more than 32
-//                     rows; smaller batches select top-k in every workgroup)
 //   routed gate/up  : 16 weight rows of one routed expert      -- waits: routing
 //   shared down     : 128 output rows of the shared expert     -- waits: its gate/up
 //   routed down     : 128 output rows of one routed expert     -- waits: its gate/up
@@ -153,7 +155,7 @@ struct Params {
   int n_router, n_topk;
   int router_tiles;    // 1: router items are 16 x 16 MFMA tiles (batches above 16 rows)
   int router_ks;       // H split of a tile: item (tile, ks) writes partial logits ks
-  int i_router_end, i_sgu_end, i_topk_end;
+  int i_router_end, i_topk_end, i_pre_end;   // list: router, top-k, shared gate/up, then routed
   int n_sdn;           // shared down items
   int n_cmb;           // combine items: ceil(T / kCombineRows) * n_rg
   // LDS offsets (bytes)
@@ -1021,7 +1023,8 @@ __device__ __forceinline__ bool combine_item(KParams& p, const Lds& L, int rc, i
 // ----------------------------------------------------------------------------
 template <int NMB, bool XL>
 struct GuStage {
-  static constexpr int D = XL ? 4 : (NMB == 1 ? 2 : 1);   // tiles per stage
+  // tiles per stage (two stages are in flight)
+  static constexpr int D = XL ? 4 : (NMB == 1 ? 2 : 1);
   u32x4 w[D];
   f32x2 s[D];
   u32x4 a[XL ? 1 : D][2][NMB];
@@ -1527,7 +1530,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
       n_ev += 2;
     }
     n_mr = L.misc[0];
-    i_rgu_end = p.i_topk_end + n_mr * p.n_rb13;
+    i_rgu_end = p.i_pre_end + n_mr * p.n_rb13;
     i_sdn_end = i_rgu_end + p.n_sdn;
     i_rdn_end = i_sdn_end + n_mr * p.n_rg;
     i_total = i_rdn_end + p.n_cmb;
@@ -1581,10 +1584,10 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
   int* const claim_ctr = p.ctr + kCtrTicket + cgroup * kLine;
   it = blockIdx.x;
   for (;;) {
-    if (!dyn && it >= p.i_topk_end) {
+    if (!dyn && it >= p.i_pre_end) {
       ensure_x();
       if (!ensure_routing()) break;
-      i_dyn = max(p.i_topk_end, i_total - G);
+      i_dyn = max(p.i_pre_end, i_total - G);
       if (it >= i_dyn) {        // past the static part: claim (blocking, once)
         dyn = true;
         if (tid == 0) L.misc[2] = i_dyn + cgroup + kClaimGroups * atomic_add_agent(claim_ctr, 1);
@@ -1601,10 +1604,10 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
       kind = 0;
       if (p.router_tiles) router_tile_item(p, L, it);
       else router_item(p, L, it);
-    } else if (it < p.i_sgu_end) {
+    } else if (it >= p.i_topk_end && it < p.i_pre_end) {
       kind = 1;
       ensure_x();
-      const int i = it - p.i_router_end;
+      const int i = it - p.i_topk_end;
       const int mr = i / p.n_rb13, rb = i % p.n_rb13;
       const int r0 = mr * kMRange;
       run_gu(p.E, p.T * p.K, r0, min(kMRange, p.T - r0), rb, true);
@@ -1612,7 +1615,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
       kind = 2;
       if (!wait_geq(p, go_flag(p.ctr + kCtrRouterGo), 1, L.misc + 1, 1 << 20)) break;
       t_ready = wall_clock64();
-      if (!topk_item(p, L, it - p.i_sgu_end)) break;
+      if (!topk_item(p, L, it - p.i_router_end)) break;
       publish_done(p.ctr + kCtrTopkDone, p.n_topk, p.ctr + kCtrTopkGo);
     } else {
       kind = 6;
@@ -1622,7 +1625,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
       if (it >= i_total) break;
       if (it < i_rgu_end) {
         kind = 4;
-        const int i = it - p.i_topk_end;
+        const int i = it - p.i_pre_end;
         const int m = i / p.n_rb13, rb = i % p.n_rb13;
         const int e = L.mrlist[m];
         const int r0 = (m - L.nmrb[e]) * kMRange;
@@ -1824,8 +1827,8 @@ Params make_params(const moe_decode_handle* h, int T) {
   }
   p.n_topk = p.local_topk ? 0 : (T + kWaves - 1) / kWaves;
   p.i_router_end = p.n_router;
-  p.i_sgu_end = p.i_router_end + p.n_mr_sh * p.n_rb13;
-  p.i_topk_end = p.i_sgu_end + p.n_topk;
+  p.i_topk_end = p.i_router_end + p.n_topk;
+  p.i_pre_end = p.i_topk_end + p.n_mr_sh * p.n_rb13;
   p.n_sdn = p.n_mr_sh * p.n_rg;
   p.n_cmb = (T + kCombineRows - 1) / kCombineRows * p.n_rg;
   // LDS layout
