@@ -83,12 +83,12 @@ constexpr int kFullTiles = 16;              // tiles per wave of the fully unrol
 constexpr int kCombineRows = 4;             // rows per combine item
 // Counter block (int32 words).  Every counter sits on a 256-byte line of its
 // own (kLine words apart): a line many workgroups poll or bump must not also
-// carry another hot word.
+// carry another hot word.  There are two blocks: a run uses block
+// (epoch & 1) and, at its start, clears the other one for the next run, so
+// no run has to reset anything on its way out.
 constexpr int kLine = 64;
 constexpr int kCtrRouterDone = 0 * kLine;   // router items done
 constexpr int kCtrTopkDone = 1 * kLine;     // distributed top-k items done
-constexpr int kCtrExit = 2 * kLine;
-constexpr int kCtrStatus = 3 * kLine;
 constexpr int kClaimGroups = 8;             // claim counters (workgroup index mod 8)
 constexpr int kCtrTicket = 4 * kLine;       // [kClaimGroups] next unclaimed dynamic item of each group
 constexpr int kCtrHReady = (4 + kClaimGroups) * kLine;   // [E+S] gate/up publications per expert (E+S <= 257)
@@ -131,7 +131,9 @@ struct Params {
   float* topk_w;       // [T][K]
   uint64_t* h_scr;     // [T*K + T*S][I/2] two bf16 of h | epoch, rows grouped by expert
   uint64_t* o_scr;     // [T*K + T*S][H] expert outputs (fp32 bits | epoch)
-  int* ctr;            // counters
+  int* ctr;            // this run's counter block
+  int* ctr_next;       // the other block: cleared during this run for the next one
+  int* status;         // in-kernel status word (0 = ok), outside the blocks
   uint32_t epoch;      // this run's tag, never 0 (the workspace starts zeroed)
   // debug copies (nullable)
   int* dbg_idx;
@@ -280,6 +282,13 @@ __device__ __forceinline__ u32x4 ld_coh16(const void* p) {
 // Wait until this wave's outstanding memory operations are acknowledged.
 __device__ __forceinline__ void wait_stores() { __builtin_amdgcn_s_waitcnt(0); }
 
+// Timeline clock: read only when a trace buffer was given (a clock read
+// costs a scalar-memory round trip).
+__device__ __forceinline__ long long tl_clock(KParams& p) { return p.trace ? (long long)wall_clock64() : 0; }
+__device__ __forceinline__ long long tl_cycles(KParams& p) {
+  return p.trace ? (long long)__builtin_amdgcn_s_memtime() : 0;
+}
+
 // Tagged hand-offs.  Logits, h and expert outputs travel as 64-bit words:
 // 32 bits of payload, and the run's epoch in the high half.  A 64-bit store
 // is single-copy atomic, so a reader that sees the current epoch sees the
@@ -359,10 +368,10 @@ __device__ bool wait_geq(KParams& p, int* ctr, int target, SHARED int* lds_flag,
       int spins = 0;
       while (true) {
         if (load_agent(ctr) >= target) break;
-        if ((spins & 7) == 7 && load_agent(p.ctr + kCtrStatus) != 0) { ok = 0; break; }
+        if ((spins & 7) == 7 && load_agent(p.status) != 0) { ok = 0; break; }
         if ((long long)wall_clock64() > t_end) {
           int expected = 0;
-          __hip_atomic_compare_exchange_strong((GLOBAL int*)(p.ctr + kCtrStatus), &expected, MOE_ERR_TIMEOUT,
+          __hip_atomic_compare_exchange_strong((GLOBAL int*)(p.status), &expected, MOE_ERR_TIMEOUT,
                                                __ATOMIC_RELAXED, __ATOMIC_RELAXED,
                                                __HIP_MEMORY_SCOPE_AGENT);
           ok = 0;
@@ -379,7 +388,7 @@ __device__ bool wait_geq(KParams& p, int* ctr, int target, SHARED int* lds_flag,
     }
     *lds_flag = ok;
     // when the last wait ended (read back by the same thread for the timeline)
-    *(SHARED long long*)(lds_flag + 11) = (long long)wall_clock64();
+    *(SHARED long long*)(lds_flag + 11) = tl_clock(p);
   }
   __syncthreads();
   const int ok = *lds_flag;
@@ -429,10 +438,10 @@ __device__ bool poll_round(KParams& p, long long* t_end, SHARED int* lds_flag) {
     if (*t_end == 0) *t_end = now + p.deadline_ticks;
     if (now > *t_end) {
       int expected = 0;
-      __hip_atomic_compare_exchange_strong((GLOBAL int*)(p.ctr + kCtrStatus), &expected, MOE_ERR_TIMEOUT,
+      __hip_atomic_compare_exchange_strong((GLOBAL int*)(p.status), &expected, MOE_ERR_TIMEOUT,
                                            __ATOMIC_RELAXED, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       ok = 0;
-    } else if (load_agent(p.ctr + kCtrStatus) != 0) {
+    } else if (load_agent(p.status) != 0) {
       ok = 0;
     }
     __builtin_amdgcn_s_sleep(4);
@@ -1009,7 +1018,7 @@ __device__ __forceinline__ bool combine_item(KParams& p, const Lds& L, int rc, i
     const int o = threadIdx.x + kThreads * j;
     if (live[j]) st(p.y + (size_t)tt[j] * p.H + c0 + o % kDownRows, f32_to_bf16(acc));
   }
-  if (threadIdx.x == 0) *(SHARED long long*)(L.misc + 12) = (long long)wall_clock64();   // timeline
+  if (threadIdx.x == 0) *(SHARED long long*)(L.misc + 12) = tl_clock(p);   // timeline
   return true;
 }
 
@@ -1389,7 +1398,7 @@ __device__ __forceinline__ bool down_item_full(KParams& p, const Lds& L, int slo
     if (!wait_geq(p, p.ctr + kCtrHReady + slot * kLine, h_target, L.misc + 1)) return false;
     if (!stage_h_rows(p, L, sbase + r0, nrows)) return false;
   } else if (threadIdx.x == 0) {
-    *(SHARED long long*)(L.misc + 12) = (long long)wall_clock64();   // inputs ready (timeline)
+    *(SHARED long long*)(L.misc + 12) = tl_clock(p);   // inputs ready (timeline)
   }
   __syncthreads();
   if (nrb <= 0) return true;
@@ -1452,10 +1461,29 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
   bool routed = false;          // routing and placement are in LDS
   int i_rgu_end = 0, i_sdn_end = 0, i_rdn_end = 0, i_total = 0, n_mr = 0;
 
+  // The last workgroup clears the other counter block for the next run (no
+  // one uses it during this run).
+  if ((int)blockIdx.x == G - 1) {
+    int* q = p.ctr_next;
+    const int n_words = 2 + kClaimGroups + (p.E + p.S) + p.n_rg + 2 * kGoLines;
+    for (int i = tid; i < n_words; i += kThreads) {
+      int off;
+      if (i < 2) off = i == 0 ? kCtrRouterDone : kCtrTopkDone;
+      else if (i < 2 + kClaimGroups) off = kCtrTicket + (i - 2) * kLine;
+      else if (i < 2 + kClaimGroups + p.E + p.S) off = kCtrHReady + (i - 2 - kClaimGroups) * kLine;
+      else if (i < 2 + kClaimGroups + p.E + p.S + p.n_rg) off = kCtrRgDone + (i - 2 - kClaimGroups - p.E - p.S) * kLine;
+      else {
+        const int g = i - 2 - kClaimGroups - p.E - p.S - p.n_rg;
+        off = (g < kGoLines ? kCtrRouterGo + g * kGoStride : kCtrTopkGo + (g - kGoLines) * kGoStride);
+      }
+      store_agent(q + off, 0);
+    }
+  }
+
   // optional timeline of this workgroup (thread 0 writes it)
   long long* trace = (p.trace && (int)blockIdx.x < p.trace_blocks)
                          ? p.trace + (size_t)blockIdx.x * (1 + p.trace_cap) * 4 : nullptr;
-  const long long t_entry = wall_clock64();
+  const long long t_entry = tl_clock(p);
   int n_ev = 0;
   long long t_got = 0, t_ready = 0;
   int kind = 0, it = 0;
@@ -1474,17 +1502,17 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
   // copied from the distributed top-k items) and the bitmap placement.
   auto ensure_routing = [&]() __attribute__((always_inline)) -> bool {
     if (routed) return true;
-    const long long r_start = wall_clock64();
+    const long long r_start = tl_clock(p);
     long long r_go = 0, r_lg = 0, r_row0 = 0, c_lg = 0;
     if (p.local_topk) {
       // the wait's barrier also keeps earlier readers of the lg area safe
       if (!wait_geq(p, go_flag(p.ctr + kCtrRouterGo), 1, L.misc + 1, 1 << 20)) return false;
-      r_go = wall_clock64();
+      r_go = tl_clock(p);
       // all T x E logits into LDS (one round of loads unless some are late)
       if (!gather_logits(p, L, 0, p.T)) return false;
       __syncthreads();
-      r_lg = wall_clock64();
-      c_lg = (long long)__builtin_amdgcn_s_memtime();
+      r_lg = tl_clock(p);
+      c_lg = tl_cycles(p);
       // rows w, w+4 | w+8, w+12 | ... two at a time per wave
       for (int t0 = wave_id(); t0 < p.T; t0 += 2 * kWaves) {
         const int t1 = t0 + kWaves;
@@ -1492,7 +1520,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
         int e[2];
         float wk[2];
         topk_rows<2>(p, L.lg, tr, e, wk);
-        if (t0 == 0) r_row0 = wall_clock64();
+        if (t0 == 0) r_row0 = tl_clock(p);
         if (lane_id() < p.K) {
           L.tki[t0 * p.K + lane_id()] = (int16_t)e[0];
           L.tkw[t0 * p.K + lane_id()] = wk[0];
@@ -1509,12 +1537,12 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
         L.tkw[i] = ld_coh(p.topk_w + i);
       }
     }
-    const long long r_rows = wall_clock64();
-    const long long c_rows = (long long)__builtin_amdgcn_s_memtime();
+    const long long r_rows = tl_clock(p);
+    const long long c_rows = tl_cycles(p);
     __syncthreads();
-    const long long r_topk = wall_clock64();
+    const long long r_topk = tl_clock(p);
     build_placement(p, L);
-    const long long r_place = wall_clock64();
+    const long long r_place = tl_clock(p);
     if (blockIdx.x == 0) write_routing_debug(p, L);
     if (trace && tid == 0 && n_ev + 1 < p.trace_cap) {   // routing phases: kinds 8, 9
       long long* r = trace + (size_t)(1 + n_ev) * 4;
@@ -1599,7 +1627,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
     const bool claim = routed && (dyn || it + G >= i_dyn);
     int claimed = 0;              // raw counter value; read only after the item
     if (tid == 0 && claim) claimed = atomic_add_agent(claim_ctr, 1);
-    t_got = t_ready = wall_clock64();
+    t_got = t_ready = tl_clock(p);
     if (it < p.i_router_end) {
       kind = 0;
       if (p.router_tiles) router_tile_item(p, L, it);
@@ -1614,14 +1642,14 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
     } else if (it < p.i_topk_end) {
       kind = 2;
       if (!wait_geq(p, go_flag(p.ctr + kCtrRouterGo), 1, L.misc + 1, 1 << 20)) break;
-      t_ready = wall_clock64();
+      t_ready = tl_clock(p);
       if (!topk_item(p, L, it - p.i_router_end)) break;
       publish_done(p.ctr + kCtrTopkDone, p.n_topk, p.ctr + kCtrTopkGo);
     } else {
       kind = 6;
       ensure_x();
       if (!ensure_routing()) break;
-      t_ready = wall_clock64();
+      t_ready = tl_clock(p);
       if (it >= i_total) break;
       if (it < i_rgu_end) {
         kind = 4;
@@ -1675,25 +1703,8 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
     st(trace + 3, (long long)G);
   }
 
-  // The last workgroup out resets the counters for the next run.
+  // a deferred column-group count still has to be given
   flush_pending_now(p, pend_rg);
-  wait_stores();
-  __syncthreads();
-  if (tid == 0) {
-    const int old = atomic_add_agent(p.ctr + kCtrExit, 1);
-    if (old == G - 1) {
-      store_agent(p.ctr + kCtrRouterDone, 0);
-      store_agent(p.ctr + kCtrTopkDone, 0);
-      for (int c = 0; c < kClaimGroups; ++c) store_agent(p.ctr + kCtrTicket + c * kLine, 0);
-      for (int i = 0; i < kGoLines; ++i) {
-        store_agent(p.ctr + kCtrRouterGo + i * kGoStride, 0);
-        store_agent(p.ctr + kCtrTopkGo + i * kGoStride, 0);
-      }
-      for (int e = 0; e < p.E + p.S; ++e) store_agent(p.ctr + kCtrHReady + e * kLine, 0);
-      for (int rg = 0; rg < p.n_rg; ++rg) store_agent(p.ctr + kCtrRgDone + rg * kLine, 0);
-      store_agent(p.ctr + kCtrExit, 0);
-    }
-  }
 }
 
 // ----------------------------------------------------------------------------
@@ -1804,7 +1815,7 @@ Params make_params(const moe_decode_handle* h, int T) {
   p.topk_w = h->topk_w;
   p.h_scr = h->h_scr;
   p.o_scr = h->o_scr;
-  p.ctr = h->ctr;
+  p.status = h->ctr + 2 * (size_t)kCtrHead;
   const long long dl = c.deadline_us > 0 ? c.deadline_us : 1000000;
   p.deadline_ticks = dl * 100;   // wall clock runs at 100 MHz
   p.router_tiles = T > kMBlock ? 1 : 0;
@@ -1941,7 +1952,7 @@ moe_status moe_decode_create(const moe_decode_config* cfg, const moe_decode_weig
                  I = cfg->intermediate, K = cfg->top_k, Tm = cfg->max_tokens;
     const size_t slots = E + S;
     const size_t scr_rows = Tm * K + Tm * S;
-    const size_t ctr_words = kCtrHead;
+    const size_t ctr_words = 2 * (size_t)kCtrHead + kLine;   // two blocks + the status line
     struct A { void** p; size_t bytes; } allocs[] = {
         {(void**)&h->router_w, E * H * 4},
         {(void**)&h->router_b, w->router_bias ? E * 4 : 0},
@@ -2014,12 +2025,29 @@ moe_status moe_decode_run(moe_decode_handle* h, const void* x, int32_t T, void* 
   }
   hipStream_t stream = (hipStream_t)hip_stream;
   std::lock_guard<std::mutex> lock(h->mu);
-  // a new tag for this run (0 is skipped: the workspace starts zeroed)
-  h->epoch = h->epoch + 1 == 0 ? 1 : h->epoch + 1;
-  p.epoch = h->epoch;
   int prev = 0;
   HIP_TRY(hipGetDevice(&prev));
   if (prev != h->device) HIP_TRY(hipSetDevice(h->device));
+  // A new tag for this run.  After 2^32 - 1 runs the tag would come back to
+  // values that old words may still carry: then every tagged buffer and both
+  // counter blocks are zeroed (on the stream) and the tags start over at 1.
+  if (h->epoch + 1 == 0) {
+    const moe_decode_config& c = h->cfg;
+    const size_t rows = (size_t)c.max_tokens * (c.top_k + c.num_shared);
+    if (hipMemsetAsync(h->lgt, 0, (size_t)c.max_tokens * c.num_experts * 8 * kRouterKsMax, stream) != hipSuccess ||
+        hipMemsetAsync(h->h_scr, 0, rows * (c.intermediate / 2) * 8, stream) != hipSuccess ||
+        hipMemsetAsync(h->o_scr, 0, rows * c.hidden * 8, stream) != hipSuccess ||
+        hipMemsetAsync(h->ctr, 0, 2 * (size_t)kCtrHead * 4, stream) != hipSuccess) {
+      if (prev != h->device) (void)hipSetDevice(prev);
+      return MOE_ERR_HIP;
+    }
+    h->epoch = 0;
+  }
+  h->epoch += 1;
+  p.epoch = h->epoch;
+  // counter block of this run (tag parity) and the one it clears for the next
+  p.ctr = h->ctr + (size_t)(h->epoch & 1) * kCtrHead;
+  p.ctr_next = h->ctr + (size_t)((h->epoch + 1) & 1) * kCtrHead;
   // variants: 0 = x in LDS, 1 = up to 16 rows, 2 = more rows (4 MFMA blocks per item)
   const int variant = p.xs_stride > 0 ? 0 : (T > kMBlock ? 2 : 1);
   const void* fn = variant == 0 ? (const void*)moe_decode_kernel<1, true>
@@ -2055,12 +2083,12 @@ moe_status moe_decode_check(moe_decode_handle* h) {
   moe_status rc = MOE_OK;
   int status = 0;
   if (hipStreamSynchronize(h->last_stream) != hipSuccess ||
-      hipMemcpy(&status, h->ctr + kCtrStatus, 4, hipMemcpyDeviceToHost) != hipSuccess) {
+      hipMemcpy(&status, h->ctr + 2 * (size_t)kCtrHead, 4, hipMemcpyDeviceToHost) != hipSuccess) {
     rc = MOE_ERR_HIP;
   } else if (status != 0) {
     rc = MOE_ERR_TIMEOUT;
     const int zero = 0;
-    if (hipMemcpy(h->ctr + kCtrStatus, &zero, 4, hipMemcpyHostToDevice) != hipSuccess) rc = MOE_ERR_HIP;
+    if (hipMemcpy(h->ctr + 2 * (size_t)kCtrHead, &zero, 4, hipMemcpyHostToDevice) != hipSuccess) rc = MOE_ERR_HIP;
   }
   if (prev != h->device) (void)hipSetDevice(prev);
   return rc;
