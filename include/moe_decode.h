@@ -119,6 +119,13 @@ typedef struct moe_decode_debug {
   int64_t* trace;
   int32_t trace_blocks;
   int32_t trace_cap;
+  /*
+   * Test control: nonzero makes every in-kernel wait of this run give up at its
+   * first check, as if its deadline had passed.  The run then ends early with
+   * MOE_ERR_TIMEOUT reported by moe_decode_check (y undefined); the next run on
+   * the handle is unaffected.  0 for normal runs.
+   */
+  int32_t expire_waits;
 } moe_decode_debug;
 
 typedef struct moe_decode_handle moe_decode_handle;

@@ -65,6 +65,7 @@ class moe_decode_debug(ctypes.Structure):
         ("trace", ctypes.c_void_p),
         ("trace_blocks", ctypes.c_int32),
         ("trace_cap", ctypes.c_int32),
+        ("expire_waits", ctypes.c_int32),
     ]
 
 
@@ -179,7 +180,8 @@ class MoeDecode:
                                    _ptr(debug.get("pair_rank")), _ptr(debug.get("expert_count")),
                                    _ptr(debug.get("logits")), _ptr(tr),
                                    0 if tr is None else tr.shape[0],
-                                   0 if tr is None else tr.shape[1] - 1)
+                                   0 if tr is None else tr.shape[1] - 1,
+                                   int(debug.get("expire_waits", 0)))
         s = stream if stream is not None else torch.cuda.current_stream()
         st = moe_decode_run(self.handle, x.data_ptr(), T, y.data_ptr(), dbg, s.cuda_stream)
         if st != MOE_OK:

@@ -145,6 +145,7 @@ struct Params {
   int trace_blocks, trace_cap;
   // derived
   long long deadline_ticks;  // wall-clock ticks (100 MHz)
+  int expire_waits;    // test control: every wait gives up at its first check
   int local_topk;      // 1: every workgroup selects top-k itself
   int n_rb13;          // gate/up row blocks per expert: I/8
   int n_q13;           // tiles along H: H/64
@@ -364,7 +365,7 @@ __device__ bool wait_geq(KParams& p, int* ctr, int target, SHARED int* lds_flag,
   if (threadIdx.x == 0) {
     int ok = 1;
     if (load_agent(ctr) < target) {
-      const long long t_end = (long long)wall_clock64() + p.deadline_ticks;
+      const long long t_end = (long long)wall_clock64() + (p.expire_waits ? 0 : p.deadline_ticks);
       int spins = 0;
       while (true) {
         if (load_agent(ctr) >= target) break;
@@ -435,7 +436,7 @@ __device__ bool poll_round(KParams& p, long long* t_end, SHARED int* lds_flag) {
   if (threadIdx.x == 0) {
     int ok = 1;
     const long long now = (long long)wall_clock64();
-    if (*t_end == 0) *t_end = now + p.deadline_ticks;
+    if (*t_end == 0) *t_end = now + (p.expire_waits ? 0 : p.deadline_ticks);
     if (now > *t_end) {
       int expected = 0;
       __hip_atomic_compare_exchange_strong((GLOBAL int*)(p.status), &expected, MOE_ERR_TIMEOUT,
@@ -2017,6 +2018,7 @@ moe_status moe_decode_run(moe_decode_handle* h, const void* x, int32_t T, void* 
     p.dbg_rank = dbg->pair_rank;
     p.dbg_count = dbg->expert_count;
     p.dbg_logits = dbg->logits;
+    p.expire_waits = dbg->expire_waits != 0;
     if (dbg->trace && dbg->trace_blocks > 0 && dbg->trace_cap > 0) {
       p.trace = (long long*)dbg->trace;
       p.trace_blocks = dbg->trace_blocks;

@@ -141,3 +141,23 @@ def test_power_of_two_down_scales_scale_y_exactly():
     got = device.run_once(layer, inp.x, wl.E, wl.K, debug=False)["y"]
     layer.close()
     assert np.array_equal(O.bf16_bits_to_f64(got), 0.25 * O.bf16_bits_to_f64(base))
+
+
+def test_expired_waits_report_timeout_and_the_next_run_recovers():
+    """Deadline path, forced from the host: every in-kernel wait of the run gives
+    up at once.  The kernel must end (no hang), report MOE_ERR_TIMEOUT through
+    check, clear it, and leave the handle fit for the next run."""
+    wl = synth.WORKLOADS[1]
+    print(f"case expire_waits on {wl.name}", flush=True)
+    inp = inputs_for(wl)
+    layer = device.make_layer(inp)
+    dev = torch.device("cuda", 0)
+    x = device.to_device(inp.x, dev)
+    y = torch.empty_like(x)
+    for _ in range(2):
+        layer.run(x, y, wl.T, {"expire_waits": 1})
+        assert layer.check() == binding.MOE_ERR_TIMEOUT
+    assert layer.check() == binding.MOE_OK
+    out = device.run_once(layer, inp.x, wl.E, wl.K)
+    check_against_oracle(wl, inp, out)
+    layer.close()
