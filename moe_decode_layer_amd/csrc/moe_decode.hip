@@ -871,6 +871,73 @@ __device__ __forceinline__ void topk_rows(KParams& p, const SHARED float* lg, co
   }
 }
 
+// Maximum / minimum over each 32-lane half of the wave (lanes 0-31 and
+// 32-63 separately), returned in every lane of the half: DPP within each
+// 16-lane row, then the gfx950 16-lane swap between the rows of a half.
+__device__ __forceinline__ uint32_t half_max_v(uint32_t v) {
+  v = max(v, dpp<kDppXor1>(v));
+  v = max(v, dpp<kDppXor2>(v));
+  v = max(v, dpp<kDppHalfMirror>(v));
+  v = max(v, dpp<kDppMirror>(v));
+  const auto b = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  return max(b[0], b[1]);
+}
+__device__ __forceinline__ uint32_t half_min_v(uint32_t v) {
+  v = min(v, dpp<kDppXor1>(v));
+  v = min(v, dpp<kDppXor2>(v));
+  v = min(v, dpp<kDppHalfMirror>(v));
+  v = min(v, dpp<kDppMirror>(v));
+  const auto b = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  return min(b[0], b[1]);
+}
+__device__ __forceinline__ float half_sum_v(float v) {
+  v += dpp<kDppXor1>(v);
+  v += dpp<kDppXor2>(v);
+  v += dpp<kDppHalfMirror>(v);
+  v += dpp<kDppMirror>(v);
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// Top-k of two rows in one wave, one per 32-lane half: lane l of half h
+// holds experts 8 (l % 32) .. 8 (l % 32) + 7 of row t[h] as order-preserving
+// keys.  Each of the K rounds takes the half's maximum key and, among its
+// holders, the lowest expert id (lowest lane, then its lowest slot), then
+// retires it, so both rows share every reduction.  Returns, in lanes k < K
+// of each half, that half's row's k-th expert and weight.
+__device__ __forceinline__ void topk_pair(KParams& p, const SHARED float* lg, int tA, int tB, int* out_e,
+                                          float* out_w) {
+  const uint32_t hl = lane_id() & 31;
+  const int t = lane_id() < 32 ? tA : tB;
+  const int K = p.K;
+  uint32_t uk[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int e = 8 * hl + j;
+    const float v = lg[t * p.E + min(e, p.E - 1)];
+    uk[j] = e < p.E ? order_ukey(v) : 0u;
+  }
+  uint32_t sel_k = 0, sel_e = 0;
+  for (int k = 0; k < K; ++k) {
+    uint32_t m = uk[0];
+#pragma unroll
+    for (int j = 1; j < 8; ++j) m = max(m, uk[j]);
+    const uint32_t M = half_max_v(m);
+    uint32_t fj = 7;
+#pragma unroll
+    for (int j = 6; j >= 0; --j) fj = uk[j] == M ? (uint32_t)j : fj;
+    const uint32_t W = half_min_v(m == M ? 8 * hl + fj : 0xffffu);
+    sel_k = hl == (uint32_t)k ? M : sel_k;
+    sel_e = hl == (uint32_t)k ? W : sel_e;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) uk[j] = 8 * hl + j == W ? 0u : uk[j];
+  }
+  const float s = (int)hl < K ? 1.0f / (1.0f + __expf(-ukey_value(sel_k))) : 0.f;
+  const float sum = half_sum_v(s);
+  *out_e = (int)sel_e;
+  *out_w = s / sum;
+}
+
 // Copy rows [t0, t0 + nt) of this run's router logits into LDS lg (row-major,
 // from row 0) once every one of them carries the current epoch.
 __device__ __forceinline__ bool gather_logits(KParams& p, const Lds& L, int t0, int nt) {
@@ -1514,21 +1581,18 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
       __syncthreads();
       r_lg = tl_clock(p);
       c_lg = tl_cycles(p);
-      // rows w, w+4 | w+8, w+12 | ... two at a time per wave
-      for (int t0 = wave_id(); t0 < p.T; t0 += 2 * kWaves) {
-        const int t1 = t0 + kWaves;
-        const int tr[2] = {t0, min(t1, p.T - 1)};
-        int e[2];
-        float wk[2];
-        topk_rows<2>(p, L.lg, tr, e, wk);
+      // rows 2w, 2w+1 (then 2w+8, 2w+9): one pair per wave, a row per half
+      for (int t0 = 2 * wave_id(); t0 < p.T; t0 += 2 * kWaves) {
+        const int t1 = min(t0 + 1, p.T - 1);
+        int e;
+        float wk;
+        topk_pair(p, L.lg, t0, t1, &e, &wk);
         if (t0 == 0) r_row0 = tl_clock(p);
-        if (lane_id() < p.K) {
-          L.tki[t0 * p.K + lane_id()] = (int16_t)e[0];
-          L.tkw[t0 * p.K + lane_id()] = wk[0];
-          if (t1 < p.T) {
-            L.tki[t1 * p.K + lane_id()] = (int16_t)e[1];
-            L.tkw[t1 * p.K + lane_id()] = wk[1];
-          }
+        const int hl = lane_id() & 31;
+        const int t = lane_id() < 32 ? t0 : t0 + 1;
+        if (hl < p.K && t < p.T) {
+          L.tki[t * p.K + hl] = (int16_t)e;
+          L.tkw[t * p.K + hl] = wk;
         }
       }
     } else {
