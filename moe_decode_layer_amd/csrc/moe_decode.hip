@@ -69,6 +69,12 @@ constexpr int kMRange = 64;                 // rows per expert item (<= 4 MFMA b
 constexpr int kRouterRows = 8;              // rows per router item (small batches)
 constexpr int kRouterTile = 16;             // rows and experts per router tile (larger batches)
 constexpr int kRouterKsMax = 8;             // a router tile's H may be split over up to 8 items
+// Small batches: the logits are laid out [copy][E][lg_tp] (lg_tp = 8 or 16
+// rows), so each expert's rows sit together and a 128-byte line has at most
+// two writers (lines written piecewise by many workgroups become readable
+// much later); every router item writes lg_copies copies and each workgroup
+// reads one, so a line has a fraction of the workgroups as readers
+constexpr int kLgCopies = 8;
 constexpr int kDownRows = 128;              // output rows per down item (8 row blocks)
 constexpr int kTileRows = 16;               // weight rows per tile
 constexpr int kTileK = 64;                  // K elements per tile (two scale groups)
@@ -87,19 +93,17 @@ constexpr int kCombineRows = 4;             // rows per combine item
 // (epoch & 1) and, at its start, clears the other one for the next run, so
 // no run has to reset anything on its way out.
 constexpr int kLine = 64;
-constexpr int kCtrRouterDone = 0 * kLine;   // router items done
 constexpr int kCtrTopkDone = 1 * kLine;     // distributed top-k items done
 constexpr int kClaimGroups = 8;             // claim counters (workgroup index mod 8)
 constexpr int kCtrTicket = 4 * kLine;       // [kClaimGroups] next unclaimed dynamic item of each group
 constexpr int kCtrHReady = (4 + kClaimGroups) * kLine;   // [E+S] gate/up publications per expert (E+S <= 257)
 constexpr int kCtrRgDone = kCtrHReady + 257 * kLine;   // [H/128] down-wave publications (<= 128)
-// "go" flags raised once by the last router item and by the last
-// distributed top-k item, polled by every workgroup: kGoLines copies, 1 KiB
-// apart, so the pollers spread over memory channels
+// "go" flag raised once by the last distributed top-k item, polled by every
+// workgroup: kGoLines copies, 1 KiB apart, so the pollers spread over memory
+// channels
 constexpr int kGoLines = 64;
 constexpr int kGoStride = 256;              // words
-constexpr int kCtrRouterGo = kCtrRgDone + 128 * kLine;
-constexpr int kCtrTopkGo = kCtrRouterGo + kGoLines * kGoStride;
+constexpr int kCtrTopkGo = kCtrRgDone + 128 * kLine;
 constexpr int kCtrHead = kCtrTopkGo + kGoLines * kGoStride;
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -113,13 +117,35 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 #define CONSTANT __attribute__((address_space(4)))
 #define SHARED __attribute__((address_space(3)))
 
+// Division of an index n < 2^23 by a fixed d > 0 as a multiply and a shift:
+// with l = ceil(log2 d), s = 23 + l and m = ceil(2^s / d), n m / 2^s exceeds
+// n / d by less than 1/d, so floor(n m / 2^s) = floor(n / d) (the round-up
+// method of Granlund and Montgomery).  Per-word index arithmetic in the
+// gathers would otherwise spend dozens of instructions on every division.
+struct FDiv {
+  uint32_t m, s, d;
+};
+static inline FDiv make_fdiv(uint32_t d) {
+  uint32_t l = 0;
+  while ((1ull << l) < d) ++l;
+  FDiv f;
+  f.d = d;
+  f.s = 23 + l;
+  f.m = (uint32_t)(((1ull << f.s) + d - 1) / d);
+  return f;
+}
+__device__ __forceinline__ uint32_t fdiv(uint32_t n, uint32_t m, uint32_t s) {
+  return (uint32_t)(((uint64_t)n * m) >> s);
+}
+
 struct Params {
   int T, H, E, K, S, I;
   // inputs / outputs
   const uint16_t* x;
   uint16_t* y;
   const float* router_w;
-  const float* router_b;
+  const float* router_b;   // [E] (without a bias: any readable [E] floats, unused)
+  int has_bias;
   const u32x4* w13p;   // [E+S][2I/16][H/64][64] tiles
   const float* s13p;   // [E+S][2I/16][H/64][16][2]
   const u32x4* w2p;    // [E+S][H/16][I/64][64]
@@ -147,6 +173,10 @@ struct Params {
   long long deadline_ticks;  // wall-clock ticks (100 MHz)
   int expire_waits;    // test control: every wait gives up at its first check
   int local_topk;      // 1: every workgroup selects top-k itself
+  int lg_copies, lg_tp_log2;
+  FDiv fd_x8;          // H / 8: 16-byte words of an x row
+  FDiv fd_h2;          // I / 2: tagged words of an h row
+  FDiv fd_part[4];     // n E for n = 1..4: logits of a distributed top-k item's rows
   int n_rb13;          // gate/up row blocks per expert: I/8
   int n_q13;           // tiles along H: H/64
   int n_rb2;           // down row blocks: H/16
@@ -430,9 +460,11 @@ __device__ __forceinline__ bool block_any(bool v, SHARED int* slots) {
   return any != 0;
 }
 
-// Thread 0 checks the deadline (started at *t_end == 0) and the error status
-// between polling rounds, then pauses; the verdict is broadcast through LDS.
-__device__ bool poll_round(KParams& p, long long* t_end, SHARED int* lds_flag) {
+// Thread 0 checks the deadline (started at *t_end == 0) between polling
+// rounds, and every 8th round (counted in *round) the error status, then
+// pauses; the verdict is broadcast through LDS.  The status is read only now
+// and then because its round trip would otherwise double every round's.
+__device__ bool poll_round(KParams& p, long long* t_end, int* round, SHARED int* lds_flag) {
   if (threadIdx.x == 0) {
     int ok = 1;
     const long long now = (long long)wall_clock64();
@@ -442,7 +474,7 @@ __device__ bool poll_round(KParams& p, long long* t_end, SHARED int* lds_flag) {
       __hip_atomic_compare_exchange_strong((GLOBAL int*)(p.status), &expected, MOE_ERR_TIMEOUT,
                                            __ATOMIC_RELAXED, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       ok = 0;
-    } else if (load_agent(p.status) != 0) {
+    } else if ((++*round & 7) == 0 && load_agent(p.status) != 0) {
       ok = 0;
     }
     __builtin_amdgcn_s_sleep(4);
@@ -500,8 +532,10 @@ struct Lds {
   SHARED float* tkw;              // [T][K] their weights
   SHARED float* red;              // partial sums of the 4 waves
   SHARED int* misc;               // [0] n_mr, [1] flag, [3..7) scan scratch, [8..12) block_any,
-                                  // [2] claimed item, [12..14) end of the last wait (thread 0)
-  SHARED uint32_t* tks;           // [kWaves][64] top-k scratch of each wave
+                                  // [2] claimed item, [12..14) end of the last wait (thread 0),
+                                  // [14] polling rounds of the last gather (thread 0),
+                                  // [16..22) ends of a gather's first rounds (timeline)
+  SHARED uint32_t* tks;           // [kThreads] one scratch word per thread (gather sink)
   SHARED uint16_t* xs;            // [T][xs_stride] the layer input (small batches)
   SHARED uint16_t* hs;            // [16][hs_stride] h rows of the current down item
   SHARED float* lg;               // [T][E] router logits (small batches)
@@ -528,32 +562,102 @@ __device__ Lds lds_view(KParams& p, SHARED char* smem) {
   return L;
 }
 
-// Gather n tagged words of this run with the whole workgroup: take(i, payload)
-// is called for every i whose word carries the current epoch (possibly more
-// than once); stale words are read again, round by round, until none is.
-// kBatch loads per thread are in flight before any is examined.  false: the
-// deadline passed or another workgroup reported an error.
-template <typename LoadFn, typename TakeFn>
-__device__ __forceinline__ bool gather_tagged(KParams& p, const Lds& L, int n, LoadFn load, TakeFn take) {
+// Gather the words i < n with want(i) of this run with the whole workgroup:
+// take(i, payload) is called for every such i whose word carries the current
+// epoch (possibly more than once); stale words are read again, round by
+// round, until none is.  kBatch loads per thread are in flight before any is
+// examined.  false: the deadline passed or another workgroup reported an
+// error.
+template <typename LoadFn, typename TakeFn, typename WantFn>
+__device__ __forceinline__ bool gather_tagged(KParams& p, const Lds& L, int n, LoadFn load, TakeFn take,
+                                              WantFn want) {
   long long t_end = 0;
+  // this thread's words still to take: bit kBatch j + b for word
+  // tid + (kBatch j + b) kThreads of the first 8 batches; words past those
+  // are all read again while any of them is stale
+  unsigned long long todo = ~0ull;
+  bool rest = true;
+  int rounds = 0;
   while (true) {
-    bool stale = false;
-    for (int i0 = threadIdx.x; i0 < n; i0 += kBatch * kThreads) {
+    bool stale = false, rest_stale = false;
+    int j = 0;
+    for (int i0 = threadIdx.x; i0 < n; i0 += kBatch * kThreads, ++j) {
+      const uint32_t m = j < 8 ? (uint32_t)(todo >> (kBatch * j)) & 0xffu : (rest ? 0xffu : 0u);
       uint64_t v[kBatch];
-#pragma unroll
-      for (int b = 0; b < kBatch; ++b) v[b] = load(min(i0 + b * kThreads, n - 1));
 #pragma unroll
       for (int b = 0; b < kBatch; ++b) {
         const int i = i0 + b * kThreads;
-        if (i < n) {
-          if (tag_ok(v[b], p.epoch)) take(i, (uint32_t)v[b]);
-          else stale = true;
+        v[b] = 0;
+        if (i < n && (m >> b & 1u) && want(i)) v[b] = load(i);
+      }
+#pragma unroll
+      for (int b = 0; b < kBatch; ++b) {
+        const int i = i0 + b * kThreads;
+        if (i < n && (m >> b & 1u) && want(i)) {
+          if (tag_ok(v[b], p.epoch)) {
+            take(i, (uint32_t)v[b]);
+            if (j < 8) todo &= ~(1ull << (kBatch * j + b));
+          } else {
+            stale = true;
+            rest_stale |= j >= 8;
+          }
         }
       }
     }
-    if (!block_any(stale, L.misc + 8)) return true;
-    if (!poll_round(p, &t_end, L.misc + 1)) return false;
+    rest = rest_stale;
+    if (p.trace && threadIdx.x == 0 && rounds < 3) ((SHARED long long*)(L.misc + 16))[rounds] = tl_clock(p);
+    if (!block_any(stale, L.misc + 8)) break;
+    if (!poll_round(p, &t_end, &rounds, L.misc + 1)) return false;
   }
+  // when the gather ended and its rounds (read back by thread 0 for the timeline)
+  if (threadIdx.x == 0) {
+    *(SHARED long long*)(L.misc + 12) = tl_clock(p);
+    L.misc[14] = rounds;
+  }
+  return true;
+}
+template <typename LoadFn, typename TakeFn>
+__device__ __forceinline__ bool gather_tagged(KParams& p, const Lds& L, int n, LoadFn load, TakeFn take) {
+  return gather_tagged(p, L, n, load, take, [](int) { return true; });
+}
+
+// The same for n <= kBatch kThreads words into LDS, without per-word
+// branches: thread tid owns words tid + b kThreads; while any of them is
+// missing it reloads all of them, and every word it examines is written,
+// to slot(i) when wanted and current, else to the thread's own scratch word.
+template <typename LoadFn, typename SlotFn, typename WantFn>
+__device__ __forceinline__ bool gather_small(KParams& p, const Lds& L, int n, LoadFn load, SlotFn slot,
+                                             WantFn want) {
+  long long t_end = 0;
+  int rounds = 0;
+  uint32_t need = 0;                           // bit b: word b wanted, not yet taken
+#pragma unroll
+  for (int b = 0; b < kBatch; ++b) {
+    const int i = threadIdx.x + b * kThreads;
+    need |= (i < n && want(i)) ? 1u << b : 0u;
+  }
+  SHARED uint32_t* const sink = L.tks + threadIdx.x;
+  while (true) {
+    if (need != 0u) {
+      uint64_t v[kBatch];
+#pragma unroll
+      for (int b = 0; b < kBatch; ++b) v[b] = load(min((int)threadIdx.x + b * kThreads, n - 1));
+#pragma unroll
+      for (int b = 0; b < kBatch; ++b) {
+        const bool ok = (need >> b & 1u) && tag_ok(v[b], p.epoch);
+        *(ok ? slot((int)threadIdx.x + b * kThreads) : sink) = (uint32_t)v[b];
+        need &= ok ? ~(1u << b) : ~0u;
+      }
+    }
+    if (p.trace && threadIdx.x == 0 && rounds < 3) ((SHARED long long*)(L.misc + 16))[rounds] = tl_clock(p);
+    if (!block_any(need != 0u, L.misc + 8)) break;
+    if (!poll_round(p, &t_end, &rounds, L.misc + 1)) return false;
+  }
+  if (threadIdx.x == 0) {
+    *(SHARED long long*)(L.misc + 12) = tl_clock(p);
+    L.misc[14] = rounds;
+  }
+  return true;
 }
 
 // Sort-free placement ("routing without sorting": each expert's rows go to
@@ -561,11 +665,15 @@ __device__ __forceinline__ bool gather_tagged(KParams& p, const Lds& L, int n, L
 // Every pair (t, k) sets bit t of expert idx[t][k]'s bitmap; an expert's
 // count is the popcount of its bitmap; a pair's rank is the popcount of the
 // expert's bits below t.  Row r of expert e lives at scratch row base[e] + r.
+// The bitmaps must be zero on entry (clear_placement, earlier, with a
+// barrier in between).  One block scan yields both the rows and the 64-row
+// ranges before each expert (packed 16 + 16 bits: T K <= 4096).
+__device__ __forceinline__ void clear_placement(KParams& p, const Lds& L) {
+  for (int i = threadIdx.x; i < p.E * p.nch; i += kThreads) L.bm[i] = 0ull;
+}
 __device__ __forceinline__ void build_placement(KParams& p, const Lds& L) {
   const int tid = threadIdx.x;
   const int E = p.E, K = p.K, T = p.T, nch = p.nch;
-  for (int i = tid; i < E * nch; i += kThreads) L.bm[i] = 0ull;
-  __syncthreads();
   for (int i = tid; i < T * K; i += kThreads) {
     const int t = i / K;
     const int e = L.tki[i];
@@ -579,20 +687,20 @@ __device__ __forceinline__ void build_placement(KParams& p, const Lds& L) {
       L.cp[tid * nch + ch] = c;
       c += __popcll(L.bm[tid * nch + ch]);
     }
-    L.cnt[tid] = c;
     nmr = (c + kMRange - 1) / kMRange;
   }
-  int tot_rows, tot_mr;
-  const int base = block_exclusive_scan(c, L.misc + 3, &tot_rows);
-  const int mrb = block_exclusive_scan(nmr, L.misc + 3, &tot_mr);
+  int tot;
+  const int packed = block_exclusive_scan(c | nmr << 16, L.misc + 3, &tot);
+  const int base = packed & 0xffff, mrb = packed >> 16;
   if (tid < E) {
+    L.cnt[tid] = c;
     L.base[tid] = base;
     L.nmrb[tid] = mrb;
     for (int j = 0; j < nmr; ++j) L.mrlist[mrb + j] = tid;
   }
   if (tid == 0) {
-    L.nmrb[E] = tot_mr;
-    L.misc[0] = tot_mr;
+    L.nmrb[E] = tot >> 16;
+    L.misc[0] = tot >> 16;
   }
   __syncthreads();
   for (int i = tid; i < T * K; i += kThreads) {
@@ -626,13 +734,6 @@ __device__ __forceinline__ void write_routing_debug(KParams& p, const Lds& L) {
 // Router: logits of expert e for up to 8 rows; the 4 waves split H.  x comes
 // from LDS when the batch is small enough to keep it there.
 // ----------------------------------------------------------------------------
-// The last router item raises the go flags (no store needs to be waited for
-// first: the readers check the tags).
-__device__ __forceinline__ void router_done(KParams& p) {
-  if (threadIdx.x == 0 && atomic_add_agent(p.ctr + kCtrRouterDone, 1) == p.n_router - 1)
-    for (int i = 0; i < kGoLines; ++i) store_agent(p.ctr + kCtrRouterGo + i * kGoStride, 1);
-}
-
 // Router tile (batches above 16 rows): logits of rows [16 rt, +16) x experts
 // [16 et, +16) with v_mfma_f32_16x16x4_f32; the 4 waves split H.  Lane l =
 // (n, kq), n = l % 16, kq = l / 16, loads 4 consecutive K of row n of x and
@@ -651,6 +752,10 @@ __device__ __forceinline__ void router_tile_item(KParams& p, const Lds& L, int i
   const int kbase = ks * (p.H / p.router_ks) + w * kw;
   const uint16_t* xr = p.x + (size_t)(t0 + min(n, nt - 1)) * p.H + kbase + 4 * kq;
   const float* wr = p.router_w + (size_t)(e0 + min(n, ne - 1)) * p.H + kbase + 4 * kq;
+  // the bias goes with part 0 (the top-k items add the parts in order); it
+  // is requested first, so its round trip overlaps the weights'
+  const float bv = ld(p.router_b + e0 + min(n, ne - 1));   // unconditional: no branch, no early wait
+  const float bias = (ks == 0 && p.has_bias && w == 0 && n < ne) ? bv : 0.f;
   // one accumulator per MFMA slot i, so consecutive MFMAs do not depend on
   // each other; the four are added in a fixed order at the end
   f32x4 acc[4];
@@ -695,25 +800,28 @@ __device__ __forceinline__ void router_tile_item(KParams& p, const Lds& L, int i
     f32x4 s = part[lane];
 #pragma unroll
     for (int ww = 1; ww < kWaves; ++ww) s += part[ww * kWave + lane];
-    // the bias goes with part 0; the top-k items add the parts in order
-    const float b = (ks == 0 && p.router_b && n < ne) ? ld(p.router_b + e0 + n) : 0.f;
     uint64_t* out = p.lgt + (size_t)ks * p.T * p.E;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = 4 * kq + i;
-      if (r < nt && n < ne) st_tag(out + (size_t)(t0 + r) * p.E + e0 + n, __float_as_uint(s[i] + b), p.epoch);
+      if (r < nt && n < ne) st_tag(out + (size_t)(t0 + r) * p.E + e0 + n, __float_as_uint(s[i] + bias), p.epoch);
     }
   }
   __syncthreads();                             // the partials area is free again
-  router_done(p);
 }
 
-__device__ __forceinline__ void router_item(KParams& p, const Lds& L, int item) {
+// With stage_x (the item covers every row), the x values it loads are also
+// written to the workgroup's LDS copy of x, which later items read.
+// Returns (timeline only) when this workgroup's partial sums were complete.
+__device__ __forceinline__ long long router_item(KParams& p, const Lds& L, int item, bool stage_x) {
   const int w = wave_id(), lane = lane_id();
   const int e = item % p.E;
   const int t0 = (item / p.E) * kRouterRows;
   const int nt = min(kRouterRows, p.T - t0);
   const int n16 = p.H / 16;                    // 16-element chunks
+  // the bias is requested first, so its round trip overlaps the weights'
+  const float bv = ld(p.router_b + e);        // unconditional: no branch, no early wait
+  const float bias = p.has_bias ? bv : 0.f;
   float acc[kRouterRows];
 #pragma unroll
   for (int j = 0; j < kRouterRows; ++j) acc[j] = 0.f;
@@ -740,6 +848,16 @@ __device__ __forceinline__ void router_item(KParams& p, const Lds& L, int item) 
       const f32x4 z = {0.f, 0.f, 0.f, 0.f};
       wv[i] = live ? wv[i] : z;
     }
+    if (stage_x && live) {
+#pragma unroll
+      for (int j = 0; j < kRouterRows; ++j) {
+        if (j < nt) {
+          SHARED u32x4* d = (SHARED u32x4*)(L.xs + (size_t)j * p.xs_stride + 16 * c);
+          d[0] = xv[j][0];
+          d[1] = xv[j][1];
+        }
+      }
+    }
 #pragma unroll
     for (int j = 0; j < kRouterRows; ++j) {
       float a = acc[j];
@@ -755,6 +873,9 @@ __device__ __forceinline__ void router_item(KParams& p, const Lds& L, int item) 
       acc[j] = a;
     }
   }
+#pragma unroll
+  for (int j = 0; j < kRouterRows; ++j) asm volatile("" ::"v"(acc[j]));
+  const long long t_sums = tl_clock(p);
   SHARED float* part = L.red;                  // [kWaves][8]
 #pragma unroll
   for (int j = 0; j < kRouterRows; ++j) {
@@ -768,15 +889,16 @@ __device__ __forceinline__ void router_item(KParams& p, const Lds& L, int item) 
     s = part[j];
 #pragma unroll
     for (int ww = 1; ww < kWaves; ++ww) s += part[ww * kRouterRows + j];
-    s += p.router_b ? ld(p.router_b + e) : 0.f;
+    s += bias;
   }
   __syncthreads();                             // the partials area is free again
   if (threadIdx.x < nt) {
     const int j = threadIdx.x;
-    st_tag(p.lgt + (size_t)(t0 + j) * p.E + e, __float_as_uint(s), p.epoch);
+    for (int c = 0; c < p.lg_copies; ++c)
+      st_tag(p.lgt + (((size_t)c * p.E + e) << p.lg_tp_log2) + t0 + j, __float_as_uint(s), p.epoch);
     if (p.dbg_logits) st(p.dbg_logits + (size_t)(t0 + j) * p.E + e, s);
   }
-  router_done(p);
+  return t_sums;
 }
 
 // ----------------------------------------------------------------------------
@@ -940,9 +1062,18 @@ __device__ __forceinline__ void topk_pair(KParams& p, const SHARED float* lg, in
 
 // Copy rows [t0, t0 + nt) of this run's router logits into LDS lg (row-major,
 // from row 0) once every one of them carries the current epoch.
-__device__ __forceinline__ bool gather_logits(KParams& p, const Lds& L, int t0, int nt) {
-  return gather_tagged(p, L, nt * p.E, [&](int i) { return ld_tag(p.lgt + (size_t)t0 * p.E + i); },
-                       [&](int i, uint32_t v) { L.lg[i] = __uint_as_float(v); });
+__device__ __forceinline__ bool gather_logits(KParams& p, const Lds& L) {
+  const int c = blockIdx.x % p.lg_copies;
+  const int sh = p.lg_tp_log2, mask = (1 << sh) - 1;
+  const uint64_t* src = p.lgt + ((size_t)c * p.E << sh);
+  auto load = [&](int i) { return ld_tag(src + i); };
+  auto want = [&](int i) { return (i & mask) < p.T; };
+  if ((p.E << sh) <= kBatch * kThreads)
+    return gather_small(p, L, p.E << sh, load,
+                        [&](int i) { return (SHARED uint32_t*)L.lg + (i & mask) * p.E + (i >> sh); }, want);
+  return gather_tagged(
+      p, L, p.E << sh, load, [&](int i, uint32_t v) { L.lg[(i & mask) * p.E + (i >> sh)] = __uint_as_float(v); },
+      want);
 }
 
 // Distributed top-k item (large batches): rows 4 item .. 4 item + 3, one per
@@ -953,10 +1084,12 @@ __device__ __forceinline__ bool topk_item(KParams& p, const Lds& L, int item) {
   const int nt = min(kWaves, p.T - t0);
   const int KS = p.router_ks;
   const int per_part = nt * p.E;
+  const uint32_t fm = p.fd_part[nt - 1].m, fs = p.fd_part[nt - 1].s;
   __syncthreads();                             // earlier readers of the lg area are done
   if (!gather_tagged(p, L, KS * per_part,
                      [&](int i) {
-                       return ld_tag(p.lgt + (size_t)(i / per_part) * p.T * p.E + (size_t)t0 * p.E + i % per_part);
+                       const int k = (int)fdiv((uint32_t)i, fm, fs);
+                       return ld_tag(p.lgt + (size_t)k * p.T * p.E + (size_t)t0 * p.E + (i - k * per_part));
                      },
                      [&](int i, uint32_t v) { L.lg[i] = __uint_as_float(v); }))
     return false;
@@ -986,9 +1119,16 @@ __device__ __forceinline__ bool topk_item(KParams& p, const Lds& L, int item) {
 // LDS, once each word carries this run's epoch.
 __device__ __forceinline__ bool stage_h_rows(KParams& p, const Lds& L, int row0, int nrows) {
   const int per_row = p.I / 2;                // tagged words per row
-  return gather_tagged(
-      p, L, nrows * per_row, [&](int i) { return ld_tag(p.h_scr + (size_t)row0 * per_row + i); },
-      [&](int i, uint32_t v) { *(SHARED uint32_t*)(L.hs + (size_t)(i / per_row) * p.hs_stride + 2 * (i % per_row)) = v; });
+  const uint64_t* src = p.h_scr + (size_t)row0 * per_row;
+  auto slot = [&](int i) {
+    const int r = (int)fdiv((uint32_t)i, p.fd_h2.m, p.fd_h2.s);
+    return (SHARED uint32_t*)(L.hs + (size_t)r * p.hs_stride + 2 * (i - r * per_row));
+  };
+  if (nrows * per_row <= kBatch * kThreads)
+    return gather_small(p, L, nrows * per_row, [&](int i) { return ld_tag(src + i); }, slot,
+                        [](int) { return true; });
+  return gather_tagged(p, L, nrows * per_row, [&](int i) { return ld_tag(src + i); },
+                       [&](int i, uint32_t v) { *slot(i) = v; });
 }
 
 // Wait until every word of h rows [row0, row0 + nrows) carries this run's
@@ -1029,6 +1169,7 @@ __device__ __forceinline__ bool combine_item(KParams& p, const Lds& L, int rc, i
   const int t0 = rc * kCombineRows;
   const int nt = min(kCombineRows, p.T - t0);
   long long t_end = 0;
+  int rounds = 0;
   // Many combine items (large batches) first wait for the column group's
   // count, so they do not poll expert outputs that are still far from done;
   // a few items poll the outputs' tags directly, re-reading only stale words.
@@ -1075,7 +1216,7 @@ __device__ __forceinline__ bool combine_item(KParams& p, const Lds& L, int rc, i
       for (int k = 0; k < kIn; ++k)
         if ((k < K || k == kMaxTopK) && live[j] && !tag_ok(v[j][k], p.epoch)) stale = true;
     if (!block_any(stale, L.misc + 8)) break;
-    if (!poll_round(p, &t_end, L.misc + 1)) return false;
+    if (!poll_round(p, &t_end, &rounds, L.misc + 1)) return false;
   }
 #pragma unroll
   for (int j = 0; j < kOut; ++j) {
@@ -1450,15 +1591,17 @@ __device__ __forceinline__ bool down_item_full(KParams& p, const Lds& L, int slo
   __syncthreads();
   bool stale = !fast;
   if (fast) {
+    // every word is written, to its place or (past the rows, or stale) to
+    // the thread's scratch word, so the check has no per-word branches
+    SHARED uint32_t* const sink = L.tks + threadIdx.x;
 #pragma unroll
     for (int b = 0; b < kHFast; ++b) {
       const int i = threadIdx.x + b * kThreads;
-      if (i < nh) {
-        if (tag_ok(hv[b], p.epoch))
-          *(SHARED uint32_t*)(L.hs + (size_t)(i / per_row) * p.hs_stride + 2 * (i % per_row)) = (uint32_t)hv[b];
-        else
-          stale = true;
-      }
+      const bool ok = tag_ok(hv[b], p.epoch);
+      const int r = (int)fdiv((uint32_t)i, p.fd_h2.m, p.fd_h2.s);
+      SHARED uint32_t* const d = (SHARED uint32_t*)(L.hs + (size_t)r * p.hs_stride + 2 * (i - r * per_row));
+      *(i < nh && ok ? d : sink) = (uint32_t)hv[b];
+      stale |= i < nh && !ok;
     }
   }
   if (block_any(stale, L.misc + 8)) {
@@ -1521,8 +1664,11 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
     if (x_staged) return;
     const int per_row = p.H / 8;
     batched_copy<u32x4>(
-        p.T * per_row, [&](int i) { return ld((const u32x4*)(p.x + (size_t)(i / per_row) * p.H) + i % per_row); },
-        [&](int i, u32x4 v) { *(SHARED u32x4*)(L.xs + (size_t)(i / per_row) * p.xs_stride + 8 * (i % per_row)) = v; });
+        p.T * per_row, [&](int i) { return ld((const u32x4*)p.x + i); },
+        [&](int i, u32x4 v) {
+          const int r = (int)fdiv((uint32_t)i, p.fd_x8.m, p.fd_x8.s);
+          *(SHARED u32x4*)(L.xs + (size_t)r * p.xs_stride + 8 * (i - r * per_row)) = v;
+        });
     __syncthreads();
     x_staged = true;
   };
@@ -1533,17 +1679,14 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
   // one uses it during this run).
   if ((int)blockIdx.x == G - 1) {
     int* q = p.ctr_next;
-    const int n_words = 2 + kClaimGroups + (p.E + p.S) + p.n_rg + 2 * kGoLines;
+    const int n_words = 1 + kClaimGroups + (p.E + p.S) + p.n_rg + kGoLines;
     for (int i = tid; i < n_words; i += kThreads) {
       int off;
-      if (i < 2) off = i == 0 ? kCtrRouterDone : kCtrTopkDone;
-      else if (i < 2 + kClaimGroups) off = kCtrTicket + (i - 2) * kLine;
-      else if (i < 2 + kClaimGroups + p.E + p.S) off = kCtrHReady + (i - 2 - kClaimGroups) * kLine;
-      else if (i < 2 + kClaimGroups + p.E + p.S + p.n_rg) off = kCtrRgDone + (i - 2 - kClaimGroups - p.E - p.S) * kLine;
-      else {
-        const int g = i - 2 - kClaimGroups - p.E - p.S - p.n_rg;
-        off = (g < kGoLines ? kCtrRouterGo + g * kGoStride : kCtrTopkGo + (g - kGoLines) * kGoStride);
-      }
+      if (i < 1) off = kCtrTopkDone;
+      else if (i < 1 + kClaimGroups) off = kCtrTicket + (i - 1) * kLine;
+      else if (i < 1 + kClaimGroups + p.E + p.S) off = kCtrHReady + (i - 1 - kClaimGroups) * kLine;
+      else if (i < 1 + kClaimGroups + p.E + p.S + p.n_rg) off = kCtrRgDone + (i - 1 - kClaimGroups - p.E - p.S) * kLine;
+      else off = kCtrTopkGo + (i - 1 - kClaimGroups - p.E - p.S - p.n_rg) * kGoStride;
       store_agent(q + off, 0);
     }
   }
@@ -1571,13 +1714,14 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
   auto ensure_routing = [&]() __attribute__((always_inline)) -> bool {
     if (routed) return true;
     const long long r_start = tl_clock(p);
+    clear_placement(p, L);                     // the barriers of the waits below order it
     long long r_go = 0, r_lg = 0, r_row0 = 0, c_lg = 0;
     if (p.local_topk) {
-      // the wait's barrier also keeps earlier readers of the lg area safe
-      if (!wait_geq(p, go_flag(p.ctr + kCtrRouterGo), 1, L.misc + 1, 1 << 20)) return false;
+      // all T x E logits into LDS: the router items' tagged words are
+      // polled directly (no completion count), late ones round by round
+      __syncthreads();                         // earlier readers of the lg area are done
       r_go = tl_clock(p);
-      // all T x E logits into LDS (one round of loads unless some are late)
-      if (!gather_logits(p, L, 0, p.T)) return false;
+      if (!gather_logits(p, L)) return false;
       __syncthreads();
       r_lg = tl_clock(p);
       c_lg = tl_cycles(p);
@@ -1616,11 +1760,17 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
       st(r + 2, r_go);
       st(r + 3, r_topk);
       r += 4;
-      st(r + 0, (long long)9 << 32 | (long long)((c_rows - c_lg) & 0xffffffff));
+      st(r + 0, (long long)9 << 32 | (long long)((c_rows - c_lg) & 0xffff) | (long long)min(L.misc[14], 0xffff) << 16);
       st(r + 1, r_lg);
       st(r + 2, r_row0);
       st(r + 3, r_rows);
       n_ev += 2;
+      if (n_ev < p.trace_cap) {                // kind 10: ends of the logits gather's first rounds
+        r += 4;
+        st(r + 0, (long long)10 << 32);
+        for (int i = 0; i < 3; ++i) st(r + 1 + i, i <= L.misc[14] ? ((SHARED long long*)(L.misc + 16))[i] : 0ll);
+        ++n_ev;
+      }
     }
     n_mr = L.misc[0];
     i_rgu_end = p.i_pre_end + n_mr * p.n_rb13;
@@ -1696,7 +1846,12 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
     if (it < p.i_router_end) {
       kind = 0;
       if (p.router_tiles) router_tile_item(p, L, it);
-      else router_item(p, L, it);
+      else {
+        // a small batch's router item reads all of x: it fills the LDS copy too
+        const bool stage = !x_staged && p.T <= kRouterRows;
+        t_ready = router_item(p, L, it, stage);
+        x_staged = x_staged || stage;
+      }
     } else if (it >= p.i_topk_end && it < p.i_pre_end) {
       kind = 1;
       ensure_x();
@@ -1706,9 +1861,8 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
       run_gu(p.E, p.T * p.K, r0, min(kMRange, p.T - r0), rb, true);
     } else if (it < p.i_topk_end) {
       kind = 2;
-      if (!wait_geq(p, go_flag(p.ctr + kCtrRouterGo), 1, L.misc + 1, 1 << 20)) break;
-      t_ready = tl_clock(p);
       if (!topk_item(p, L, it - p.i_router_end)) break;
+      t_ready = *(SHARED long long*)(L.misc + 12);
       publish_done(p.ctr + kCtrTopkDone, p.n_topk, p.ctr + kCtrTopkGo);
     } else {
       kind = 6;
@@ -1829,6 +1983,7 @@ struct moe_decode_handle {
   u32x4* w2p = nullptr;
   float* s2p = nullptr;
   uint64_t* lgt = nullptr;
+  size_t lgt_bytes = 0;   // tile path: [ks][T][E]; small batches: [copy][E][8 or 16]
   int* topk_idx = nullptr;
   float* topk_w = nullptr;
   uint64_t* h_scr = nullptr;
@@ -1870,12 +2025,18 @@ Params make_params(const moe_decode_handle* h, int T) {
   p.S = c.num_shared;
   p.I = c.intermediate;
   p.router_w = h->router_w;
-  p.router_b = h->router_b;
+  p.router_b = h->router_b ? h->router_b : h->router_w;
+  p.has_bias = h->router_b != nullptr;
   p.w13p = h->w13p;
   p.s13p = h->s13p;
   p.w2p = h->w2p;
   p.s2p = h->s2p;
   p.lgt = h->lgt;
+  p.lg_copies = kLgCopies;
+  p.lg_tp_log2 = T <= 8 ? 3 : 4;
+  p.fd_x8 = make_fdiv((uint32_t)(p.H / 8));
+  p.fd_h2 = make_fdiv((uint32_t)(p.I / 2));
+  for (int n = 1; n <= 4; ++n) p.fd_part[n - 1] = make_fdiv((uint32_t)(n * p.E));
   p.topk_idx = h->topk_idx;
   p.topk_w = h->topk_w;
   p.h_scr = h->h_scr;
@@ -1923,7 +2084,7 @@ Params make_params(const moe_decode_handle* h, int T) {
   p.lds_tki = take((size_t)T * K * 2);
   p.lds_prow = take((size_t)T * K * 4);
   p.lds_tkw = take((size_t)T * K * 4);
-  p.lds_misc = take(16 * 4);
+  p.lds_misc = take(32 * 4);
   p.lds_tks = take((size_t)kWaves * kWave * 4);
   // small batches (every expert then has at most 16 rows: one MFMA block) keep
   // x in LDS (rows padded by 16 bytes against bank conflicts) and stage each
@@ -2025,7 +2186,7 @@ moe_status moe_decode_create(const moe_decode_config* cfg, const moe_decode_weig
         {(void**)&h->s13p, slots * 2 * I * (H / 32) * 4},
         {(void**)&h->w2p, slots * H * I},
         {(void**)&h->s2p, slots * H * (I / 32) * 4},
-        {(void**)&h->lgt, Tm * E * 8 * kRouterKsMax},
+        {(void**)&h->lgt, h->lgt_bytes = std::max(Tm * E * kRouterKsMax, (size_t)kLgCopies * E * 16) * 8},
         {(void**)&h->topk_idx, Tm * K * 4},
         {(void**)&h->topk_w, Tm * K * 4},
         {(void**)&h->h_scr, scr_rows * (I / 2) * 8},
@@ -2039,7 +2200,7 @@ moe_status moe_decode_create(const moe_decode_config* cfg, const moe_decode_weig
     if (rc != MOE_OK) break;
     // counters and every tagged word start at zero (no run has epoch 0)
     if (hipMemset(h->ctr, 0, ctr_words * 4) != hipSuccess ||
-        hipMemset(h->lgt, 0, Tm * E * 8 * kRouterKsMax) != hipSuccess ||
+        hipMemset(h->lgt, 0, h->lgt_bytes) != hipSuccess ||
         hipMemset(h->h_scr, 0, scr_rows * (I / 2) * 8) != hipSuccess ||
         hipMemset(h->o_scr, 0, scr_rows * H * 8) != hipSuccess) { rc = MOE_ERR_HIP; break; }
     if (hipMemcpy(h->router_w, w->router_w, E * H * 4, hipMemcpyDeviceToDevice) != hipSuccess) { rc = MOE_ERR_HIP; break; }
@@ -2100,7 +2261,7 @@ moe_status moe_decode_run(moe_decode_handle* h, const void* x, int32_t T, void* 
   if (h->epoch + 1 == 0) {
     const moe_decode_config& c = h->cfg;
     const size_t rows = (size_t)c.max_tokens * (c.top_k + c.num_shared);
-    if (hipMemsetAsync(h->lgt, 0, (size_t)c.max_tokens * c.num_experts * 8 * kRouterKsMax, stream) != hipSuccess ||
+    if (hipMemsetAsync(h->lgt, 0, h->lgt_bytes, stream) != hipSuccess ||
         hipMemsetAsync(h->h_scr, 0, rows * (c.intermediate / 2) * 8, stream) != hipSuccess ||
         hipMemsetAsync(h->o_scr, 0, rows * c.hidden * 8, stream) != hipSuccess ||
         hipMemsetAsync(h->ctr, 0, 2 * (size_t)kCtrHead * 4, stream) != hipSuccess) {
