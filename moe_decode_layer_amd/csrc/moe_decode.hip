@@ -1021,6 +1021,28 @@ __device__ __forceinline__ float half_sum_v(float v) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
+// Keys of experts 8 hl .. 8 hl + 7 of row t (lane hl of a half): read as two
+// 16-byte LDS words when the row allows (E a multiple of 4), all reads issued
+// before any key is formed, absent experts (id >= E) keyed 0.
+__device__ __forceinline__ void load_keys8(KParams& p, const SHARED float* lg, int t, uint32_t hl, uint32_t (&uk)[8]) {
+  float v[8];
+  const int e0 = 8 * (int)hl;
+  if ((p.E & 3) == 0 && e0 + 8 <= p.E) {
+    const SHARED f32x4* q = (const SHARED f32x4*)(lg + t * p.E + e0);
+    const f32x4 a = q[0], b = q[1];
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  } else {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = lg[t * p.E + min(e0 + j, p.E - 1)];
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const uint32_t k = order_ukey(v[j]);
+    uk[j] = e0 + j < p.E ? k : 0u;
+  }
+}
+
 // Top-k of two rows in one wave, one per 32-lane half: lane l of half h
 // holds experts 8 (l % 32) .. 8 (l % 32) + 7 of row t[h] as order-preserving
 // keys.  Each of the K rounds takes the half's maximum key and, among its
@@ -1033,12 +1055,7 @@ __device__ __forceinline__ void topk_pair(KParams& p, const SHARED float* lg, in
   const int t = lane_id() < 32 ? tA : tB;
   const int K = p.K;
   uint32_t uk[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int e = 8 * hl + j;
-    const float v = lg[t * p.E + min(e, p.E - 1)];
-    uk[j] = e < p.E ? order_ukey(v) : 0u;
-  }
+  load_keys8(p, lg, t, hl, uk);
   uint32_t sel_k = 0, sel_e = 0;
   for (int k = 0; k < K; ++k) {
     uint32_t m = uk[0];
@@ -1060,8 +1077,8 @@ __device__ __forceinline__ void topk_pair(KParams& p, const SHARED float* lg, in
   *out_w = s / sum;
 }
 
-// Copy rows [t0, t0 + nt) of this run's router logits into LDS lg (row-major,
-// from row 0) once every one of them carries the current epoch.
+// This run's router logits (this workgroup's copy, [E][lg_tp] tagged words)
+// into LDS lg as [T][E], once every one of them carries the current epoch.
 __device__ __forceinline__ bool gather_logits(KParams& p, const Lds& L) {
   const int c = blockIdx.x % p.lg_copies;
   const int sh = p.lg_tp_log2, mask = (1 << sh) - 1;
@@ -1648,7 +1665,11 @@ __device__ __forceinline__ bool down_item_full(KParams& p, const Lds& L, int slo
 // ----------------------------------------------------------------------------
 // The persistent kernel
 // ----------------------------------------------------------------------------
-template <int NMBMAX, bool XL>
+// FULL: the variant for x in LDS with the full-tile gate/up and down items
+// (H = 64 kFullTiles, I = 32 kFullTiles) and local routing only; the other
+// variants hold the general code.  Each variant carries only the code its
+// batches reach, which keeps register pressure (and spills) down.
+template <int NMBMAX, bool XL, bool FULL>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(NMBMAX == 1 ? 2 : 1))) moe_decode_kernel(Params arg) {
   KParams& p = *(const CONSTANT Params*)__builtin_amdgcn_kernarg_segment_ptr();
   (void)arg;
@@ -1716,7 +1737,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
     const long long r_start = tl_clock(p);
     clear_placement(p, L);                     // the barriers of the waits below order it
     long long r_go = 0, r_lg = 0, r_row0 = 0, c_lg = 0;
-    if (p.local_topk) {
+    if (FULL || p.local_topk) {
       // all T x E logits into LDS: the router items' tagged words are
       // polled directly (no completion count), late ones round by round
       __syncthreads();                         // earlier readers of the lg area are done
@@ -1739,7 +1760,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
           L.tkw[t * p.K + hl] = wk;
         }
       }
-    } else {
+    } else if constexpr (!FULL) {
       if (!wait_geq(p, go_flag(p.ctr + kCtrTopkGo), 1, L.misc + 1, 1 << 20)) return false;
       for (int i = tid; i < p.T * p.K; i += kThreads) {
         L.tki[i] = (int16_t)ld_coh(p.topk_idx + i);
@@ -1786,7 +1807,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
   auto run_gu = [&](int slot, int sbase, int r0, int nrows, int rb, bool shared) __attribute__((always_inline)) {
     const int nmb = (nrows + kMBlock - 1) / kMBlock;
     const int par = gu_count++;
-    if (XL && p.n_q13 == 4 * kFullTiles) gu_item_full<kFullTiles>(p, L, slot, sbase, r0, nrows, rb, shared, par, pend_rg);
+    if constexpr (FULL) gu_item_full<kFullTiles>(p, L, slot, sbase, r0, nrows, rb, shared, par, pend_rg);
     else if (NMBMAX == 1 || nmb <= 1) gu_item<1, XL, NMBMAX>(p, L, slot, sbase, r0, nrows, rb, shared, par, pend_rg);
     else if (nmb == 2) gu_item<NMBMAX >= 2 ? 2 : 1, XL, NMBMAX>(p, L, slot, sbase, r0, nrows, rb, shared, par, pend_rg);
     else if (nmb == 3) gu_item<NMBMAX >= 3 ? 3 : 1, XL, NMBMAX>(p, L, slot, sbase, r0, nrows, rb, shared, par, pend_rg);
@@ -1796,8 +1817,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
   // expert's gate/up items have counted in ht publications
   auto run_down = [&](int slot, int sbase, int r0, int nrows, int rg, int ht) __attribute__((always_inline)) -> bool {
     const int nmb = (nrows + kMBlock - 1) / kMBlock;
-    if (XL && p.hs_stride > 0 && p.n_q2 == kFullTiles / 2)
-      return down_item_full<kFullTiles / 2>(p, L, slot, sbase, r0, nrows, rg, ht, pend_rg);
+    if constexpr (FULL) return down_item_full<kFullTiles / 2>(p, L, slot, sbase, r0, nrows, rg, ht, pend_rg);
     else if (XL && p.hs_stride > 0) return down_item<1, XL>(p, L, slot, sbase, r0, nrows, rg, ht, pend_rg);
     else if (NMBMAX == 1 || nmb <= 1) return down_item<1, false>(p, L, slot, sbase, r0, nrows, rg, ht, pend_rg);
     else if (nmb == 2) return down_item<NMBMAX >= 2 ? 2 : 1, false>(p, L, slot, sbase, r0, nrows, rg, ht, pend_rg);
@@ -1845,8 +1865,9 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
     t_got = t_ready = tl_clock(p);
     if (it < p.i_router_end) {
       kind = 0;
-      if (p.router_tiles) router_tile_item(p, L, it);
-      else {
+      if (!FULL && p.router_tiles) {
+        if constexpr (!FULL) router_tile_item(p, L, it);
+      } else {
         // a small batch's router item reads all of x: it fills the LDS copy too
         const bool stage = !x_staged && p.T <= kRouterRows;
         t_ready = router_item(p, L, it, stage);
@@ -1859,7 +1880,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
       const int mr = i / p.n_rb13, rb = i % p.n_rb13;
       const int r0 = mr * kMRange;
       run_gu(p.E, p.T * p.K, r0, min(kMRange, p.T - r0), rb, true);
-    } else if (it < p.i_topk_end) {
+    } else if (!FULL && it < p.i_topk_end) {
       kind = 2;
       if (!topk_item(p, L, it - p.i_router_end)) break;
       t_ready = *(SHARED long long*)(L.misc + 12);
@@ -1993,8 +2014,8 @@ struct moe_decode_handle {
   hipStream_t last_stream = nullptr;
   std::mutex mu;
   // occupancy cache, by (kernel variant, LDS bytes)
-  int occ_lds[3] = {-1, -1, -1};
-  int occ_blocks[3] = {0, 0, 0};
+  int occ_lds[4] = {-1, -1, -1, -1};
+  int occ_blocks[4] = {0, 0, 0, 0};
 };
 
 namespace {
@@ -2275,11 +2296,16 @@ moe_status moe_decode_run(moe_decode_handle* h, const void* x, int32_t T, void* 
   // counter block of this run (tag parity) and the one it clears for the next
   p.ctr = h->ctr + (size_t)(h->epoch & 1) * kCtrHead;
   p.ctr_next = h->ctr + (size_t)((h->epoch + 1) & 1) * kCtrHead;
-  // variants: 0 = x in LDS, 1 = up to 16 rows, 2 = more rows (4 MFMA blocks per item)
-  const int variant = p.xs_stride > 0 ? 0 : (T > kMBlock ? 2 : 1);
-  const void* fn = variant == 0 ? (const void*)moe_decode_kernel<1, true>
-                 : variant == 1 ? (const void*)moe_decode_kernel<1, false>
-                                : (const void*)moe_decode_kernel<4, false>;
+  // variants: 0 = x in LDS, 1 = up to 16 rows, 2 = more rows (4 MFMA blocks
+  // per item), 3 = x in LDS with full-tile items (H = 64 kFullTiles,
+  // I = 32 kFullTiles, h staged in LDS, local routing)
+  const bool full = p.xs_stride > 0 && p.hs_stride > 0 && p.n_q13 == 4 * kFullTiles &&
+                    p.n_q2 == kFullTiles / 2 && p.local_topk && !p.router_tiles;
+  const int variant = full ? 3 : p.xs_stride > 0 ? 0 : (T > kMBlock ? 2 : 1);
+  const void* fn = variant == 3   ? (const void*)moe_decode_kernel<1, true, true>
+                   : variant == 0 ? (const void*)moe_decode_kernel<1, true, false>
+                   : variant == 1 ? (const void*)moe_decode_kernel<1, false, false>
+                                  : (const void*)moe_decode_kernel<4, false, false>;
   if (h->occ_lds[variant] != p.lds_bytes) {
     int nb = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fn, kThreads, p.lds_bytes) != hipSuccess ||

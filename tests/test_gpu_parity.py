@@ -161,3 +161,61 @@ def test_expired_waits_report_timeout_and_the_next_run_recovers():
     out = device.run_once(layer, inp.x, wl.E, wl.K)
     check_against_oracle(wl, inp, out)
     layer.close()
+
+
+def _check_routing_in_kernel_precision(wl, inp, out):
+    """Routing decided in the precision the kernel decides it in: the oracle's
+    selection and placement applied to the kernel's own fp32 logits, which
+    are themselves checked against the oracle's."""
+    ref_l = O.router_logits(O.bf16_bits_to_f64(inp.x), inp.router_w, inp.router_b)
+    scale = max(np.abs(ref_l).max(), 1e-30)
+    assert np.abs(out["logits"] - ref_l).max() / scale <= 1e-4
+    idx, w = O.select_topk(O.sigmoid(out["logits"].astype(np.float64)), wl.K)
+    assert np.array_equal(out["topk_idx"], idx), "top-k indices differ"
+    assert np.abs(out["topk_w"] - w).max() <= 1e-5
+    plc = O.place(idx, wl.E)
+    assert np.array_equal(out["expert_count"], plc.count)
+    assert np.array_equal(out["pair_rank"], plc.rank)
+    check_placement(out["topk_idx"], out["pair_rank"], out["expert_count"], wl.E)
+
+
+def test_exactly_tied_router_rows_break_ties_by_expert_id():
+    """Experts 2j and 2j+1 get identical router rows (and biases), so every
+    row's logits come in exactly equal pairs: the filtered selection must
+    order each tied pair by expert id, as the round-by-round one does."""
+    wl = synth.WORKLOADS[1]
+    print(f"case tied router rows on {wl.name}", flush=True)
+    inp = inputs_for(wl)
+    rw = inp.router_w.copy()
+    rw[1::2] = rw[0::2]
+    rb = None if inp.router_b is None else inp.router_b.copy()
+    if rb is not None:
+        rb[1::2] = rb[0::2]
+    tied = synth.Inputs(wl, inp.x, rw, rb, inp.w13, inp.s13, inp.w2, inp.s2, inp.attempts)
+    layer = device.make_layer(tied)
+    out = device.run_once(layer, tied.x, wl.E, wl.K)
+    layer.close()
+    lg = out["logits"]
+    assert np.array_equal(lg[:, 0::2], lg[:, 1::2]), "tied experts got different logits"
+    _check_routing_in_kernel_precision(wl, tied, out)
+    # some row selects both members of a tied pair (else the case tests nothing)
+    sel = out["topk_idx"]
+    assert any(len(set(sel[t] // 2)) < wl.K for t in range(wl.T))
+
+
+def test_all_equal_logits_select_the_lowest_expert_ids():
+    """A zero router (and bias) makes all logits equal: every row selects
+    experts 0..K-1 in order with equal weights (the many-candidates path)."""
+    wl = synth.WORKLOADS[1]
+    print(f"case all-equal logits on {wl.name}", flush=True)
+    inp = inputs_for(wl)
+    zero = synth.Inputs(wl, inp.x, np.zeros_like(inp.router_w),
+                        None if inp.router_b is None else np.zeros_like(inp.router_b),
+                        inp.w13, inp.s13, inp.w2, inp.s2, inp.attempts)
+    layer = device.make_layer(zero)
+    out = device.run_once(layer, zero.x, wl.E, wl.K)
+    layer.close()
+    assert np.all(out["logits"] == 0.0)
+    assert np.array_equal(out["topk_idx"], np.tile(np.arange(wl.K, dtype=np.int32), (wl.T, 1)))
+    assert np.abs(out["topk_w"] - 1.0 / wl.K).max() <= 1e-6
+    _check_routing_in_kernel_precision(wl, zero, out)
