@@ -1205,34 +1205,36 @@ __device__ __forceinline__ bool combine_item(KParams& p, const Lds& L, int rc, i
     tt[j] = t0 + min(r, nt - 1);
     src[j] = p.o_scr + c0 + min(c, nc - 1);
   }
-  const uint64_t fresh = (uint64_t)p.epoch << 32;   // tag-only stand-in for a missing shared expert
-  uint64_t v[kOut][kIn];
+  // scratch row of every input: the K routed outputs, then the shared one
+  int row[kOut][kIn];
 #pragma unroll
   for (int j = 0; j < kOut; ++j)
 #pragma unroll
-    for (int k = 0; k < kIn; ++k) v[j][k] = 0;
+    for (int k = 0; k < kIn; ++k)
+      row[j][k] = k == kMaxTopK ? p.T * K + tt[j] : (k < K ? L.prow[tt[j] * K + k] : 0);
+  // A thread missing any of its inputs reads all of them again (no
+  // per-word branches; the conditions on k are uniform).
+  uint64_t v[kOut][kIn];
+  const uint64_t fresh = (uint64_t)p.epoch << 32;   // tag-only stand-in for a missing shared expert
+#pragma unroll
+  for (int j = 0; j < kOut; ++j)
+#pragma unroll
+    for (int k = 0; k < kIn; ++k) v[j][k] = fresh;
+  bool need = true;
   while (true) {
-    bool stale = false;
+    if (need) {
 #pragma unroll
-    for (int j = 0; j < kOut; ++j) {
+      for (int j = 0; j < kOut; ++j)
 #pragma unroll
-      for (int k = 0; k < kIn; ++k) {
-        if (k < K || k == kMaxTopK) {
-          if (!tag_ok(v[j][k], p.epoch)) {
-            if (k == kMaxTopK)
-              v[j][k] = p.S ? ld_tag(src[j] + (size_t)(p.T * K + tt[j]) * p.H) : fresh;
-            else
-              v[j][k] = ld_tag(src[j] + (size_t)L.prow[tt[j] * K + k] * p.H);
-          }
-        }
-      }
+        for (int k = 0; k < kIn; ++k)
+          if (k < K || (k == kMaxTopK && p.S)) v[j][k] = ld_tag(src[j] + (size_t)row[j][k] * p.H);
+      need = false;
+#pragma unroll
+      for (int j = 0; j < kOut; ++j)
+#pragma unroll
+        for (int k = 0; k < kIn; ++k) need |= live[j] && !tag_ok(v[j][k], p.epoch);
     }
-#pragma unroll
-    for (int j = 0; j < kOut; ++j)
-#pragma unroll
-      for (int k = 0; k < kIn; ++k)
-        if ((k < K || k == kMaxTopK) && live[j] && !tag_ok(v[j][k], p.epoch)) stale = true;
-    if (!block_any(stale, L.misc + 8)) break;
+    if (!block_any(need, L.misc + 8)) break;
     if (!poll_round(p, &t_end, &rounds, L.misc + 1)) return false;
   }
 #pragma unroll
