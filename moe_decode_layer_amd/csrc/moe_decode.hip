@@ -883,21 +883,20 @@ __device__ __forceinline__ long long router_item(KParams& p, const Lds& L, int i
     if (lane == 0) part[w * kRouterRows + j] = s;
   }
   __syncthreads();
-  float s = 0.f;
-  if (threadIdx.x < nt) {
-    const int j = threadIdx.x;
-    s = part[j];
+  // wave 0, lane 8 c + j: row j's logit, stored as copy c (every copy and row
+  // in one store instruction)
+  static_assert(kLgCopies * kRouterRows == kWave, "one lane per (copy, row)");
+  if (w == 0) {
+    const int j = lane % kRouterRows, c = lane / kRouterRows;
+    float s = part[j];
 #pragma unroll
     for (int ww = 1; ww < kWaves; ++ww) s += part[ww * kRouterRows + j];
     s += bias;
+    if (j < nt && c < p.lg_copies)
+      st_tag(p.lgt + (((size_t)c * p.E + e) << p.lg_tp_log2) + t0 + j, __float_as_uint(s), p.epoch);
+    if (j < nt && c == 0 && p.dbg_logits) st(p.dbg_logits + (size_t)(t0 + j) * p.E + e, s);
   }
   __syncthreads();                             // the partials area is free again
-  if (threadIdx.x < nt) {
-    const int j = threadIdx.x;
-    for (int c = 0; c < p.lg_copies; ++c)
-      st_tag(p.lgt + (((size_t)c * p.E + e) << p.lg_tp_log2) + t0 + j, __float_as_uint(s), p.epoch);
-    if (p.dbg_logits) st(p.dbg_logits + (size_t)(t0 + j) * p.E + e, s);
-  }
   return t_sums;
 }
 
