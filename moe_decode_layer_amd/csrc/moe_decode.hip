@@ -992,9 +992,9 @@ __device__ __forceinline__ void topk_rows(KParams& p, const SHARED float* lg, co
   }
 }
 
-// Maximum / minimum over each 32-lane half of the wave (lanes 0-31 and
-// 32-63 separately), returned in every lane of the half: DPP within each
-// 16-lane row, then the gfx950 16-lane swap between the rows of a half.
+// Maximum over each 32-lane half of the wave (lanes 0-31 and 32-63
+// separately), returned in every lane of the half: DPP within each 16-lane
+// row, then the gfx950 16-lane swap between the rows of a half.
 __device__ __forceinline__ uint32_t half_max_v(uint32_t v) {
   v = max(v, dpp<kDppXor1>(v));
   v = max(v, dpp<kDppXor2>(v));
@@ -1002,14 +1002,6 @@ __device__ __forceinline__ uint32_t half_max_v(uint32_t v) {
   v = max(v, dpp<kDppMirror>(v));
   const auto b = __builtin_amdgcn_permlane16_swap(v, v, false, false);
   return max(b[0], b[1]);
-}
-__device__ __forceinline__ uint32_t half_min_v(uint32_t v) {
-  v = min(v, dpp<kDppXor1>(v));
-  v = min(v, dpp<kDppXor2>(v));
-  v = min(v, dpp<kDppHalfMirror>(v));
-  v = min(v, dpp<kDppMirror>(v));
-  const auto b = __builtin_amdgcn_permlane16_swap(v, v, false, false);
-  return min(b[0], b[1]);
 }
 __device__ __forceinline__ float half_sum_v(float v) {
   v += dpp<kDppXor1>(v);
@@ -1044,31 +1036,51 @@ __device__ __forceinline__ void load_keys8(KParams& p, const SHARED float* lg, i
 
 // Top-k of two rows in one wave, one per 32-lane half: lane l of half h
 // holds experts 8 (l % 32) .. 8 (l % 32) + 7 of row t[h] as order-preserving
-// keys.  Each of the K rounds takes the half's maximum key and, among its
-// holders, the lowest expert id (lowest lane, then its lowest slot), then
-// retires it, so both rows share every reduction.  Returns, in lanes k < K
-// of each half, that half's row's k-th expert and weight.
+// keys, first sorted within the lane (keys descending; the sort is stable,
+// so equal keys keep ascending ids).  Each of the K rounds takes the half's
+// maximum head key; its lowest holder lane (lanes hold ascending id ranges)
+// gives the pick's id and pops its head, so both rows share every
+// reduction and the picks come out in (score desc, id asc) order.  Returns,
+// in lanes k < K of each half, that half's row's k-th expert and weight.
 __device__ __forceinline__ void topk_pair(KParams& p, const SHARED float* lg, int tA, int tB, int* out_e,
                                           float* out_w) {
   const uint32_t hl = lane_id() & 31;
-  const int t = lane_id() < 32 ? tA : tB;
+  const bool lo = lane_id() < 32;
+  const int t = lo ? tA : tB;
   const int K = p.K;
-  uint32_t uk[8];
+  uint32_t uk[8], ui[8];
   load_keys8(p, lg, t, hl, uk);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) ui[j] = 8 * hl + j;
+  // odd-even transposition sort: adjacent exchanges on strictly greater keys
+#pragma unroll
+  for (int r = 0; r < 8; ++r) {
+#pragma unroll
+    for (int j = r & 1; j + 1 < 8; j += 2) {
+      const bool sw = uk[j + 1] > uk[j];
+      const uint32_t k0 = sw ? uk[j + 1] : uk[j], k1 = sw ? uk[j] : uk[j + 1];
+      const uint32_t i0 = sw ? ui[j + 1] : ui[j], i1 = sw ? ui[j] : ui[j + 1];
+      uk[j] = k0;
+      uk[j + 1] = k1;
+      ui[j] = i0;
+      ui[j + 1] = i1;
+    }
+  }
   uint32_t sel_k = 0, sel_e = 0;
   for (int k = 0; k < K; ++k) {
-    uint32_t m = uk[0];
-#pragma unroll
-    for (int j = 1; j < 8; ++j) m = max(m, uk[j]);
-    const uint32_t M = half_max_v(m);
-    uint32_t fj = 7;
-#pragma unroll
-    for (int j = 6; j >= 0; --j) fj = uk[j] == M ? (uint32_t)j : fj;
-    const uint32_t W = half_min_v(m == M ? 8 * hl + fj : 0xffffu);
+    const uint32_t M = half_max_v(uk[0]);
+    const unsigned long long bal = __ballot(uk[0] == M);
+    const int wlo = __builtin_ctz((uint32_t)bal), whi = 32 + __builtin_ctz((uint32_t)(bal >> 32));
+    const uint32_t W = lo ? __builtin_amdgcn_readlane(ui[0], wlo) : __builtin_amdgcn_readlane(ui[0], whi);
     sel_k = hl == (uint32_t)k ? M : sel_k;
     sel_e = hl == (uint32_t)k ? W : sel_e;
+    const bool win = (int)lane_id() == (lo ? wlo : whi);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) uk[j] = 8 * hl + j == W ? 0u : uk[j];
+    for (int j = 0; j < 7; ++j) {
+      uk[j] = win ? uk[j + 1] : uk[j];
+      ui[j] = win ? ui[j + 1] : ui[j];
+    }
+    uk[7] = win ? 0u : uk[7];
   }
   const float s = (int)hl < K ? 1.0f / (1.0f + __expf(-ukey_value(sel_k))) : 0.f;
   const float sum = half_sum_v(s);
