@@ -1624,13 +1624,6 @@ __device__ __forceinline__ bool down_item_full(KParams& p, const Lds& L, int slo
   const int nh = nrows * per_row;
   const bool fast = nh <= kHFast * kThreads;
   const uint64_t* hsrc = p.h_scr + (size_t)(sbase + r0) * per_row;
-  uint64_t hv[kHFast];
-  if (fast) {
-    // only the batches that hold words are issued (the condition is uniform)
-#pragma unroll
-    for (int b = 0; b < kHFast; ++b)
-      hv[b] = b * kThreads < nh ? ld_tag(hsrc + min((int)threadIdx.x + b * kThreads, nh - 1)) : 0ull;
-  }
   u32x4 wv[2][NQ];
   f32x2 sv[2][NQ];
 #pragma unroll
@@ -1644,8 +1637,15 @@ __device__ __forceinline__ bool down_item_full(KParams& p, const Lds& L, int slo
       sv[j][q] = ld(sc + (size_t)q * kTileRows);
     }
   }
-  // (at least one h batch was issued before the weights: waiting for all but
-  // the last 4 NQ + 1 operations also covers the older stores)
+  uint64_t hv[kHFast];
+  if (fast) {
+    // only the batches that hold words are issued (the condition is uniform)
+#pragma unroll
+    for (int b = 0; b < kHFast; ++b)
+      hv[b] = b * kThreads < nh ? ld_tag(hsrc + min((int)threadIdx.x + b * kThreads, nh - 1)) : 0ull;
+  }
+  // the 4 NQ weight and scale loads, then at least one h batch: waiting for
+  // all but the last 4 NQ + 1 operations covers the older stores
   if (fast) flush_pending<4 * NQ + 1>(p, pend);
   else flush_pending<4 * NQ>(p, pend);
   // the previous item's readers of the h area are done past this barrier
