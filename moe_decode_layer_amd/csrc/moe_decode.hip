@@ -242,6 +242,12 @@ __device__ __forceinline__ T ld(const T* p) { return *(const GLOBAL T*)p; }
 __device__ __forceinline__ u32x4 ld_stream(const u32x4* p) {
   return __builtin_nontemporal_load((const GLOBAL u32x4*)p);
 }
+// Group scales are also read once: streamed like the weights (cached loads
+// of a once-read stream ran at less than half the bandwidth of streaming
+// ones in a read-only sweep on this GPU).
+__device__ __forceinline__ f32x2 ld_stream(const f32x2* p) {
+  return __builtin_nontemporal_load((const GLOBAL f32x2*)p);
+}
 template <typename T>
 __device__ __forceinline__ void st(T* p, T v) { *(GLOBAL T*)p = v; }
 
@@ -1341,7 +1347,7 @@ __device__ __forceinline__ void gu_item(KParams& p, const Lds& L, int slot, int 
       const int j = min(j0 + u, nj - 1);               // past the end: reload the last tile
       const int q = w + kWaves * j;
       S.w[u] = ld_stream(wt + (size_t)q * kWave);
-      S.s[u] = ld(sc + (size_t)q * kTileRows);
+      S.s[u] = ld_stream(sc + (size_t)q * kTileRows);
       if (!XL) {
 #pragma unroll
         for (int g = 0; g < 2; ++g)
@@ -1469,7 +1475,7 @@ __device__ __forceinline__ bool down_item(KParams& p, const Lds& L, int slot, in
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         S.w[u][j] = ld_stream(wt[j] + (size_t)q * kWave);
-        S.s[u][j] = ld(sc[j] + (size_t)q * kTileRows);
+        S.s[u][j] = ld_stream(sc[j] + (size_t)q * kTileRows);
       }
       if (!HL) {
 #pragma unroll
@@ -1570,7 +1576,7 @@ __device__ __forceinline__ void gu_item_full(KParams& p, const Lds& L, int slot,
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
     wv[j] = ld_stream(wt + (size_t)j * kWaves * kWave);
-    sv[j] = ld(sc + (size_t)j * kWaves * kTileRows);
+    sv[j] = ld_stream(sc + (size_t)j * kWaves * kTileRows);
   }
   flush_pending<2 * NJ>(p, pend);
   const bool aval = n < nrows;
@@ -1634,7 +1640,7 @@ __device__ __forceinline__ bool down_item_full(KParams& p, const Lds& L, int slo
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
       wv[j][q] = ld_stream(wt + (size_t)q * kWave);
-      sv[j][q] = ld(sc + (size_t)q * kTileRows);
+      sv[j][q] = ld_stream(sc + (size_t)q * kTileRows);
     }
   }
   uint64_t hv[kHFast];
