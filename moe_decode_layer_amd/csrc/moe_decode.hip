@@ -85,6 +85,12 @@ constexpr int kMaxTopK = 16;
 constexpr size_t kXsMaxBytes = 64 * 1024;   // x kept in LDS up to this size
 constexpr int kHsMaxI = 1024;               // h staged in LDS up to this intermediate width
 constexpr int kFullTiles = 16;              // tiles per wave of the fully unrolled items (H 4096, I 512)
+// Wide items (batches above 16 rows at H = 64 kWideTiles, I = 64 kWideQ2)
+constexpr int kWideTiles = 16;              // K tiles per wave of a wide gate/up item
+constexpr int kWideQ2 = 8;                  // K tiles of a down row block
+constexpr int kWideRb = 4;                  // gate/up row blocks per wide item (one per wave at the end)
+constexpr int kWideRows = 32;               // rows per wide expert item (two MFMA blocks)
+constexpr int kWideDnBlocks = 8;            // down row blocks per wave (128 output rows)
 
 constexpr int kCombineRows = 4;             // rows per combine item
 // Counter block (int32 words).  Every counter sits on a 256-byte line of its
@@ -182,7 +188,12 @@ struct Params {
   int n_rb2;           // down row blocks: H/16
   int n_q2;            // tiles along I: I/64
   int n_rg;            // down row groups: ceil(H/128)
-  int n_mr_sh;         // shared M-ranges: ceil(T/64) (0 without a shared expert)
+  int n_mr_sh;         // shared M-ranges: ceil(T/mrange) (0 without a shared expert)
+  int wide;            // 1: wide items (see gu_item_wide / dn_item_wide)
+  int mrange;          // rows per expert item: 64, wide 32
+  int n_gu_mr;         // gate/up items per M-range: n_rb13, wide n_rb13/4
+  int n_dn_mr;         // down items per M-range: n_rg, wide H/512
+  int h_rows_per_count;  // gate/up publications per row block come one per this many rows
   int nch;             // 64-row chunks: ceil(T/64)
   // item list boundaries
   int n_router, n_topk;
@@ -534,7 +545,7 @@ struct Lds {
   SHARED int* mrlist;             // [n_mr] expert of each routed M-range
   SHARED int16_t* rows;           // [T*K] scratch row -> token, grouped by expert
   SHARED int16_t* tki;            // [T][K] selected experts
-  SHARED int* prow;               // [T][K] scratch row of each pair (its expert output row)
+  SHARED int16_t* prow;           // [T][K] scratch row of each pair (its expert output row)
   SHARED float* tkw;              // [T][K] their weights
   SHARED float* red;              // partial sums of the 4 waves
   SHARED int* misc;               // [0] n_mr, [1] flag, [3..7) scan scratch, [8..12) block_any,
@@ -557,7 +568,7 @@ __device__ Lds lds_view(KParams& p, SHARED char* smem) {
   L.mrlist = (SHARED int*)(smem + p.lds_mrlist);
   L.rows = (SHARED int16_t*)(smem + p.lds_rows);
   L.tki = (SHARED int16_t*)(smem + p.lds_tki);
-  L.prow = (SHARED int*)(smem + p.lds_prow);
+  L.prow = (SHARED int16_t*)(smem + p.lds_prow);
   L.tkw = (SHARED float*)(smem + p.lds_tkw);
   L.red = (SHARED float*)(smem + p.lds_red);
   L.misc = (SHARED int*)(smem + p.lds_misc);
@@ -673,7 +684,7 @@ __device__ __forceinline__ bool gather_small(KParams& p, const Lds& L, int n, Lo
 // expert's bits below t.  Row r of expert e lives at scratch row base[e] + r.
 // The bitmaps must be zero on entry (clear_placement, earlier, with a
 // barrier in between).  One block scan yields both the rows and the 64-row
-// ranges before each expert (packed 16 + 16 bits: T K <= 4096).
+// ranges before each expert (packed 16 + 16 bits: T K <= 8192).
 __device__ __forceinline__ void clear_placement(KParams& p, const Lds& L) {
   for (int i = threadIdx.x; i < p.E * p.nch; i += kThreads) L.bm[i] = 0ull;
 }
@@ -693,7 +704,7 @@ __device__ __forceinline__ void build_placement(KParams& p, const Lds& L) {
       L.cp[tid * nch + ch] = c;
       c += __popcll(L.bm[tid * nch + ch]);
     }
-    nmr = (c + kMRange - 1) / kMRange;
+    nmr = (c + p.mrange - 1) / p.mrange;
   }
   int tot;
   const int packed = block_exclusive_scan(c | nmr << 16, L.misc + 3, &tot);
@@ -715,7 +726,7 @@ __device__ __forceinline__ void build_placement(KParams& p, const Lds& L) {
     const unsigned long long below = L.bm[e * nch + (t >> 6)] & ((1ull << (t & 63)) - 1ull);
     const int rank = L.cp[e * nch + (t >> 6)] + __popcll(below);
     L.rows[L.base[e] + rank] = (int16_t)t;
-    L.prow[i] = L.base[e] + rank;
+    L.prow[i] = (int16_t)(L.base[e] + rank);
   }
   __syncthreads();
 }
@@ -1211,6 +1222,7 @@ __device__ __forceinline__ u32x4 ld_h8(const uint64_t* w) {
 // counts itself in for its 128-column group (no wait for the stores).
 // ----------------------------------------------------------------------------
 __device__ __forceinline__ int down_waves_in_group(KParams& p, int rg) {
+  if (p.wide) return 1;                       // a wide down wave covers a whole group
   const int nc = min(kDownRows, p.H - rg * kDownRows);
   return min(kWaves, (nc + 2 * kTileRows - 1) / (2 * kTileRows));
 }
@@ -1713,14 +1725,240 @@ __device__ __forceinline__ bool down_item_full(KParams& p, const Lds& L, int slo
 }
 
 // ----------------------------------------------------------------------------
+// Wide items: batches above 16 rows at H = 64 kWideTiles and I = 64 kWideQ2,
+// up to kWideRows (two MFMA blocks) rows of one expert per item, two
+// workgroups per compute unit.
+//
+// Gate/up: kWideRb row blocks (4 x 16 weight rows, 256 KiB of FP8) of one
+// expert.  Wave w takes K tiles [16 w, 16 w + 16) of all four blocks, so every
+// activation value it loads (from global memory; the batch does not fit in
+// LDS) feeds four blocks' MFMAs; four K steps (16 weight tiles) are in flight
+// per wave.  The waves' partial sums meet in LDS and wave w finishes block
+// kWideRb rg + w, summing the four K quarters in wave order.
+// ----------------------------------------------------------------------------
+template <int NMB>
+__device__ __forceinline__ void gu_item_wide(KParams& p, const Lds& L, int slot, int sbase, int r0, int nrows,
+                                             int rg, bool shared, int& pend) {
+  constexpr int NJ = kWideTiles;               // K tiles per wave
+  constexpr int P = NMB == 1 ? 4 : 3;          // K steps in flight
+  const int w = wave_id(), lane = lane_id();
+  const int n = lane & 15, kq = lane >> 4;
+  const int nq = p.n_q13;
+  const int q0 = NJ * w;
+  const u32x4* wt[kWideRb];
+  const f32x2* sc[kWideRb];
+#pragma unroll
+  for (int r = 0; r < kWideRb; ++r) {
+    const size_t blk = (size_t)slot * p.n_rb13 + kWideRb * rg + r;
+    wt[r] = p.w13p + (blk * nq + q0) * kWave + lane;
+    sc[r] = (const f32x2*)p.s13p + (blk * nq + q0) * kTileRows + n;
+  }
+  // A operand rows: rows past nrows read row r0 and are zeroed before the MFMA
+  const uint16_t* arow[NMB];
+  bool aval[NMB];
+#pragma unroll
+  for (int mb = 0; mb < NMB; ++mb) {
+    const int r = mb * kMBlock + n;
+    aval[mb] = r < nrows;
+    const int rr = aval[mb] ? r : 0;
+    const int tok = shared ? (r0 + rr) : (int)L.rows[sbase + r0 + rr];
+    arow[mb] = p.x + (size_t)tok * p.H + kTileK * q0 + 8 * kq;
+  }
+  struct Step {
+    u32x4 a[2][NMB];
+    u32x4 w[kWideRb];
+    f32x2 s[kWideRb];
+  };
+  Step S[P];
+  auto load = [&](Step& st_, int j) __attribute__((always_inline)) {
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+      for (int mb = 0; mb < NMB; ++mb) st_.a[g][mb] = ld((const u32x4*)(arow[mb] + kTileK * j + kGroup * g));
+#pragma unroll
+    for (int r = 0; r < kWideRb; ++r) {
+      st_.w[r] = ld_stream(wt[r] + (size_t)j * kWave);
+      st_.s[r] = ld_stream(sc[r] + (size_t)j * kTileRows);
+    }
+  };
+#pragma unroll
+  for (int j = 0; j < P; ++j) load(S[j], j);
+  flush_pending<P * (2 * NMB + 2 * kWideRb)>(p, pend);
+  const u32x4 zero4 = {0u, 0u, 0u, 0u};
+  f32x4 acc[kWideRb][NMB];
+#pragma unroll
+  for (int r = 0; r < kWideRb; ++r)
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb) acc[r][mb] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  // step j lives in S[j % P]; the inner loop keeps that index a constant
+#pragma unroll
+  for (int j0 = 0; j0 < NJ; j0 += P) {
+#pragma unroll
+    for (int u = 0; u < P; ++u) {
+      const int j = j0 + u;
+      if (j < NJ) {
+        Step& st_ = S[u];
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+          bf16x8 a[NMB];
+#pragma unroll
+          for (int mb = 0; mb < NMB; ++mb) a[mb] = as_bf16x8(aval[mb] ? st_.a[g][mb] : zero4);
+#pragma unroll
+          for (int r = 0; r < kWideRb; ++r) {
+            const bf16x8 b = fp8x8_to_bf16(st_.w[r][2 * g], st_.w[r][2 * g + 1]);
+            const float s = g ? st_.s[r].y : st_.s[r].x;
+#pragma unroll
+            for (int mb = 0; mb < NMB; ++mb) acc[r][mb] += s * mfma16(a[mb], b);
+          }
+        }
+        if (j + P < NJ) load(st_, j + P);
+      }
+    }
+  }
+  // the first barrier also ends the previous item's reads of the area
+  __syncthreads();
+  SHARED f32x4* red = (SHARED f32x4*)L.red;    // [kWaves][kWideRb][NMB][64]
+#pragma unroll
+  for (int r = 0; r < kWideRb; ++r)
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb) red[((w * kWideRb + r) * NMB + mb) * kWave + lane] = acc[r][mb];
+  __syncthreads();
+  const int rb = kWideRb * rg + w;
+#pragma unroll
+  for (int mb = 0; mb < NMB; ++mb) {
+    if (mb * kMBlock < nrows) {
+      f32x4 s = red[((0 * kWideRb + w) * NMB + mb) * kWave + lane];
+#pragma unroll
+      for (int ww = 1; ww < kWaves; ++ww) s += red[((ww * kWideRb + w) * NMB + mb) * kWave + lane];
+      // column n < 8 is gate row 8 rb + n, column n + 8 the matching up row
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float g = s[i];
+        const float u = dpp<kDppRowRor8>(s[i]);
+        const uint32_t hb = f32_to_bf16(g / (1.0f + __expf(-g)) * u);
+        const uint32_t hb_next = dpp<kDppRowShl1>(hb);          // column n + 1
+        const int r = mb * kMBlock + 4 * kq + i;
+        if (n < 8 && (n & 1) == 0 && r < nrows)
+          st_tag(p.h_scr + (size_t)(sbase + r0 + r) * (p.I / 2) + (8 * rb + n) / 2, hb | (hb_next << 16), p.epoch);
+      }
+    }
+  }
+  // one publication per wave and item: an M-range counts n_rb13 in all
+  if (lane == 0) count_done(p.ctr + kCtrHReady + slot * kLine);
+}
+
+// ----------------------------------------------------------------------------
+// Wide down item: 512 output rows of one expert (wave w: the 128-row column
+// group 4 rg + w, kWideDnBlocks row blocks) for up to kWideRows rows.  The
+// wave's first 16 weight tiles are requested before the item waits for its
+// expert's gate/up items; then the item's h rows go to LDS and the wave runs
+// K tile by K tile, each h operand feeding its 8 row blocks, 16 tiles in
+// flight.
+// ----------------------------------------------------------------------------
+template <int NMB>
+__device__ __forceinline__ bool dn_item_wide(KParams& p, const Lds& L, int slot, int sbase, int r0, int nrows,
+                                             int rg, int h_target, int& pend) {
+  constexpr int NB = kWideDnBlocks;
+  constexpr int NQ = kWideQ2;
+  constexpr int NT = NB * NQ;
+  constexpr int P = NMB == 1 ? 16 : 8;         // tiles in flight
+  const int w = wave_id(), lane = lane_id();
+  const int n = lane & 15, kq = lane >> 4;
+  const int grp = rg * kWaves + w;             // this wave's 128-column group
+  const size_t blk0 = (size_t)slot * p.n_rb2 + (size_t)grp * NB;
+  const u32x4* wt = p.w2p + blk0 * NQ * kWave + lane;
+  const f32x2* sc = (const f32x2*)p.s2p + blk0 * NQ * kTileRows + n;
+  // tile t = NB q + b is K tile q of row block b
+  static_assert(P % NB == 0 && NT % P == 0, "tile ring");
+  u32x4 wv[P];
+  f32x2 sv[P];
+  // tile t into ring slot u = t mod P (u passed as a constant)
+  auto load = [&](int t, int u) __attribute__((always_inline)) {
+    const int q = t / NB, b = t % NB;
+    wv[u] = ld_stream(wt + (size_t)(b * NQ + q) * kWave);
+    sv[u] = ld_stream(sc + (size_t)(b * NQ + q) * kTileRows);
+  };
+#pragma unroll
+  for (int t = 0; t < P; ++t) load(t, t);
+  flush_pending<2 * P>(p, pend);
+  // the barriers of the wait also end the previous item's reads of the area
+  if (!wait_geq(p, p.ctr + kCtrHReady + slot * kLine, h_target, L.misc + 1)) return false;
+  if (!stage_h_rows(p, L, sbase + r0, nrows)) return false;
+  __syncthreads();
+  const u32x4 zero4 = {0u, 0u, 0u, 0u};
+  const SHARED uint16_t* arow[NMB];
+  bool aval[NMB];
+#pragma unroll
+  for (int mb = 0; mb < NMB; ++mb) {
+    const int r = mb * kMBlock + n;
+    aval[mb] = r < nrows;
+    arow[mb] = L.hs + (size_t)(aval[mb] ? r : 0) * p.hs_stride + 8 * kq;
+  }
+  f32x4 acc[NB][NMB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb) acc[b][mb] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int t0 = 0; t0 < NT; t0 += P) {
+#pragma unroll
+    for (int qq = 0; qq < P / NB; ++qq) {
+      const int q = t0 / NB + qq;
+      bf16x8 a[2][NMB];
+#pragma unroll
+      for (int g = 0; g < 2; ++g)
+#pragma unroll
+        for (int mb = 0; mb < NMB; ++mb)
+          a[g][mb] = as_bf16x8(aval[mb] ? *(const SHARED u32x4*)(arow[mb] + kTileK * q + kGroup * g) : zero4);
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const int u = qq * NB + b;             // ring slot of tile t0 + u
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+          const bf16x8 bw = fp8x8_to_bf16(wv[u][2 * g], wv[u][2 * g + 1]);
+          const float s = g ? sv[u].y : sv[u].x;
+#pragma unroll
+          for (int mb = 0; mb < NMB; ++mb) acc[b][mb] += s * mfma16(a[g][mb], bw);
+        }
+        // pin the sums here, in tile order (else the compiler runs every MFMA
+        // first and keeps all their results for the multiply-adds at the end)
+#pragma unroll
+        for (int mb = 0; mb < NMB; ++mb) asm volatile("" : "+v"(acc[b][mb]));
+        if (t0 + u + P < NT) load(t0 + u + P, u);
+      }
+    }
+  }
+  // the sums are final here: without this the compiler sinks each element's
+  // whole multiply-add chain into its conditional store below, which keeps
+  // every MFMA result alive to the end of the item
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb) asm volatile("" : "+v"(acc[b][mb]));
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = mb * kMBlock + 4 * kq + i;
+        if (r < nrows)
+          st_tag(p.o_scr + (size_t)(sbase + r0 + r) * p.H + (grp * NB + b) * kTileRows + n,
+                 __float_as_uint(acc[b][mb][i]), p.epoch);
+      }
+  pend = grp;
+  return true;
+}
+
+// ----------------------------------------------------------------------------
 // The persistent kernel
 // ----------------------------------------------------------------------------
 // FULL: the variant for x in LDS with the full-tile gate/up and down items
 // (H = 64 kFullTiles, I = 32 kFullTiles) and local routing only; the other
 // variants hold the general code.  Each variant carries only the code its
 // batches reach, which keeps register pressure (and spills) down.
-template <int NMBMAX, bool XL, bool FULL>
-__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(NMBMAX == 1 ? 2 : 1))) moe_decode_kernel(Params arg) {
+template <int NMBMAX, bool XL, bool FULL, bool WIDE>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(NMBMAX == 1 || WIDE ? 2 : 1))) moe_decode_kernel(Params arg) {
   KParams& p = *(const CONSTANT Params*)__builtin_amdgcn_kernarg_segment_ptr();
   (void)arg;
   extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -1785,6 +2023,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
   auto ensure_routing = [&]() __attribute__((always_inline)) -> bool {
     if (routed) return true;
     const long long r_start = tl_clock(p);
+    if constexpr (WIDE) __syncthreads();       // the bitmaps share an area with earlier items' partial sums
     clear_placement(p, L);                     // the barriers of the waits below order it
     long long r_go = 0, r_lg = 0, r_row0 = 0, c_lg = 0;
     uint32_t touch = 0;
@@ -1847,9 +2086,9 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
       }
     }
     n_mr = L.misc[0];
-    i_rgu_end = p.i_pre_end + n_mr * p.n_rb13;
+    i_rgu_end = p.i_pre_end + n_mr * p.n_gu_mr;
     i_sdn_end = i_rgu_end + p.n_sdn;
-    i_rdn_end = i_sdn_end + n_mr * p.n_rg;
+    i_rdn_end = i_sdn_end + n_mr * p.n_dn_mr;
     i_total = i_rdn_end + p.n_cmb;
     routed = true;
     return true;
@@ -1860,7 +2099,10 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
   auto run_gu = [&](int slot, int sbase, int r0, int nrows, int rb, bool shared) __attribute__((always_inline)) {
     const int nmb = (nrows + kMBlock - 1) / kMBlock;
     const int par = gu_count++;
-    if constexpr (FULL) gu_item_full<kFullTiles>(p, L, slot, sbase, r0, nrows, rb, shared, par, pend_rg);
+    if constexpr (WIDE) {
+      if (nmb <= 1) gu_item_wide<1>(p, L, slot, sbase, r0, nrows, rb, shared, pend_rg);
+      else gu_item_wide<2>(p, L, slot, sbase, r0, nrows, rb, shared, pend_rg);
+    } else if constexpr (FULL) gu_item_full<kFullTiles>(p, L, slot, sbase, r0, nrows, rb, shared, par, pend_rg);
     else if (NMBMAX == 1 || nmb <= 1) gu_item<1, XL, NMBMAX>(p, L, slot, sbase, r0, nrows, rb, shared, par, pend_rg);
     else if (nmb == 2) gu_item<NMBMAX >= 2 ? 2 : 1, XL, NMBMAX>(p, L, slot, sbase, r0, nrows, rb, shared, par, pend_rg);
     else if (nmb == 3) gu_item<NMBMAX >= 3 ? 3 : 1, XL, NMBMAX>(p, L, slot, sbase, r0, nrows, rb, shared, par, pend_rg);
@@ -1870,17 +2112,20 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
   // expert's gate/up items have counted in ht publications
   auto run_down = [&](int slot, int sbase, int r0, int nrows, int rg, int ht) __attribute__((always_inline)) -> bool {
     const int nmb = (nrows + kMBlock - 1) / kMBlock;
-    if constexpr (FULL) return down_item_full<kFullTiles / 2>(p, L, slot, sbase, r0, nrows, rg, ht, pend_rg);
+    if constexpr (WIDE) {
+      if (nmb <= 1) return dn_item_wide<1>(p, L, slot, sbase, r0, nrows, rg, ht, pend_rg);
+      return dn_item_wide<2>(p, L, slot, sbase, r0, nrows, rg, ht, pend_rg);
+    } else if constexpr (FULL) return down_item_full<kFullTiles / 2>(p, L, slot, sbase, r0, nrows, rg, ht, pend_rg);
     else if (XL && p.hs_stride > 0) return down_item<1, XL>(p, L, slot, sbase, r0, nrows, rg, ht, pend_rg);
     else if (NMBMAX == 1 || nmb <= 1) return down_item<1, false>(p, L, slot, sbase, r0, nrows, rg, ht, pend_rg);
     else if (nmb == 2) return down_item<NMBMAX >= 2 ? 2 : 1, false>(p, L, slot, sbase, r0, nrows, rg, ht, pend_rg);
     else if (nmb == 3) return down_item<NMBMAX >= 3 ? 3 : 1, false>(p, L, slot, sbase, r0, nrows, rg, ht, pend_rg);
     else return down_item<NMBMAX >= 4 ? 4 : 1, false>(p, L, slot, sbase, r0, nrows, rg, ht, pend_rg);
   };
-  // gate/up publications an expert's down items wait for: one per 16-row
-  // MFMA block per gate/up row block
+  // gate/up publications an expert's down items wait for: per gate/up row
+  // block, one per 16-row MFMA block (wide items: one per 32-row M-range)
   auto h_target = [&](int rows) __attribute__((always_inline)) {
-    return p.n_rb13 * ((rows + kMBlock - 1) / kMBlock);
+    return p.n_rb13 * ((rows + p.h_rows_per_count - 1) / p.h_rows_per_count);
   };
 
   // Schedule.  Items [0, S) are static: workgroup g takes g, g + G, ... in
@@ -1930,9 +2175,9 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
       kind = 1;
       ensure_x();
       const int i = it - p.i_topk_end;
-      const int mr = i / p.n_rb13, rb = i % p.n_rb13;
-      const int r0 = mr * kMRange;
-      run_gu(p.E, p.T * p.K, r0, min(kMRange, p.T - r0), rb, true);
+      const int mr = i / p.n_gu_mr, rb = i % p.n_gu_mr;
+      const int r0 = mr * p.mrange;
+      run_gu(p.E, p.T * p.K, r0, min(p.mrange, p.T - r0), rb, true);
     } else if (!FULL && it < p.i_topk_end) {
       kind = 2;
       if (!topk_item(p, L, it - p.i_router_end)) break;
@@ -1947,24 +2192,24 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
       if (it < i_rgu_end) {
         kind = 4;
         const int i = it - p.i_pre_end;
-        const int m = i / p.n_rb13, rb = i % p.n_rb13;
+        const int m = i / p.n_gu_mr, rb = i % p.n_gu_mr;
         const int e = L.mrlist[m];
-        const int r0 = (m - L.nmrb[e]) * kMRange;
-        run_gu(e, L.base[e], r0, min(kMRange, L.cnt[e] - r0), rb, false);
+        const int r0 = (m - L.nmrb[e]) * p.mrange;
+        run_gu(e, L.base[e], r0, min(p.mrange, L.cnt[e] - r0), rb, false);
       } else if (it < i_sdn_end) {
         kind = 3;
         const int i = it - i_rgu_end;
-        const int mr = i / p.n_rg, rg = i % p.n_rg;
-        const int r0 = mr * kMRange;
-        if (!run_down(p.E, p.T * p.K, r0, min(kMRange, p.T - r0), rg, h_target(p.T))) break;
+        const int mr = i / p.n_dn_mr, rg = i % p.n_dn_mr;
+        const int r0 = mr * p.mrange;
+        if (!run_down(p.E, p.T * p.K, r0, min(p.mrange, p.T - r0), rg, h_target(p.T))) break;
         t_ready = *(SHARED long long*)(L.misc + 12);
       } else if (it < i_rdn_end) {
         kind = 5;
         const int i = it - i_sdn_end;
-        const int m = i / p.n_rg, rg = i % p.n_rg;
+        const int m = i / p.n_dn_mr, rg = i % p.n_dn_mr;
         const int e = L.mrlist[m];
-        const int r0 = (m - L.nmrb[e]) * kMRange;
-        if (!run_down(e, L.base[e], r0, min(kMRange, L.cnt[e] - r0), rg, h_target(L.cnt[e]))) break;
+        const int r0 = (m - L.nmrb[e]) * p.mrange;
+        if (!run_down(e, L.base[e], r0, min(p.mrange, L.cnt[e] - r0), rg, h_target(L.cnt[e]))) break;
         t_ready = *(SHARED long long*)(L.misc + 12);
       } else {
         kind = 7;
@@ -2067,8 +2312,8 @@ struct moe_decode_handle {
   hipStream_t last_stream = nullptr;
   std::mutex mu;
   // occupancy cache, by (kernel variant, LDS bytes)
-  int occ_lds[4] = {-1, -1, -1, -1};
-  int occ_blocks[4] = {0, 0, 0, 0};
+  int occ_lds[5] = {-1, -1, -1, -1, -1};
+  int occ_blocks[5] = {0, 0, 0, 0, 0};
 };
 
 namespace {
@@ -2126,7 +2371,12 @@ Params make_params(const moe_decode_handle* h, int T) {
   p.n_q2 = p.I / kTileK;
   p.n_rg = (p.H + kDownRows - 1) / kDownRows;
   p.nch = (T + 63) / 64;
-  p.n_mr_sh = p.S ? (T + kMRange - 1) / kMRange : 0;
+  p.wide = T > kMBlock && p.n_q13 == kWaves * kWideTiles && p.n_q2 == kWideQ2;
+  p.mrange = p.wide ? kWideRows : kMRange;
+  p.n_gu_mr = p.wide ? p.n_rb13 / kWideRb : p.n_rb13;
+  p.n_dn_mr = p.wide ? p.H / (kWaves * kWideDnBlocks * kTileRows) : p.n_rg;
+  p.h_rows_per_count = p.wide ? kWideRows : kMBlock;
+  p.n_mr_sh = p.S ? (T + p.mrange - 1) / p.mrange : 0;
   {
     const int n_tiles = ((T + kRouterTile - 1) / kRouterTile) * ((p.E + kRouterTile - 1) / kRouterTile);
     // split H so that the tiles fill about one item per CU; each wave's share
@@ -2139,42 +2389,62 @@ Params make_params(const moe_decode_handle* h, int T) {
   p.n_topk = p.local_topk ? 0 : (T + kWaves - 1) / kWaves;
   p.i_router_end = p.n_router;
   p.i_topk_end = p.i_router_end + p.n_topk;
-  p.i_pre_end = p.i_topk_end + p.n_mr_sh * p.n_rb13;
-  p.n_sdn = p.n_mr_sh * p.n_rg;
+  p.i_pre_end = p.i_topk_end + p.n_mr_sh * p.n_gu_mr;
+  p.n_sdn = p.n_mr_sh * p.n_dn_mr;
   p.n_cmb = (T + kCombineRows - 1) / kCombineRows * p.n_rg;
   // LDS layout
   const int E = p.E, K = p.K;
-  const int max_mr = E + (T * K + kMRange - 1) / kMRange;
+  const int max_mr = E + (T * K + p.mrange - 1) / p.mrange;
   const int nmb = T > kMBlock ? 4 : 1;
   size_t off = 0;
   auto take = [&](size_t bytes) __attribute__((always_inline)) { size_t o = off; off = align_up(off + bytes, 16); return (int)o; };
-  p.lds_bm = take((size_t)E * p.nch * 8);
-  p.lds_cp = take((size_t)E * p.nch * 4);
+  if (p.wide) {
+    // one area used in turn by the placement bitmaps, the partial sums of
+    // router tiles and gate/up items, the top-k items' logits and a down
+    // item's h rows (each user is separated from the previous one by a
+    // barrier); with it two workgroups fit on a compute unit
+    p.hs_stride = p.I + 8;
+    const size_t bm_bytes = align_up((size_t)E * p.nch * 8, 16);
+    const size_t u = std::max({bm_bytes + (size_t)E * p.nch * 4,
+                               (size_t)kWaves * kWideRb * 2 * kWave * 16,
+                               (size_t)kWideRows * p.hs_stride * 2,
+                               (size_t)kWaves * p.router_ks * E * 4,
+                               (size_t)kWaves * kWave * 16});
+    const int ua = take(u);
+    p.lds_bm = ua;
+    p.lds_cp = ua + (int)bm_bytes;
+    p.lds_red = p.lds_hs = p.lds_lg = ua;
+  } else {
+    p.lds_bm = take((size_t)E * p.nch * 8);
+    p.lds_cp = take((size_t)E * p.nch * 4);
+  }
   p.lds_cnt = take((size_t)E * 4);
   p.lds_base = take((size_t)E * 4);
   p.lds_nmrb = take((size_t)(E + 1) * 4);
   p.lds_mrlist = take((size_t)max_mr * 4);
   p.lds_rows = take((size_t)T * K * 2);
   p.lds_tki = take((size_t)T * K * 2);
-  p.lds_prow = take((size_t)T * K * 4);
+  p.lds_prow = take((size_t)T * K * 2);
   p.lds_tkw = take((size_t)T * K * 4);
   p.lds_misc = take(32 * 4);
   p.lds_tks = take((size_t)kWaves * kWave * 4);
-  // small batches (every expert then has at most 16 rows: one MFMA block) keep
-  // x in LDS (rows padded by 16 bytes against bank conflicts) and stage each
-  // down item's h rows there as well
-  const size_t xs_stride = (size_t)p.H + 8;
-  if (T <= kMBlock && (size_t)T * xs_stride * 2 <= kXsMaxBytes) {
-    p.xs_stride = (int)xs_stride;
-    p.lds_xs = take((size_t)T * xs_stride * 2);
-    if (p.I <= kHsMaxI) p.hs_stride = p.I + 8;
+  if (!p.wide) {
+    // small batches (every expert then has at most 16 rows: one MFMA block) keep
+    // x in LDS (rows padded by 16 bytes against bank conflicts) and stage each
+    // down item's h rows there as well
+    const size_t xs_stride = (size_t)p.H + 8;
+    if (T <= kMBlock && (size_t)T * xs_stride * 2 <= kXsMaxBytes) {
+      p.xs_stride = (int)xs_stride;
+      p.lds_xs = take((size_t)T * xs_stride * 2);
+      if (p.I <= kHsMaxI) p.hs_stride = p.I + 8;
+    }
+    // partial sums of the router and of gate/up items (two alternating halves)
+    p.lds_red = take((size_t)2 * kWaves * nmb * kWave * 16);
+    // one region used in turn by the routing logits and a down item's h rows
+    const size_t hs_bytes = p.hs_stride ? (size_t)std::min(T, kMBlock) * p.hs_stride * 2 : 0;
+    const size_t lg_bytes = (size_t)(p.local_topk ? T : kWaves * p.router_ks) * E * 4;
+    p.lds_hs = p.lds_lg = take(std::max(hs_bytes, lg_bytes));
   }
-  // partial sums of the router and of gate/up items (two alternating halves)
-  p.lds_red = take((size_t)2 * kWaves * nmb * kWave * 16);
-  // one region used in turn by the routing logits and a down item's h rows
-  const size_t hs_bytes = p.hs_stride ? (size_t)std::min(T, kMBlock) * p.hs_stride * 2 : 0;
-  const size_t lg_bytes = (size_t)(p.local_topk ? T : kWaves * p.router_ks) * E * 4;
-  p.lds_hs = p.lds_lg = take(std::max(hs_bytes, lg_bytes));
   p.lds_bytes = (int)off;
   return p;
 }
@@ -2351,14 +2621,16 @@ moe_status moe_decode_run(moe_decode_handle* h, const void* x, int32_t T, void* 
   p.ctr_next = h->ctr + (size_t)((h->epoch + 1) & 1) * kCtrHead;
   // variants: 0 = x in LDS, 1 = up to 16 rows, 2 = more rows (4 MFMA blocks
   // per item), 3 = x in LDS with full-tile items (H = 64 kFullTiles,
-  // I = 32 kFullTiles, h staged in LDS, local routing)
+  // I = 32 kFullTiles, h staged in LDS, local routing), 4 = more than 16 rows
+  // with wide items (H = 64 kWideTiles, I = 64 kWideQ2)
   const bool full = p.xs_stride > 0 && p.hs_stride > 0 && p.n_q13 == 4 * kFullTiles &&
                     p.n_q2 == kFullTiles / 2 && p.local_topk && !p.router_tiles;
-  const int variant = full ? 3 : p.xs_stride > 0 ? 0 : (T > kMBlock ? 2 : 1);
-  const void* fn = variant == 3   ? (const void*)moe_decode_kernel<1, true, true>
-                   : variant == 0 ? (const void*)moe_decode_kernel<1, true, false>
-                   : variant == 1 ? (const void*)moe_decode_kernel<1, false, false>
-                                  : (const void*)moe_decode_kernel<4, false, false>;
+  const int variant = p.wide ? 4 : full ? 3 : p.xs_stride > 0 ? 0 : (T > kMBlock ? 2 : 1);
+  const void* fn = variant == 4   ? (const void*)moe_decode_kernel<2, false, false, true>
+                   : variant == 3 ? (const void*)moe_decode_kernel<1, true, true, false>
+                   : variant == 0 ? (const void*)moe_decode_kernel<1, true, false, false>
+                   : variant == 1 ? (const void*)moe_decode_kernel<1, false, false, false>
+                                  : (const void*)moe_decode_kernel<4, false, false, false>;
   if (h->occ_lds[variant] != p.lds_bytes) {
     int nb = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fn, kThreads, p.lds_bytes) != hipSuccess ||
