@@ -102,6 +102,25 @@ def test_ragged_T_on_one_handle():
     layer.close()
 
 
+def test_ragged_T_on_one_wide_handle():
+    """Batches above 16 rows take the wide items (32-row expert ranges, 4-block
+    gate/up and 512-row down items): the smallest such batch, ragged expert
+    ranges and the full 384 rows, on one handle."""
+    wl = synth.WORKLOADS[4]
+    inp = inputs_for(wl)
+    layer = device.make_layer(inp, max_tokens=wl.T)
+    for T in (17, 45, 200, wl.T):
+        print(f"case wide T={T} on {wl.name}", flush=True)
+        sub = synth.Inputs(wl.with_rows(T), inp.x[:T], inp.router_w, inp.router_b, inp.w13,
+                           inp.s13, inp.w2, inp.s2, inp.attempts[:T])
+        out = device.run_once(layer, sub.x, wl.E, wl.K)
+        rows = None
+        if T > 64:
+            rows = np.sort(np.random.default_rng(T).choice(T, 32, replace=False))
+        check_against_oracle(sub.workload, sub, out, rows)
+    layer.close()
+
+
 def test_zero_rows_is_a_noop():
     wl = synth.WORKLOADS[0]
     inp = inputs_for(wl)
