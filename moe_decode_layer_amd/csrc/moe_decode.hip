@@ -1811,6 +1811,13 @@ __device__ __forceinline__ void gu_item_wide(KParams& p, const Lds& L, int slot,
             for (int mb = 0; mb < NMB; ++mb) acc[r][mb] += s * mfma16(a[mb], b);
           }
         }
+        // pin the sums here, step by step, so the step's registers are free
+        // for its reload (else the compiler reorders the ring and waits on
+        // loads it has only just issued)
+#pragma unroll
+        for (int r = 0; r < kWideRb; ++r)
+#pragma unroll
+          for (int mb = 0; mb < NMB; ++mb) asm volatile("" : "+v"(acc[r][mb]));
         if (j + P < NJ) load(st_, j + P);
       }
     }
