@@ -2203,26 +2203,50 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
         const int e = L.mrlist[m];
         const int r0 = (m - L.nmrb[e]) * p.mrange;
         run_gu(e, L.base[e], r0, min(p.mrange, L.cnt[e] - r0), rb, false);
-      } else if (it < i_sdn_end) {
-        kind = 3;
-        const int i = it - i_rgu_end;
-        const int mr = i / p.n_dn_mr, rg = i % p.n_dn_mr;
-        const int r0 = mr * p.mrange;
-        if (!run_down(p.E, p.T * p.K, r0, min(p.mrange, p.T - r0), rg, h_target(p.T))) break;
-        t_ready = *(SHARED long long*)(L.misc + 12);
       } else if (it < i_rdn_end) {
-        kind = 5;
-        const int i = it - i_sdn_end;
-        const int m = i / p.n_dn_mr, rg = i % p.n_dn_mr;
-        const int e = L.mrlist[m];
-        const int r0 = (m - L.nmrb[e]) * p.mrange;
-        if (!run_down(e, L.base[e], r0, min(p.mrange, L.cnt[e] - r0), rg, h_target(L.cnt[e]))) break;
+        // down items.  Wide items go column group by column group (all
+        // M-ranges of a 512-row group, shared first), so a group's combine
+        // items find it complete while later groups still stream; otherwise
+        // the shared M-ranges come first, then the routed ones, each
+        // M-range's groups together.
+        const int i = it - i_rgu_end;
+        int mm, rg;
+        if (p.wide) {
+          const int nm = p.n_mr_sh + n_mr;
+          rg = i / nm;
+          mm = i - rg * nm;
+        } else {
+          const int j = i < p.n_sdn ? i : i - p.n_sdn;
+          mm = j / p.n_dn_mr + (i < p.n_sdn ? 0 : p.n_mr_sh);
+          rg = j % p.n_dn_mr;
+        }
+        int slot, sbase, r0, rows;
+        if (mm < p.n_mr_sh) {
+          kind = 3;
+          slot = p.E;
+          sbase = p.T * p.K;
+          r0 = mm * p.mrange;
+          rows = p.T;
+        } else {
+          kind = 5;
+          const int m = mm - p.n_mr_sh;
+          const int e = L.mrlist[m];
+          slot = e;
+          sbase = L.base[e];
+          r0 = (m - L.nmrb[e]) * p.mrange;
+          rows = L.cnt[e];
+        }
+        if (!run_down(slot, sbase, r0, min(p.mrange, rows - r0), rg, h_target(rows))) break;
         t_ready = *(SHARED long long*)(L.misc + 12);
       } else {
         kind = 7;
         flush_pending_now(p, pend_rg);
+        // combine items: by column group for wide items (the order their
+        // down items complete in), else by row group
         const int c = it - i_rdn_end;
-        if (!combine_item(p, L, c / p.n_rg, c % p.n_rg, n_mr)) break;
+        const int n_rc = (p.T + kCombineRows - 1) / kCombineRows;
+        const int rc = p.wide ? c % n_rc : c / p.n_rg, rg = p.wide ? c / n_rc : c % p.n_rg;
+        if (!combine_item(p, L, rc, rg, n_mr)) break;
         t_ready = *(SHARED long long*)(L.misc + 12);
       }
     }
@@ -2386,10 +2410,11 @@ Params make_params(const moe_decode_handle* h, int T) {
   p.n_mr_sh = p.S ? (T + p.mrange - 1) / p.mrange : 0;
   {
     const int n_tiles = ((T + kRouterTile - 1) / kRouterTile) * ((p.E + kRouterTile - 1) / kRouterTile);
-    // split H so that the tiles fill about one item per CU; each wave's share
-    // of H must stay a multiple of 16
+    // split H until the tiles make up to about two items per workgroup (the
+    // top-k items then add ks partial logits); each wave's share of H must
+    // stay a multiple of 16
     int ks = 1;
-    while (2 * ks <= kRouterKsMax && n_tiles * 2 * ks <= 256 && (p.H / kTileK) % (2 * ks) == 0) ks *= 2;
+    while (2 * ks <= kRouterKsMax && n_tiles * 2 * ks <= 1024 && (p.H / kTileK) % (2 * ks) == 0) ks *= 2;
     p.router_ks = p.router_tiles ? ks : 1;
     p.n_router = p.router_tiles ? n_tiles * p.router_ks : p.E * ((T + kRouterRows - 1) / kRouterRows);
   }
