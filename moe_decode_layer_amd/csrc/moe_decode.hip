@@ -182,6 +182,7 @@ struct Params {
   int lg_copies, lg_tp_log2;
   FDiv fd_x8;          // H / 8: 16-byte words of an x row
   FDiv fd_h2;          // I / 2: tagged words of an h row
+  FDiv fd_k;           // K: the row of a (row, k) pair index
   FDiv fd_part[4];     // n E for n = 1..4: logits of a distributed top-k item's rows
   int n_rb13;          // gate/up row blocks per expert: I/8
   int n_q13;           // tiles along H: H/64
@@ -690,12 +691,23 @@ __device__ __forceinline__ void clear_placement(KParams& p, const Lds& L) {
 }
 __device__ __forceinline__ void build_placement(KParams& p, const Lds& L) {
   const int tid = threadIdx.x;
-  const int E = p.E, K = p.K, T = p.T, nch = p.nch;
-  for (int i = tid; i < T * K; i += kThreads) {
-    const int t = i / K;
-    const int e = L.tki[i];
-    __hip_atomic_fetch_or(&L.bm[e * nch + (t >> 6)], 1ull << (t & 63), __ATOMIC_RELAXED,
-                          __HIP_MEMORY_SCOPE_WORKGROUP);
+  const int E = p.E, T = p.T, nch = p.nch, n = p.T * p.K;
+  // the pair loops take kPairBatch pairs per thread at a time, so their LDS
+  // round trips overlap
+  constexpr int kPairBatch = 4;
+  for (int i0 = tid; i0 < n; i0 += kPairBatch * kThreads) {
+    int e[kPairBatch], t[kPairBatch];
+#pragma unroll
+    for (int u = 0; u < kPairBatch; ++u) {
+      const int i = min(i0 + u * kThreads, n - 1);
+      e[u] = L.tki[i];
+      t[u] = (int)fdiv((uint32_t)i, p.fd_k.m, p.fd_k.s);
+    }
+#pragma unroll
+    for (int u = 0; u < kPairBatch; ++u)
+      if (i0 + u * kThreads < n)
+        __hip_atomic_fetch_or(&L.bm[e[u] * nch + (t[u] >> 6)], 1ull << (t[u] & 63), __ATOMIC_RELAXED,
+                              __HIP_MEMORY_SCOPE_WORKGROUP);
   }
   __syncthreads();
   int c = 0, nmr = 0;
@@ -720,13 +732,27 @@ __device__ __forceinline__ void build_placement(KParams& p, const Lds& L) {
     L.misc[0] = tot >> 16;
   }
   __syncthreads();
-  for (int i = tid; i < T * K; i += kThreads) {
-    const int t = i / K;
-    const int e = L.tki[i];
-    const unsigned long long below = L.bm[e * nch + (t >> 6)] & ((1ull << (t & 63)) - 1ull);
-    const int rank = L.cp[e * nch + (t >> 6)] + __popcll(below);
-    L.rows[L.base[e] + rank] = (int16_t)t;
-    L.prow[i] = (int16_t)(L.base[e] + rank);
+  for (int i0 = tid; i0 < n; i0 += kPairBatch * kThreads) {
+    int e[kPairBatch], t[kPairBatch], r[kPairBatch];
+#pragma unroll
+    for (int u = 0; u < kPairBatch; ++u) {
+      const int i = min(i0 + u * kThreads, n - 1);
+      e[u] = L.tki[i];
+      t[u] = (int)fdiv((uint32_t)i, p.fd_k.m, p.fd_k.s);
+    }
+#pragma unroll
+    for (int u = 0; u < kPairBatch; ++u) {
+      const unsigned long long below = L.bm[e[u] * nch + (t[u] >> 6)] & ((1ull << (t[u] & 63)) - 1ull);
+      r[u] = L.base[e[u]] + L.cp[e[u] * nch + (t[u] >> 6)] + __popcll(below);
+    }
+#pragma unroll
+    for (int u = 0; u < kPairBatch; ++u) {
+      const int i = i0 + u * kThreads;
+      if (i < n) {
+        L.rows[r[u]] = (int16_t)t[u];
+        L.prow[i] = (int16_t)r[u];
+      }
+    }
   }
   __syncthreads();
 }
@@ -2061,10 +2087,14 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
       if (touch == 0x9e3779b9u) L.misc[15] = 1;   // keeps the page touches alive
     } else if constexpr (!FULL) {
       if (!wait_geq(p, go_flag(p.ctr + kCtrTopkGo), 1, L.misc + 1, 1 << 20)) return false;
-      for (int i = tid; i < p.T * p.K; i += kThreads) {
-        L.tki[i] = (int16_t)ld_coh(p.topk_idx + i);
-        L.tkw[i] = ld_coh(p.topk_w + i);
-      }
+      // indices, then weights, kBatch loads in flight per thread
+      const int tk = p.T * p.K;
+      batched_copy<int>(
+          2 * tk, [&](int i) { return i < tk ? ld_coh(p.topk_idx + i) : __float_as_int(ld_coh(p.topk_w + i - tk)); },
+          [&](int i, int v) {
+            if (i < tk) L.tki[i] = (int16_t)v;
+            else L.tkw[i - tk] = __int_as_float(v);
+          });
     }
     const long long r_rows = tl_clock(p);
     const long long c_rows = tl_cycles(p);
@@ -2386,6 +2416,7 @@ Params make_params(const moe_decode_handle* h, int T) {
   p.lg_tp_log2 = T <= 8 ? 3 : 4;
   p.fd_x8 = make_fdiv((uint32_t)(p.H / 8));
   p.fd_h2 = make_fdiv((uint32_t)(p.I / 2));
+  p.fd_k = make_fdiv((uint32_t)p.K);
   for (int n = 1; n <= 4; ++n) p.fd_part[n - 1] = make_fdiv((uint32_t)(n * p.E));
   p.topk_idx = h->topk_idx;
   p.topk_w = h->topk_w;
