@@ -691,7 +691,7 @@ __device__ __forceinline__ void clear_placement(KParams& p, const Lds& L) {
 }
 __device__ __forceinline__ void build_placement(KParams& p, const Lds& L) {
   const int tid = threadIdx.x;
-  const int E = p.E, T = p.T, nch = p.nch, n = p.T * p.K;
+  const int E = p.E, nch = p.nch, n = p.T * p.K;
   // the pair loops take kPairBatch pairs per thread at a time, so their LDS
   // round trips overlap
   constexpr int kPairBatch = 4;
