@@ -2166,8 +2166,8 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
   };
 
   // Schedule.  Items [0, S) are static: workgroup g takes g, g + G, ... in
-  // order.  The last G items, [S, i_total), are claimed, so the tail
-  // balances itself: claim group c = g mod 8 owns items S + c, S + c + 8, ...
+  // order.  The items [S, i_total) are claimed, S = the later of the end of
+  // the gate/up items and i_total - G, so the tail balances itself: claim group c = g mod 8 owns items S + c, S + c + 8, ...
   // and hands them out in order from its own counter (eight counters on
   // separate lines, so simultaneous claims do not queue on one address).  A
   // claim is issued when an item starts and read when it ends, so its round
@@ -2185,7 +2185,10 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
     if (!dyn && it >= p.i_pre_end) {
       ensure_x();
       if (!ensure_routing()) break;
-      i_dyn = max(p.i_pre_end, i_total - G);
+      // every gate/up item is static: a claimed one could be queued behind
+      // the busy workgroup that claimed it while an idle one takes a down
+      // item that waits for it
+      i_dyn = max(i_rgu_end, i_total - G);
       if (it >= i_dyn) {        // past the static part: claim (blocking, once)
         dyn = true;
         if (tid == 0) L.misc[2] = i_dyn + cgroup + kClaimGroups * atomic_add_agent(claim_ctr, 1);
