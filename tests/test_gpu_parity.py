@@ -121,6 +121,19 @@ def test_ragged_T_on_one_wide_handle():
     layer.close()
 
 
+def test_maximum_batch_on_the_wide_path():
+    """512 rows (the supported maximum): eight 64-row bitmap chunks, the
+    widest LDS layout of the wide items, checked on sampled rows."""
+    wl = synth.Workload("t512_h4096_e256_k8_s1", T=512, H=4096, E=256, K=8, S=1, I=512)
+    print(f"case {wl.name}", flush=True)
+    inp = inputs_for(wl)
+    layer = device.make_layer(inp)
+    out = device.run_once(layer, inp.x, wl.E, wl.K)
+    rows = np.sort(np.random.default_rng(5).choice(wl.T, 32, replace=False))
+    check_against_oracle(wl, inp, out, rows)
+    layer.close()
+
+
 def test_zero_rows_is_a_noop():
     wl = synth.WORKLOADS[0]
     inp = inputs_for(wl)
