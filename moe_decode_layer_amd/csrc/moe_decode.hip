@@ -202,7 +202,8 @@ struct Params {
   int router_ks;       // H split of a tile: item (tile, ks) writes partial logits ks
   int i_router_end, i_topk_end, i_pre_end;   // list: router, top-k, shared gate/up, then routed
   int n_sdn;           // shared down items
-  int n_cmb;           // combine items: ceil(T / kCombineRows) * n_rg
+  int n_cmb;           // combine items: ceil(T / cmb_rows) * n_rg
+  int cmb_rows;        // rows per combine item: 8 for wide items with K <= 8 and T >= 128, else 4
   // LDS offsets (bytes)
   int lds_bm, lds_cp, lds_cnt, lds_base, lds_nmrb, lds_mrlist, lds_rows, lds_tki, lds_prow, lds_tkw,
       lds_red, lds_misc, lds_tks, lds_xs, lds_hs, lds_lg;
@@ -1254,19 +1255,22 @@ __device__ __forceinline__ int down_waves_in_group(KParams& p, int rg) {
 }
 
 // ----------------------------------------------------------------------------
-// Combine item: rows [4 rc, 4 rc + 4) x columns [128 rg, 128 rg + 128) of
+// Combine item: rows [R rc, R rc + R) x columns [128 rg, 128 rg + 128) of
 //   y[t] = bf16( o_shared[t] + sum_k w[t][k] o_{idx[t][k]}[t] ),
 // summed in exactly that order, once every down wave of column group rg has
-// counted in and every expert output read carries this run's epoch.
+// counted in and every expert output read carries this run's epoch.  Each
+// thread computes kOut outputs (R = 2 kOut rows per item) from up to kIn
+// inputs each (K <= kIn - 1 routed ones, the shared one last).
 // ----------------------------------------------------------------------------
+template <int kOut, int kIn>
 __device__ __forceinline__ bool combine_item(KParams& p, const Lds& L, int rc, int rg, int n_mr) {
-  constexpr int kOut = kCombineRows * kDownRows / kThreads;   // outputs per thread (2)
-  constexpr int kIn = kMaxTopK + 1;                           // inputs per output: K routed, shared last
+  constexpr int kRows = kOut * kThreads / kDownRows;
+  constexpr int kSh = kIn - 1;                                // slot of the shared input
   const int K = p.K;
   const int c0 = rg * kDownRows;
   const int nc = min(kDownRows, p.H - c0);
-  const int t0 = rc * kCombineRows;
-  const int nt = min(kCombineRows, p.T - t0);
+  const int t0 = rc * kRows;
+  const int nt = min(kRows, p.T - t0);
   long long t_end = 0;
   int rounds = 0;
   // Many combine items (large batches) first wait for the column group's
@@ -1293,7 +1297,7 @@ __device__ __forceinline__ bool combine_item(KParams& p, const Lds& L, int rc, i
   for (int j = 0; j < kOut; ++j)
 #pragma unroll
     for (int k = 0; k < kIn; ++k)
-      row[j][k] = k == kMaxTopK ? p.T * K + tt[j] : (k < K ? L.prow[tt[j] * K + k] : 0);
+      row[j][k] = k == kSh ? p.T * K + tt[j] : (k < K ? L.prow[tt[j] * K + k] : 0);
   // A thread missing any of its inputs reads all of them again (no
   // per-word branches; the conditions on k are uniform).
   uint64_t v[kOut][kIn];
@@ -1309,7 +1313,7 @@ __device__ __forceinline__ bool combine_item(KParams& p, const Lds& L, int rc, i
       for (int j = 0; j < kOut; ++j)
 #pragma unroll
         for (int k = 0; k < kIn; ++k)
-          if (k < K || (k == kMaxTopK && p.S)) v[j][k] = ld_tag(src[j] + (size_t)row[j][k] * p.H);
+          if ((k < K && k < kSh) || (k == kSh && p.S)) v[j][k] = ld_tag(src[j] + (size_t)row[j][k] * p.H);
       need = false;
 #pragma unroll
       for (int j = 0; j < kOut; ++j)
@@ -1321,9 +1325,9 @@ __device__ __forceinline__ bool combine_item(KParams& p, const Lds& L, int rc, i
   }
 #pragma unroll
   for (int j = 0; j < kOut; ++j) {
-    float acc = p.S ? __uint_as_float((uint32_t)v[j][kMaxTopK]) : 0.f;
+    float acc = p.S ? __uint_as_float((uint32_t)v[j][kSh]) : 0.f;
 #pragma unroll
-    for (int k = 0; k < kMaxTopK; ++k)
+    for (int k = 0; k < kSh; ++k)
       if (k < K) acc += L.tkw[tt[j] * K + k] * __uint_as_float((uint32_t)v[j][k]);
     const int o = threadIdx.x + kThreads * j;
     if (live[j]) st(p.y + (size_t)tt[j] * p.H + c0 + o % kDownRows, f32_to_bf16(acc));
@@ -2277,9 +2281,15 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
         // combine items: by column group for wide items (the order their
         // down items complete in), else by row group
         const int c = it - i_rdn_end;
-        const int n_rc = (p.T + kCombineRows - 1) / kCombineRows;
+        const int n_rc = (p.T + p.cmb_rows - 1) / p.cmb_rows;
         const int rc = p.wide ? c % n_rc : c / p.n_rg, rg = p.wide ? c / n_rc : c % p.n_rg;
-        if (!combine_item(p, L, rc, rg, n_mr)) break;
+        bool ok;
+        if constexpr (WIDE) {
+          ok = p.cmb_rows == 8 ? combine_item<4, 9>(p, L, rc, rg, n_mr) : combine_item<2, kMaxTopK + 1>(p, L, rc, rg, n_mr);
+        } else {
+          ok = combine_item<2, kMaxTopK + 1>(p, L, rc, rg, n_mr);
+        }
+        if (!ok) break;
         t_ready = *(SHARED long long*)(L.misc + 12);
       }
     }
@@ -2457,7 +2467,11 @@ Params make_params(const moe_decode_handle* h, int T) {
   p.i_topk_end = p.i_router_end + p.n_topk;
   p.i_pre_end = p.i_topk_end + p.n_mr_sh * p.n_gu_mr;
   p.n_sdn = p.n_mr_sh * p.n_dn_mr;
-  p.n_cmb = (T + kCombineRows - 1) / kCombineRows * p.n_rg;
+  // larger combine items once the 4-row ones outnumber the workgroups about
+  // twice (fewer latency-bound items in the tail); below that the items
+  // would not fill the grid
+  p.cmb_rows = p.wide && p.K <= 8 && T >= 128 ? 8 : kCombineRows;
+  p.n_cmb = (T + p.cmb_rows - 1) / p.cmb_rows * p.n_rg;
   // LDS layout
   const int E = p.E, K = p.K;
   const int max_mr = E + (T * K + p.mrange - 1) / p.mrange;
