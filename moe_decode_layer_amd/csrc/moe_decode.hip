@@ -150,6 +150,7 @@ struct Params {
   const uint16_t* x;
   uint16_t* y;
   const float* router_w;
+  const f32x4* router_wt;  // [ceil(E/16)][H/16][64]: lane (n, kq) holds router row 16 et + n, K 16 s + 4 kq .. + 3
   const float* router_b;   // [E] (without a bias: any readable [E] floats, unused)
   int has_bias;
   const u32x4* w13p;   // [E+S][2I/16][H/64][64] tiles
@@ -795,7 +796,9 @@ __device__ __forceinline__ void router_tile_item(KParams& p, const Lds& L, int i
   const int kw = p.H / p.router_ks / kWaves;   // K per wave (a multiple of 16)
   const int kbase = ks * (p.H / p.router_ks) + w * kw;
   const uint16_t* xr = p.x + (size_t)(t0 + min(n, nt - 1)) * p.H + kbase + 4 * kq;
-  const float* wr = p.router_w + (size_t)(e0 + min(n, ne - 1)) * p.H + kbase + 4 * kq;
+  // the router rows come from their tiled copy: one step of 16 K of the 16
+  // experts is one contiguous KiB, lane (n, kq) holding expert n's K 4 kq .. + 3
+  const f32x4* wr = p.router_wt + ((size_t)(e0 / kRouterTile) * (p.H / 16) + kbase / 16) * kWave + lane;
   // the bias goes with part 0 (the top-k items add the parts in order); it
   // is requested first, so its round trip overlaps the weights'
   const float bv = ld(p.router_b + e0 + min(n, ne - 1));   // unconditional: no branch, no early wait
@@ -813,7 +816,7 @@ __device__ __forceinline__ void router_tile_item(KParams& p, const Lds& L, int i
     for (int u = 0; u < kU; ++u) {
       const int k = min(k0 + 16 * u, kw - 16);  // past the end: reread the last step (unused)
       S.xa[u] = ld((const u32x2*)(xr + k));
-      S.wb[u] = ld((const f32x4*)(wr + k));
+      S.wb[u] = ld(wr + (size_t)(k / 16) * kWave);
     }
   };
   auto compute = [&](const Stage& S, int k0) __attribute__((always_inline)) {
@@ -2357,6 +2360,21 @@ __global__ void pack_kernel(const uint8_t* __restrict__ w, const float* __restri
   }
 }
 
+// Router rows -> tiled copy for the router tiles (create time); experts past
+// E are zero.
+__global__ void pack_router_kernel(const float* __restrict__ w, f32x4* __restrict__ wt, int E, int H) {
+  const int n_et = (E + kRouterTile - 1) / kRouterTile, ns = H / 16;
+  const size_t total = (size_t)n_et * ns * kWave;
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < total;
+       i += (size_t)gridDim.x * blockDim.x) {
+    const int lane = (int)(i % kWave);
+    const size_t st = i / kWave;
+    const int step = (int)(st % ns), et = (int)(st / ns);
+    const int e = kRouterTile * et + (lane & 15), k = 16 * step + 4 * (lane >> 4);
+    wt[i] = e < E ? *(const f32x4*)(w + (size_t)e * H + k) : (f32x4){0.f, 0.f, 0.f, 0.f};
+  }
+}
+
 // ----------------------------------------------------------------------------
 // Host side
 // ----------------------------------------------------------------------------
@@ -2370,6 +2388,7 @@ struct moe_decode_handle {
   int n_cu;
   int coop;
   float* router_w = nullptr;
+  f32x4* router_wt = nullptr;
   float* router_b = nullptr;
   u32x4* w13p = nullptr;
   float* s13p = nullptr;
@@ -2418,6 +2437,7 @@ Params make_params(const moe_decode_handle* h, int T) {
   p.S = c.num_shared;
   p.I = c.intermediate;
   p.router_w = h->router_w;
+  p.router_wt = h->router_wt;
   p.router_b = h->router_b ? h->router_b : h->router_w;
   p.has_bias = h->router_b != nullptr;
   p.w13p = h->w13p;
@@ -2566,7 +2586,7 @@ void moe_decode_destroy(moe_decode_handle* h) {
   (void)hipGetDevice(&prev);
   (void)hipSetDevice(h->device);
   (void)hipDeviceSynchronize();
-  void* ptrs[] = {h->router_w, h->router_b, h->w13p, h->s13p, h->w2p, h->s2p, h->lgt,
+  void* ptrs[] = {h->router_w, h->router_wt, h->router_b, h->w13p, h->s13p, h->w2p, h->s2p, h->lgt,
                   h->topk_idx, h->topk_w, h->h_scr, h->o_scr, h->ctr};
   for (void* q : ptrs)
     if (q) (void)hipFree(q);
@@ -2605,6 +2625,7 @@ moe_status moe_decode_create(const moe_decode_config* cfg, const moe_decode_weig
     const size_t ctr_words = 2 * (size_t)kCtrHead + kLine;   // two blocks + the status line
     struct A { void** p; size_t bytes; } allocs[] = {
         {(void**)&h->router_w, E * H * 4},
+        {(void**)&h->router_wt, (E + kRouterTile - 1) / kRouterTile * kRouterTile * H * 4},
         {(void**)&h->router_b, w->router_bias ? E * 4 : 0},
         {(void**)&h->w13p, slots * 2 * I * H},
         {(void**)&h->s13p, slots * 2 * I * (H / 32) * 4},
@@ -2630,6 +2651,8 @@ moe_status moe_decode_create(const moe_decode_config* cfg, const moe_decode_weig
     if (hipMemcpy(h->router_w, w->router_w, E * H * 4, hipMemcpyDeviceToDevice) != hipSuccess) { rc = MOE_ERR_HIP; break; }
     if (w->router_bias &&
         hipMemcpy(h->router_b, w->router_bias, E * 4, hipMemcpyDeviceToDevice) != hipSuccess) { rc = MOE_ERR_HIP; break; }
+    hipLaunchKernelGGL(pack_router_kernel, dim3(1024), dim3(256), 0, 0, h->router_w, h->router_wt, (int)E, (int)H);
+    if (hipGetLastError() != hipSuccess) { rc = MOE_ERR_HIP; break; }
     hipLaunchKernelGGL(pack_kernel, dim3(4096), dim3(256), 0, 0, w->w13, w->s13, h->w13p, h->s13p,
                        (int)slots, (int)(2 * I), (int)H, (int)I);
     if (hipGetLastError() != hipSuccess) { rc = MOE_ERR_HIP; break; }
