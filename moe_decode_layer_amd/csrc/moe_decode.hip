@@ -2,9 +2,10 @@
 // include/moe_decode.h.
 //
 // One launch runs the whole layer.  Every workgroup stays resident and walks
-// its own share of one global list of work items (item i belongs to
-// workgroup i mod G, taken in order); an item that needs earlier results
-// for a counter the producing items bump, then for the tags of its inputs.  Blocks that stay
+// its own share of one global list of work items (the early items are
+// static, item i belonging to workgroup i mod G; the tail is claimed from
+// counters); an item that needs earlier results waits for a counter the
+// producing items bump, then for the tags of its inputs.  Blocks that stay
 // resident across stages, pass ready results on through tagged buffers and
 // load weights while earlier stages still compute follow "FlyDSL Mono
 // Kernels for High-Interactivity LLM Serving in ATOM" (sections "What FlyDSL
@@ -18,19 +19,23 @@
 // were not all resident, the deadline turns the stall into an error):
 //   router          : logits of one expert for up to 8 rows (batches above
 //                     16 rows: a 16-row x 16-expert MFMA tile, or part of
-//                     its H)
+//                     its H, read from a tiled copy of the router rows)
 //   top-k           : 4 rows, one per wave (only for batches above 16 rows;
 //                     smaller batches select top-k in every workgroup)
 //   shared gate/up  : 16 weight rows (8 gate + 8 up) of the shared expert
 //   routed gate/up  : 16 weight rows of one routed expert      -- waits: routing
 //   shared down     : 128 output rows of the shared expert     -- waits: its gate/up
 //   routed down     : 128 output rows of one routed expert     -- waits: its gate/up
-//   combine         : 4 rows x 128 columns of y                -- waits: the down
+//   combine         : 4 (or 8) rows x 128 columns of y         -- waits: the down
 //                                                                 items of those columns
 // A gate/up or down item covers up to 64 rows of its expert (four 16-row
-// MFMA blocks); experts with more rows get one item per 64 rows.  Results
-// handed between workgroups carry the run's epoch (tagged words), so a
-// producer never waits for its own stores: it bumps a counter and moves on.
+// MFMA blocks); experts with more rows get one item per 64 rows.  Batches
+// above 16 rows at H = 4096, I = 512 use wide items instead: gate/up items of
+// 64 weight rows and down items of 512 output rows, for up to 32 rows each,
+// with the down and combine items ordered by column group (see
+// gu_item_wide).  Results handed between workgroups carry the run's epoch
+// (tagged words), so a producer never waits for its own stores: it bumps a
+// counter and moves on.
 //
 // Expert weights are re-laid out once, at create time, into 1 KiB tiles of
 // 16 weight rows x 64 K: lane l of a wave reads bytes [16 l, 16 l + 16) of a
