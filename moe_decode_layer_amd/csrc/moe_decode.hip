@@ -155,7 +155,6 @@ struct Params {
   const uint16_t* x;
   uint16_t* y;
   const float* router_w;
-  const f32x4* router_wt;  // [ceil(E/16)][H/16][64]: lane (n, kq) holds router row 16 et + n, K 16 s + 4 kq .. + 3
   const float* router_b;   // [E] (without a bias: any readable [E] floats, unused)
   int has_bias;
   const u32x4* w13p;   // [E+S][2I/16][H/64][64] tiles
@@ -188,7 +187,6 @@ struct Params {
   int lg_copies, lg_tp_log2;
   FDiv fd_x8;          // H / 8: 16-byte words of an x row
   FDiv fd_h2;          // I / 2: tagged words of an h row
-  FDiv fd_k;           // K: the row of a (row, k) pair index
   FDiv fd_part[4];     // n E for n = 1..4: logits of a distributed top-k item's rows
   int n_rb13;          // gate/up row blocks per expert: I/8
   int n_q13;           // tiles along H: H/64
@@ -196,11 +194,6 @@ struct Params {
   int n_q2;            // tiles along I: I/64
   int n_rg;            // down row groups: ceil(H/128)
   int n_mr_sh;         // shared M-ranges: ceil(T/mrange) (0 without a shared expert)
-  int wide;            // 1: wide items (see gu_item_wide / dn_item_wide)
-  int mrange;          // rows per expert item: 64, wide 32
-  int n_gu_mr;         // gate/up items per M-range: n_rb13, wide n_rb13/4
-  int n_dn_mr;         // down items per M-range: n_rg, wide H/512
-  int h_rows_per_count;  // gate/up publications per row block come one per this many rows
   int nch;             // 64-row chunks: ceil(T/64)
   // item list boundaries
   int n_router, n_topk;
@@ -209,13 +202,21 @@ struct Params {
   int i_router_end, i_topk_end, i_pre_end;   // list: router, top-k, shared gate/up, then routed
   int n_sdn;           // shared down items
   int n_cmb;           // combine items: ceil(T / cmb_rows) * n_rg
-  int cmb_rows;        // rows per combine item: 8 for wide items with K <= 8 and T >= 128, else 4
   // LDS offsets (bytes)
   int lds_bm, lds_cp, lds_cnt, lds_base, lds_nmrb, lds_mrlist, lds_rows, lds_tki, lds_prow, lds_tkw,
       lds_red, lds_misc, lds_tks, lds_xs, lds_hs, lds_lg;
   int lds_bytes;
   int xs_stride;       // x rows in LDS (bf16 elements per row), 0 when x stays in global memory
   int hs_stride;       // h rows staged in LDS for a down item, 0 when read from global memory
+  // (kept last: the fields above are the ones the small-batch path reads)
+  int wide;            // 1: wide items (see gu_item_wide / dn_item_wide)
+  int mrange;          // rows per expert item: 64, wide 32
+  int n_gu_mr;         // gate/up items per M-range: n_rb13, wide n_rb13/4
+  int n_dn_mr;         // down items per M-range: n_rg, wide H/512
+  int h_rows_per_count;  // gate/up publications per row block come one per this many rows
+  FDiv fd_k;           // K: the row of a (row, k) pair index
+  int cmb_rows;        // rows per combine item: 8 for wide items with K <= 8 and T >= 128, else 4
+  const f32x4* router_wt;  // [ceil(E/16)][H/16][64]: lane (n, kq) holds router row 16 et + n, K 16 s + 4 kq .. + 3
 };
 // The kernel reads its parameters in place, from the constant kernel-argument
 // segment, so the compiler can reload a field with a scalar load instead of
@@ -2630,7 +2631,6 @@ moe_status moe_decode_create(const moe_decode_config* cfg, const moe_decode_weig
     const size_t ctr_words = 2 * (size_t)kCtrHead + kLine;   // two blocks + the status line
     struct A { void** p; size_t bytes; } allocs[] = {
         {(void**)&h->router_w, E * H * 4},
-        {(void**)&h->router_wt, (E + kRouterTile - 1) / kRouterTile * kRouterTile * H * 4},
         {(void**)&h->router_b, w->router_bias ? E * 4 : 0},
         {(void**)&h->w13p, slots * 2 * I * H},
         {(void**)&h->s13p, slots * 2 * I * (H / 32) * 4},
@@ -2642,6 +2642,8 @@ moe_status moe_decode_create(const moe_decode_config* cfg, const moe_decode_weig
         {(void**)&h->h_scr, scr_rows * (I / 2) * 8},
         {(void**)&h->o_scr, scr_rows * H * 8},
         {(void**)&h->ctr, ctr_words * 4},
+        // tiled router rows, only for handles that can run router tiles
+        {(void**)&h->router_wt, Tm > (size_t)kMBlock ? (E + kRouterTile - 1) / kRouterTile * kRouterTile * H * 4 : 0},
     };
     for (auto& a : allocs) {
       if (a.bytes == 0) continue;
@@ -2656,8 +2658,10 @@ moe_status moe_decode_create(const moe_decode_config* cfg, const moe_decode_weig
     if (hipMemcpy(h->router_w, w->router_w, E * H * 4, hipMemcpyDeviceToDevice) != hipSuccess) { rc = MOE_ERR_HIP; break; }
     if (w->router_bias &&
         hipMemcpy(h->router_b, w->router_bias, E * 4, hipMemcpyDeviceToDevice) != hipSuccess) { rc = MOE_ERR_HIP; break; }
-    hipLaunchKernelGGL(pack_router_kernel, dim3(1024), dim3(256), 0, 0, h->router_w, h->router_wt, (int)E, (int)H);
-    if (hipGetLastError() != hipSuccess) { rc = MOE_ERR_HIP; break; }
+    if (h->router_wt) {
+      hipLaunchKernelGGL(pack_router_kernel, dim3(1024), dim3(256), 0, 0, h->router_w, h->router_wt, (int)E, (int)H);
+      if (hipGetLastError() != hipSuccess) { rc = MOE_ERR_HIP; break; }
+    }
     hipLaunchKernelGGL(pack_kernel, dim3(4096), dim3(256), 0, 0, w->w13, w->s13, h->w13p, h->s13p,
                        (int)slots, (int)(2 * I), (int)H, (int)I);
     if (hipGetLastError() != hipSuccess) { rc = MOE_ERR_HIP; break; }
