@@ -2003,7 +2003,7 @@ __device__ __forceinline__ bool dn_item_wide(KParams& p, const Lds& L, int slot,
 // (H = 64 kFullTiles, I = 32 kFullTiles) and local routing only; the other
 // variants hold the general code.  Each variant carries only the code its
 // batches reach, which keeps register pressure (and spills) down.
-template <int NMBMAX, bool XL, bool FULL, bool WIDE>
+template <int NMBMAX, bool XL, bool FULL, bool WIDE, int NQ2 = kFullTiles / 2>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(NMBMAX == 1 || WIDE ? 2 : 1))) moe_decode_kernel(Params arg) {
   KParams& p = *(const CONSTANT Params*)__builtin_amdgcn_kernarg_segment_ptr();
   (void)arg;
@@ -2165,7 +2165,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
     if constexpr (WIDE) {
       if (nmb <= 1) return dn_item_wide<1>(p, L, slot, sbase, r0, nrows, rg, ht, pend_rg);
       return dn_item_wide<2>(p, L, slot, sbase, r0, nrows, rg, ht, pend_rg);
-    } else if constexpr (FULL) return down_item_full<kFullTiles / 2>(p, L, slot, sbase, r0, nrows, rg, ht, pend_rg);
+    } else if constexpr (FULL) return down_item_full<NQ2>(p, L, slot, sbase, r0, nrows, rg, ht, pend_rg);
     else if (XL && p.hs_stride > 0) return down_item<1, XL>(p, L, slot, sbase, r0, nrows, rg, ht, pend_rg);
     else if (NMBMAX == 1 || nmb <= 1) return down_item<1, false>(p, L, slot, sbase, r0, nrows, rg, ht, pend_rg);
     else if (nmb == 2) return down_item<NMBMAX >= 2 ? 2 : 1, false>(p, L, slot, sbase, r0, nrows, rg, ht, pend_rg);
@@ -2411,8 +2411,8 @@ struct moe_decode_handle {
   hipStream_t last_stream = nullptr;
   std::mutex mu;
   // occupancy cache, by (kernel variant, LDS bytes)
-  int occ_lds[5] = {-1, -1, -1, -1, -1};
-  int occ_blocks[5] = {0, 0, 0, 0, 0};
+  int occ_lds[6] = {-1, -1, -1, -1, -1, -1};
+  int occ_blocks[6] = {0, 0, 0, 0, 0, 0};
 };
 
 namespace {
@@ -2733,13 +2733,16 @@ moe_status moe_decode_run(moe_decode_handle* h, const void* x, int32_t T, void* 
   p.ctr_next = h->ctr + (size_t)((h->epoch + 1) & 1) * kCtrHead;
   // variants: 0 = x in LDS, 1 = up to 16 rows, 2 = more rows (4 MFMA blocks
   // per item), 3 = x in LDS with full-tile items (H = 64 kFullTiles,
-  // I = 32 kFullTiles, h staged in LDS, local routing), 4 = more than 16 rows
-  // with wide items (H = 64 kWideTiles, I = 64 kWideQ2)
+  // I = 32 kFullTiles, h staged in LDS, local routing), 5 = the same at
+  // I = 576 (9 K tiles per down row block: the pages' per-GPU width without
+  // padding), 4 = more than 16 rows with wide items (H = 64 kWideTiles,
+  // I = 64 kWideQ2)
   const bool full = p.xs_stride > 0 && p.hs_stride > 0 && p.n_q13 == 4 * kFullTiles &&
-                    p.n_q2 == kFullTiles / 2 && p.local_topk && !p.router_tiles;
-  const int variant = p.wide ? 4 : full ? 3 : p.xs_stride > 0 ? 0 : (T > kMBlock ? 2 : 1);
+                    (p.n_q2 == kFullTiles / 2 || p.n_q2 == kFullTiles / 2 + 1) && p.local_topk && !p.router_tiles;
+  const int variant = p.wide ? 4 : full ? (p.n_q2 == kFullTiles / 2 ? 3 : 5) : p.xs_stride > 0 ? 0 : (T > kMBlock ? 2 : 1);
   const void* fn = variant == 4   ? (const void*)moe_decode_kernel<2, false, false, true>
                    : variant == 3 ? (const void*)moe_decode_kernel<1, true, true, false>
+                   : variant == 5 ? (const void*)moe_decode_kernel<1, true, true, false, kFullTiles / 2 + 1>
                    : variant == 0 ? (const void*)moe_decode_kernel<1, true, false, false>
                    : variant == 1 ? (const void*)moe_decode_kernel<1, false, false, false>
                                   : (const void*)moe_decode_kernel<4, false, false, false>;

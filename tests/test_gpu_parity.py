@@ -76,6 +76,9 @@ SMALL = [
     synth.Workload("t200_h256_e4_k2_s0", T=200, H=256, E=4, K=2, S=0, I=128),   # 100 rows/expert
     synth.Workload("t33_h320_e64_k6_s1", T=33, H=320, E=64, K=6, S=1, I=128, zipf_s=1.2),
     synth.Workload("t9_h4096_e256_k8_s1", T=9, H=4096, E=256, K=8, S=1, I=512),
+    # the real per-GPU intermediate width of the pages' model (18 scale groups),
+    # run without padding to 640: the general items, x in LDS
+    synth.Workload("t6_h4096_e256_k8_s1_i576", T=6, H=4096, E=256, K=8, S=1, I=576),
 ]
 
 
