@@ -137,6 +137,32 @@ def test_maximum_batch_on_the_wide_path():
     layer.close()
 
 
+@pytest.mark.parametrize("wi,Ts", [(1, (6, 1, 3, 6, 2, 5)), (4, (384, 17, 200, 64, 33))],
+                         ids=["small_batches", "wide_batches"])
+def test_many_runs_on_one_handle_repeat_bit_for_bit(wi, Ts):
+    """Forty runs on one handle with the row count changing every run: every
+    run's y equals, bit for bit, the first run with the same rows (the epoch
+    tags, the alternating counter blocks and the per-run clearing leave no
+    state behind), and the first run of each row count matches the oracle."""
+    wl = synth.WORKLOADS[wi]
+    inp = inputs_for(wl)
+    layer = device.make_layer(inp, max_tokens=wl.T)
+    first = {}
+    for i in range(40):
+        T = Ts[i % len(Ts)]
+        out = device.run_once(layer, np.ascontiguousarray(inp.x[:T]), wl.E, wl.K, debug=(T not in first))
+        if T not in first:
+            print(f"case {wl.name} T={T}", flush=True)
+            sub = synth.Inputs(wl.with_rows(T), inp.x[:T], inp.router_w, inp.router_b, inp.w13,
+                               inp.s13, inp.w2, inp.s2, inp.attempts[:T])
+            rows = None if T <= 64 else np.sort(np.random.default_rng(T).choice(T, 16, replace=False))
+            check_against_oracle(sub.workload, sub, out, rows)
+            first[T] = out["y"]
+        else:
+            assert np.array_equal(out["y"], first[T]), f"run {i} (T={T}) differs from the first"
+    layer.close()
+
+
 def test_zero_rows_is_a_noop():
     wl = synth.WORKLOADS[0]
     inp = inputs_for(wl)
