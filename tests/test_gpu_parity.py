@@ -163,6 +163,32 @@ def test_many_runs_on_one_handle_repeat_bit_for_bit(wi, Ts):
     layer.close()
 
 
+def test_two_handles_interleaved_on_one_stream():
+    """Two handles (different shapes and variants) alternating on one stream
+    keep separate counters and tags: each one's output is its own first
+    output, bit for bit, run after run."""
+    wa, wb = synth.WORKLOADS[1], synth.WORKLOADS[0]
+    ia = synth.make_inputs(wa, GOLDEN["attempts"].get(wa.name))
+    ib = synth.make_inputs(wb, GOLDEN["attempts"].get(wb.name))
+    la, lb = device.make_layer(ia), device.make_layer(ib)
+    ya = device.run_once(la, ia.x, wa.E, wa.K, debug=False)["y"]
+    yb = device.run_once(lb, ib.x, wb.E, wb.K, debug=False)["y"]
+    dev = torch.device("cuda", 0)
+    xa, xb = device.to_device(ia.x, dev), device.to_device(ib.x, dev)
+    outs = []
+    for _ in range(6):
+        for layer, x, T in ((la, xa, wa.T), (lb, xb, wb.T)):
+            y = torch.empty_like(x)
+            layer.run(x, y, T)
+            outs.append(y)
+    assert la.check() == binding.MOE_OK and lb.check() == binding.MOE_OK
+    for i, y in enumerate(outs):
+        ref = ya if i % 2 == 0 else yb
+        assert np.array_equal(y.cpu().numpy().view(np.uint16), ref), f"run {i} differs"
+    la.close()
+    lb.close()
+
+
 def test_zero_rows_is_a_noop():
     wl = synth.WORKLOADS[0]
     inp = inputs_for(wl)
