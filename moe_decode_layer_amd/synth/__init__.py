@@ -27,6 +27,7 @@ TENSOR_X = 1
 TENSOR_ROUTER = 2
 TENSOR_W13 = 3
 TENSOR_W2 = 4
+TENSOR_NORM = 5
 
 
 @dataclasses.dataclass(frozen=True)
@@ -49,6 +50,10 @@ class Workload:
     seed: int = 0
     x_std: float = 1.0
     expert_std: float = 0.02
+    # pre-norm block: x is the residual stream, normalised (RMSNorm, weight
+    # from ``norm_weight``) before the layer and added back to its output
+    prenorm: bool = False
+    norm_eps: float = 1e-6
 
     @property
     def router_std(self) -> float:
@@ -80,7 +85,11 @@ WORKLOADS = [
     Workload("verify_t384_h4096_e256_k8_s1", T=384, H=4096, E=256, K=8, S=1, I=512),
 ]
 
-BY_NAME = {w.name: w for w in WORKLOADS}
+# The same shapes as pre-norm blocks (input RMSNorm + residual add fused
+# around the layer).
+PRENORM = [dataclasses.replace(w, name=w.name + "_prenorm", prenorm=True) for w in WORKLOADS]
+
+BY_NAME = {w.name: w for w in WORKLOADS + PRENORM}
 
 _lib = None
 
@@ -136,6 +145,29 @@ def x_rows(w: Workload, attempts) -> np.ndarray:
     if T:
         lib().synth_x_bf16(w.seed, TENSOR_X, T, w.H, w.x_std, _ptr(att), _ptr(out))
     return out
+
+
+def block_rows(w: Workload, attempts) -> np.ndarray:
+    """Residual-stream rows of a pre-norm block (bf16 bits [T][H]): the rows
+    of ``x_rows`` with row t scaled by 2^((t mod 3) - 1), so rows differ in
+    magnitude (a power of two keeps every value exact)."""
+    b = x_rows(w, attempts)
+    f = (b.astype(np.uint32) << np.uint32(16)).view(np.float32)
+    f = f * np.ldexp(np.float32(1.0), (np.arange(b.shape[0]) % 3 - 1))[:, None].astype(np.float32)
+    return (f.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+
+
+def norm_weight(w: Workload) -> np.ndarray:
+    """RMSNorm weight [H] fp32: 1 + fp32(N(0, 0.1^2))."""
+    out = np.empty((1, w.H), np.float32)
+    lib().synth_f32(w.seed, TENSOR_NORM, 0, 1, w.H, 0.1, _ptr(out))
+    return (out[0] + np.float32(1.0)).astype(np.float32)
+
+
+def candidate_rows(w: Workload):
+    """The row generator whose draws the margin selection picks from: the
+    block input for a pre-norm block, else the layer input."""
+    return (lambda a: block_rows(w, a)) if w.prenorm else (lambda a: x_rows(w, a))
 
 
 def router_weights(w: Workload) -> np.ndarray:
@@ -194,6 +226,7 @@ class Inputs:
     w2: np.ndarray
     s2: np.ndarray
     attempts: np.ndarray   # [T] int32
+    norm_w: np.ndarray | None = None  # [H] fp32, pre-norm blocks only
 
 
 def make_inputs(w: Workload, attempts=None) -> Inputs:
@@ -203,5 +236,5 @@ def make_inputs(w: Workload, attempts=None) -> Inputs:
     attempts = np.asarray(attempts, np.int32)
     assert attempts.shape == (w.T,)
     w13, s13, w2, s2 = expert_weights(w)
-    return Inputs(w, x_rows(w, attempts), router_weights(w), zipf_bias(w),
-                  w13, s13, w2, s2, attempts)
+    return Inputs(w, candidate_rows(w)(attempts), router_weights(w), zipf_bias(w),
+                  w13, s13, w2, s2, attempts, norm_weight(w) if w.prenorm else None)

@@ -40,6 +40,17 @@ definitions, else the plainest reading):
   * FP8 is OCP e4m3fn (bias 7, max 448, S.1111.111 is NaN, no infinities);
     dequantised weight = e4m3fn(q) * scale of its 32-element K group.
 
+The pre-norm block form (input RMSNorm before the router, residual added
+after the combine) follows "SGLang's Low-Latency Mode Boosts DeepSeek-V4.1-
+Flash Speed by 1.56x on AMD", section "AMD keeps the layer resident" (the
+MoE input is normalised and its rows handed on as they become ready), and
+"Beyond Day-0 ...", section 2.1 (the next layer's input combined and
+normalised right after the MoE).  The pages give no formula; the readings:
+  * xn[t] = bf16(x[t] * gamma / sqrt(mean_h x[t][h]^2 + eps)), one rounding
+    (the layer's bf16 input), in fp64 here;
+  * y[t] = bf16(x[t] + moe(xn)[t]) with the MoE sum unrounded: one rounding
+    of the residual stream, where the plain layer rounds the MoE sum alone.
+
 Every function here is pinned by the CPU tests (tests/test_oracle_*.py)
 against closed forms, library routines, invariants and brute force.
 """
@@ -238,6 +249,36 @@ def forward(inp, rows=None) -> Result:
 
 
 # --------------------------------------------------------------------------
+# Pre-norm block: input RMSNorm and residual
+# --------------------------------------------------------------------------
+def rmsnorm_bf16(x_bits: np.ndarray, gamma: np.ndarray, eps: float) -> np.ndarray:
+    """bf16 bits of x * gamma / sqrt(mean(x^2) + eps) per row of x [T][H]
+    (bf16 bits), computed in fp64 and rounded once."""
+    X = bf16_bits_to_f64(x_bits)
+    ms = np.mean(X * X, axis=1, keepdims=True)
+    xn = X * (1.0 / np.sqrt(ms + float(eps))) * np.asarray(gamma, np.float64)[None, :]
+    return bf16_value_to_bits(bf16_round(xn))
+
+
+@dataclasses.dataclass
+class BlockResult:
+    xn: np.ndarray       # [T][H] bf16 bits: the rows the MoE layer ran on
+    moe: Result          # the plain layer on xn
+    y: np.ndarray        # [len(rows)][H] fp64 x + moe, before output rounding
+    y_bf16: np.ndarray   # [len(rows)][H] fp64 values of the bf16 output
+
+
+def forward_block(inp, rows=None) -> BlockResult:
+    """x -> xn = RMSNorm(x) -> the layer -> y = bf16(x + layer(xn)).  ``inp``
+    carries the block input in ``x`` and the norm weight and epsilon in
+    ``norm_w`` / ``workload.norm_eps``."""
+    xn = rmsnorm_bf16(inp.x, inp.norm_w, inp.workload.norm_eps)
+    res = forward(dataclasses.replace(inp, x=xn), rows)
+    y = bf16_bits_to_f64(inp.x)[res.rows] + res.y
+    return BlockResult(xn, res, y, bf16_round(y))
+
+
+# --------------------------------------------------------------------------
 # Input selection with routing margins
 # --------------------------------------------------------------------------
 def choose_attempts(wl, x_rows, router_w, router_b, max_attempts: int = 1000) -> np.ndarray:
@@ -255,3 +296,18 @@ def choose_attempts(wl, x_rows, router_w, router_b, max_attempts: int = 1000) ->
         att[bad] += 1
         todo = bad
     return att
+
+
+def choose_attempts_block(wl, x_rows, norm_w, router_w, router_b,
+                          max_attempts: int = 1000) -> np.ndarray:
+    """choose_attempts for a pre-norm block: the margins are those of the
+    normalised rows the router sees."""
+    return choose_attempts(wl, lambda a: rmsnorm_bf16(x_rows(a), norm_w, wl.norm_eps),
+                           router_w, router_b, max_attempts)
+
+
+def attempts_for(wl, rows, router_w, router_b, norm_w=None) -> np.ndarray:
+    """The margin selection that fits the workload (plain layer or block)."""
+    if getattr(wl, "prenorm", False):
+        return choose_attempts_block(wl, rows, norm_w, router_w, router_b)
+    return choose_attempts(wl, rows, router_w, router_b)

@@ -11,11 +11,14 @@ from oracle import moe_oracle as O
 PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "attempts.json")
 
 
-@pytest.mark.parametrize("i", range(len(synth.WORKLOADS)))
+ALL = synth.WORKLOADS + synth.PRENORM
+
+
+@pytest.mark.parametrize("i", range(len(ALL)))
 def test_stored_attempts_are_current(i):
-    wl = synth.WORKLOADS[i]
+    wl = ALL[i]
     stored = json.load(open(PATH))
     assert stored["margin"] == O.MARGIN and stored["seed"] == wl.seed
-    got = O.choose_attempts(wl, lambda a: synth.x_rows(wl, a), synth.router_weights(wl),
-                            synth.zipf_bias(wl))
+    got = O.attempts_for(wl, synth.candidate_rows(wl), synth.router_weights(wl),
+                         synth.zipf_bias(wl), synth.norm_weight(wl) if wl.prenorm else None)
     assert stored["attempts"][wl.name] == [int(a) for a in got]

@@ -27,8 +27,8 @@ def inputs_for(wl):
     if wl.name not in _cache:
         att = GOLDEN["attempts"].get(wl.name)
         if att is None:
-            att = O.choose_attempts(wl, lambda a: synth.x_rows(wl, a), synth.router_weights(wl),
-                                    synth.zipf_bias(wl))
+            att = O.attempts_for(wl, synth.candidate_rows(wl), synth.router_weights(wl),
+                                 synth.zipf_bias(wl), synth.norm_weight(wl) if wl.prenorm else None)
         _cache.clear()
         _cache[wl.name] = synth.make_inputs(wl, att)
     return _cache[wl.name]
