@@ -69,7 +69,7 @@ def cpu_baseline(inp, expert_bytes: int, budget_s: float = 15.0):
     t_start = time.perf_counter()
     while len(times) < 3 or (len(times) < 10 and time.perf_counter() - t_start < budget_s):
         t0 = time.perf_counter()
-        O.forward(inp)
+        (O.forward_block if inp.workload.prenorm else O.forward)(inp)
         times.append(time.perf_counter() - t0)
     med = float(np.median(times))
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
@@ -113,14 +113,18 @@ def main():
     y = torch.empty_like(x)
     dbg = device.debug_buffers(wl.T, wl.E, wl.K, dev)
 
+    # pre-norm block workloads time the fused block (RMSNorm + layer + residual)
+    run = layer.run_block if wl.prenorm else layer.run
+
     # one checked call: routing tells how many experts the call streams
-    layer.run(x, y, wl.T, dbg)
+    run(x, y, wl.T, dbg)
     assert layer.check() == 0
     counts = dbg["expert_count"].cpu().numpy()
     touched = int((counts > 0).sum()) + wl.S
     expert_bytes = touched * wl.expert_bytes()
     router_bytes = wl.E * wl.H * 4
-    act_bytes = 2 * wl.T * wl.H * 2
+    # x in, y out; a block run also writes and reads back xn and reads the norm weight
+    act_bytes = 2 * wl.T * wl.H * 2 + (2 * wl.T * wl.H * 2 + wl.H * 4 if wl.prenorm else 0)
 
     stream = torch.cuda.current_stream()
     scrub = torch.ones(1 << 28, dtype=torch.int32, device=dev)    # 1 GiB, swept read-only
@@ -130,14 +134,14 @@ def main():
     for _ in range(args.warmup):
         if not args.no_scrub:
             scrub.amax()
-        layer.run(x, y, wl.T, None, stream)
+        run(x, y, wl.T, None, stream)
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
     for i in range(args.steps):
         if not args.no_scrub:
             scrub.amax()
         starts[i].record(stream)
-        layer.run(x, y, wl.T, None, stream)
+        run(x, y, wl.T, None, stream)
         ends[i].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_wall

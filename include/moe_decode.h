@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define MOE_DECODE_ABI_VERSION 1
+#define MOE_DECODE_ABI_VERSION 2
 
 typedef int32_t moe_status;
 #define MOE_OK                0  /* success */
@@ -126,6 +126,11 @@ typedef struct moe_decode_debug {
    * the handle is unaffected.  0 for normal runs.
    */
   int32_t expire_waits;
+  /*
+   * [T][H] bf16: the normalised rows a pre-norm block run fed to the router
+   * and the experts (moe_decode_run_block only; ignored by moe_decode_run).
+   */
+  uint16_t* norm_x;
 } moe_decode_debug;
 
 typedef struct moe_decode_handle moe_decode_handle;
@@ -158,6 +163,39 @@ moe_status moe_decode_create(const moe_decode_config* cfg, const moe_decode_weig
  */
 moe_status moe_decode_run(moe_decode_handle* h, const void* x, int32_t T, void* y,
                           const moe_decode_debug* dbg, void* hip_stream);
+
+/*
+ * Pre-norm block form of the layer: the RMSNorm that feeds the MoE input and
+ * the residual add after the combine, fused into the same single launch.
+ * Sources: "SGLang's Low-Latency Mode Boosts DeepSeek-V4.1-Flash Speed by
+ * 1.56x on AMD", section "AMD keeps the layer resident" (the MoE input is
+ * normalised inside the resident kernel and each row is handed on to the
+ * router and experts as soon as it is ready); "Beyond Day-0: Optimizing
+ * DeepSeek-V4.1 Flash in SGLang", section 2.1 (the layer's output combined
+ * into the next layer's input right after the MoE, without extra passes).
+ *
+ * set_input_norm: the RMSNorm weight gamma (device pointer, [H] fp32, copied:
+ * the caller may free it on return) and epsilon (finite, > 0).  The first call
+ * allocates the handle's normalised-row buffer ([max_tokens][H] bf16) and row
+ * ready words; later calls replace the weight.  Synchronous: waits for the
+ * handle's last run first.  MOE_ERR_INVALID_ARG for a NULL pointer or a bad
+ * epsilon, MOE_ERR_OUT_OF_MEMORY / MOE_ERR_HIP on device errors.
+ */
+moe_status moe_decode_set_input_norm(moe_decode_handle* h, const float* norm_w, float eps);
+
+/*
+ * run_block: like moe_decode_run, but x [T][H] bf16 is the block input (the
+ * residual stream) and
+ *   xn[t] = bf16( x[t][h] * gamma[h] / sqrt(mean_h x[t][h]^2 + eps) )   (fp32 arithmetic)
+ *   y[t]  = bf16( x[t] + o_shared[t] + sum_k w[t][k] * o_{idx[t][k]}[t] )  with the
+ *           layer above run on xn (routing included): one rounding of the sum.
+ * Each workgroup normalises rows in the kernel's prologue; a reader of a row
+ * waits only for that row's ready word.  Same argument rules, ordering and
+ * error reporting as moe_decode_run; MOE_ERR_INVALID_ARG if set_input_norm has
+ * not been called.  dbg->norm_x, when set, receives xn.
+ */
+moe_status moe_decode_run_block(moe_decode_handle* h, const void* x, int32_t T, void* y,
+                                const moe_decode_debug* dbg, void* hip_stream);
 
 /*
  * Wait for the last run's stream and report its in-kernel status:

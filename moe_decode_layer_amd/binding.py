@@ -25,6 +25,8 @@ EXPORTS = (
     "moe_decode_supported",
     "moe_decode_create",
     "moe_decode_run",
+    "moe_decode_set_input_norm",
+    "moe_decode_run_block",
     "moe_decode_check",
     "moe_decode_destroy",
     "moe_decode_status_string",
@@ -66,6 +68,7 @@ class moe_decode_debug(ctypes.Structure):
         ("trace_blocks", ctypes.c_int32),
         ("trace_cap", ctypes.c_int32),
         ("expire_waits", ctypes.c_int32),
+        ("norm_x", ctypes.c_void_p),
     ]
 
 
@@ -96,6 +99,10 @@ def lib() -> ctypes.CDLL:
                                         ctypes.POINTER(P)]
         L.moe_decode_run.restype = ctypes.c_int32
         L.moe_decode_run.argtypes = [P, P, ctypes.c_int32, P, ctypes.POINTER(moe_decode_debug), P]
+        L.moe_decode_set_input_norm.restype = ctypes.c_int32
+        L.moe_decode_set_input_norm.argtypes = [P, P, ctypes.c_float]
+        L.moe_decode_run_block.restype = ctypes.c_int32
+        L.moe_decode_run_block.argtypes = [P, P, ctypes.c_int32, P, ctypes.POINTER(moe_decode_debug), P]
         L.moe_decode_check.restype = ctypes.c_int32
         L.moe_decode_check.argtypes = [P]
         L.moe_decode_destroy.restype = None
@@ -129,6 +136,16 @@ def moe_decode_run(h, x_ptr: int, T: int, y_ptr: int, dbg: moe_decode_debug | No
                    stream: int) -> int:
     return lib().moe_decode_run(h, x_ptr, T, y_ptr, ctypes.byref(dbg) if dbg is not None else None,
                                 stream)
+
+
+def moe_decode_set_input_norm(h, norm_w_ptr: int, eps: float) -> int:
+    return lib().moe_decode_set_input_norm(h, norm_w_ptr, eps)
+
+
+def moe_decode_run_block(h, x_ptr: int, T: int, y_ptr: int, dbg: moe_decode_debug | None,
+                         stream: int) -> int:
+    return lib().moe_decode_run_block(h, x_ptr, T, y_ptr,
+                                      ctypes.byref(dbg) if dbg is not None else None, stream)
 
 
 def moe_decode_check(h) -> int:
@@ -168,24 +185,46 @@ class MoeDecode:
         self.cfg = cfg
         self.handle = h
 
+    @staticmethod
+    def _debug(debug: dict | None):
+        if not debug:
+            return None
+        tr = debug.get("trace")
+        return moe_decode_debug(_ptr(debug.get("topk_idx")), _ptr(debug.get("topk_w")),
+                                _ptr(debug.get("pair_rank")), _ptr(debug.get("expert_count")),
+                                _ptr(debug.get("logits")), _ptr(tr),
+                                0 if tr is None else tr.shape[0],
+                                0 if tr is None else tr.shape[1] - 1,
+                                int(debug.get("expire_waits", 0)), _ptr(debug.get("norm_x")))
+
     def run(self, x, y, T: int | None = None, debug: dict | None = None, stream=None) -> None:
         """Enqueue one layer call: x [T][H] bf16 -> y [T][H] bf16 (torch tensors)."""
         import torch
         if T is None:
             T = x.shape[0]
-        dbg = None
-        if debug:
-            tr = debug.get("trace")
-            dbg = moe_decode_debug(_ptr(debug.get("topk_idx")), _ptr(debug.get("topk_w")),
-                                   _ptr(debug.get("pair_rank")), _ptr(debug.get("expert_count")),
-                                   _ptr(debug.get("logits")), _ptr(tr),
-                                   0 if tr is None else tr.shape[0],
-                                   0 if tr is None else tr.shape[1] - 1,
-                                   int(debug.get("expire_waits", 0)))
         s = stream if stream is not None else torch.cuda.current_stream()
-        st = moe_decode_run(self.handle, x.data_ptr(), T, y.data_ptr(), dbg, s.cuda_stream)
+        st = moe_decode_run(self.handle, x.data_ptr(), T, y.data_ptr(), self._debug(debug),
+                            s.cuda_stream)
         if st != MOE_OK:
             raise MoeDecodeError("moe_decode_run", st)
+
+    def set_input_norm(self, norm_w, eps: float) -> None:
+        """RMSNorm weight [H] fp32 (torch tensor on the device) and epsilon of block runs."""
+        assert norm_w.is_cuda and norm_w.is_contiguous()
+        st = moe_decode_set_input_norm(self.handle, norm_w.data_ptr(), eps)
+        if st != MOE_OK:
+            raise MoeDecodeError("moe_decode_set_input_norm", st)
+
+    def run_block(self, x, y, T: int | None = None, debug: dict | None = None, stream=None) -> None:
+        """Enqueue one pre-norm block call: y = x + layer(RMSNorm(x)), [T][H] bf16."""
+        import torch
+        if T is None:
+            T = x.shape[0]
+        s = stream if stream is not None else torch.cuda.current_stream()
+        st = moe_decode_run_block(self.handle, x.data_ptr(), T, y.data_ptr(), self._debug(debug),
+                                  s.cuda_stream)
+        if st != MOE_OK:
+            raise MoeDecodeError("moe_decode_run_block", st)
 
     def check(self) -> int:
         return moe_decode_check(self.handle)

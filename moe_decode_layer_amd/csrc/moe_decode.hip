@@ -217,6 +217,13 @@ struct Params {
   FDiv fd_k;           // K: the row of a (row, k) pair index
   int cmb_rows;        // rows per combine item: 8 for wide items with K <= 8 and T >= 128, else 4
   const f32x4* router_wt;  // [ceil(E/16)][H/16][64]: lane (n, kq) holds router row 16 et + n, K 16 s + 4 kq .. + 3
+  // pre-norm block runs: x then points at xn, the normalised rows
+  const uint16_t* x_in;    // [T][H] bf16 block input (the residual stream)
+  const float* norm_w;     // [H] RMSNorm weight
+  uint16_t* xn;            // [T][H] bf16 normalised rows (written by the kernel)
+  int* norm_ready;         // [T] epoch of the run that last wrote each xn row
+  uint16_t* dbg_norm;      // [T][H] copy of xn (nullable)
+  float norm_eps;
 };
 // The kernel reads its parameters in place, from the constant kernel-argument
 // segment, so the compiler can reload a field with a scalar load instead of
@@ -1269,9 +1276,11 @@ __device__ __forceinline__ int down_waves_in_group(KParams& p, int rg) {
 // summed in exactly that order, once every down wave of column group rg has
 // counted in and every expert output read carries this run's epoch.  Each
 // thread computes kOut outputs (R = 2 kOut rows per item) from up to kIn
-// inputs each (K <= kIn - 1 routed ones, the shared one last).
+// inputs each (K <= kIn - 1 routed ones, the shared one last).  RES (pre-norm
+// block runs): y[t] = bf16( x_in[t] + that sum ), the residual added to the
+// unrounded sum.
 // ----------------------------------------------------------------------------
-template <int kOut, int kIn>
+template <int kOut, int kIn, bool RES = false>
 __device__ __forceinline__ bool combine_item(KParams& p, const Lds& L, int rc, int rg, int n_mr) {
   constexpr int kRows = kOut * kThreads / kDownRows;
   constexpr int kSh = kIn - 1;                                // slot of the shared input
@@ -1299,6 +1308,15 @@ __device__ __forceinline__ bool combine_item(KParams& p, const Lds& L, int rc, i
     live[j] = r < nt && c < nc;
     tt[j] = t0 + min(r, nt - 1);
     src[j] = p.o_scr + c0 + min(c, nc - 1);
+  }
+  // the residual, requested before the outputs are polled
+  uint32_t res[kOut];
+  if constexpr (RES) {
+#pragma unroll
+    for (int j = 0; j < kOut; ++j) {
+      const int o = threadIdx.x + kThreads * j;
+      res[j] = ld(p.x_in + (size_t)tt[j] * p.H + c0 + min(o % kDownRows, nc - 1));
+    }
   }
   // scratch row of every input: the K routed outputs, then the shared one
   int row[kOut][kIn];
@@ -1338,6 +1356,7 @@ __device__ __forceinline__ bool combine_item(KParams& p, const Lds& L, int rc, i
 #pragma unroll
     for (int k = 0; k < kSh; ++k)
       if (k < K) acc += L.tkw[tt[j] * K + k] * __uint_as_float((uint32_t)v[j][k]);
+    if constexpr (RES) acc = bf16_to_f32(res[j]) + acc;
     const int o = threadIdx.x + kThreads * j;
     if (live[j]) st(p.y + (size_t)tt[j] * p.H + c0 + o % kDownRows, f32_to_bf16(acc));
   }
@@ -1997,13 +2016,125 @@ __device__ __forceinline__ bool dn_item_wide(KParams& p, const Lds& L, int slot,
 }
 
 // ----------------------------------------------------------------------------
+// Pre-norm block runs: the input RMSNorm in the kernel's prologue, rows handed
+// on one by one as they become ready.  Workgroup g normalises rows g, g + G,
+// ...: xn[t][h] = bf16(x[t][h] r_t gamma[h]), r_t = 1 / sqrt(mean_h x[t][h]^2
+// + eps), the mean in fp32 in a fixed order.  The row goes out with
+// device-scope stores (to the device coherence point, past this XCD's L2);
+// once every wave's stores are acknowledged, thread 0 sets the row's ready
+// word to the run's epoch.  A reader waits for the words of the rows it needs
+// and then reads them with ordinary loads: no L1 or L2 can hold a stale line
+// of a row, since nothing reads it in this run before its word is set and the
+// caches start each kernel clean.  The prologue comes before any wait, so the
+// rows are ready while all workgroups are resident.
+// ----------------------------------------------------------------------------
+constexpr int kNormChunks = 16384 / 8 / kThreads;   // 16-byte words per thread at the largest H
+__device__ __forceinline__ void st_coh64(uint64_t* p, uint64_t v) {
+  __hip_atomic_store((GLOBAL uint64_t*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void norm_rows(KParams& p, SHARED float* red) {
+  const int n8 = p.H / 8;
+  for (int t = blockIdx.x; t < p.T; t += gridDim.x) {
+    const u32x4* src = (const u32x4*)(p.x_in + (size_t)t * p.H);
+    const f32x4* gw = (const f32x4*)p.norm_w;
+    u32x4 v[kNormChunks];
+    f32x4 g[kNormChunks][2];
+#pragma unroll
+    for (int j = 0; j < kNormChunks; ++j) {
+      const int c = (int)threadIdx.x + j * kThreads;
+      if (c < n8) {
+        v[j] = ld(src + c);
+        g[j][0] = ld(gw + 2 * c);
+        g[j][1] = ld(gw + 2 * c + 1);
+      }
+    }
+    float ss = 0.f;
+#pragma unroll
+    for (int j = 0; j < kNormChunks; ++j) {
+      if ((int)threadIdx.x + j * kThreads < n8) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float a = bf16_to_f32(v[j][i] & 0xffffu), b = bf16_to_f32(v[j][i] >> 16);
+          ss = fmaf(a, a, ss);
+          ss = fmaf(b, b, ss);
+        }
+      }
+    }
+    ss = wave_sum(ss);
+    if (lane_id() == 0) red[wave_id()] = ss;
+    __syncthreads();
+    const float tot = (red[0] + red[1]) + (red[2] + red[3]);
+    __syncthreads();                           // the partials area is free again
+    const float r = 1.0f / sqrtf(tot / (float)p.H + p.norm_eps);
+    uint64_t* dst = (uint64_t*)(p.xn + (size_t)t * p.H);
+#pragma unroll
+    for (int j = 0; j < kNormChunks; ++j) {
+      const int c = (int)threadIdx.x + j * kThreads;
+      if (c < n8) {
+        const float gg[8] = {g[j][0].x, g[j][0].y, g[j][0].z, g[j][0].w, g[j][1].x, g[j][1].y, g[j][1].z, g[j][1].w};
+        u32x4 o;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t lo = f32_to_bf16(bf16_to_f32(v[j][i] & 0xffffu) * r * gg[2 * i]);
+          const uint32_t hi = f32_to_bf16(bf16_to_f32(v[j][i] >> 16) * r * gg[2 * i + 1]);
+          o[i] = lo | hi << 16;
+        }
+        st_coh64(dst + 2 * c, (uint64_t)o.y << 32 | o.x);
+        st_coh64(dst + 2 * c + 1, (uint64_t)o.w << 32 | o.z);
+        if (p.dbg_norm) st((u32x4*)(p.dbg_norm + (size_t)t * p.H) + c, o);
+      }
+    }
+    wait_stores();
+    __syncthreads();
+    if (threadIdx.x == 0) store_agent(p.norm_ready + t, (int)p.epoch);
+  }
+}
+
+// Workgroup-wide wait until rows [t0, t0 + n) of xn are ready: the lanes of
+// wave 0 poll one ready word each, under the deadline.  false: deadline
+// passed or another workgroup reported an error.
+__device__ bool wait_rows(KParams& p, int t0, int n, SHARED int* lds_flag) {
+  if ((int)threadIdx.x < kWave) {
+    uint32_t bad = 0;
+    long long t_end = 0;
+    bool timed = false;
+    for (int r = threadIdx.x; r < n && !bad; r += kWave) {
+      int spins = 0;
+      while (load_agent(p.norm_ready + t0 + r) != (int)p.epoch) {
+        if (!timed) {
+          t_end = (long long)wall_clock64() + (p.expire_waits ? 0 : p.deadline_ticks);
+          timed = true;
+        }
+        if ((spins & 7) == 7 && load_agent(p.status) != 0) { bad = 1; break; }
+        if ((long long)wall_clock64() > t_end) {
+          int expected = 0;
+          __hip_atomic_compare_exchange_strong((GLOBAL int*)(p.status), &expected, MOE_ERR_TIMEOUT,
+                                               __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT);
+          bad = 1;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(2);
+        ++spins;
+      }
+    }
+    bad = wave_max_v(bad);
+    if (threadIdx.x == 0) *lds_flag = bad ? 0 : 1;
+  }
+  __syncthreads();
+  const int ok = *lds_flag;
+  __syncthreads();
+  return ok != 0;
+}
+
+// ----------------------------------------------------------------------------
 // The persistent kernel
 // ----------------------------------------------------------------------------
 // FULL: the variant for x in LDS with the full-tile gate/up and down items
 // (H = 64 kFullTiles, I = 32 kFullTiles) and local routing only; the other
 // variants hold the general code.  Each variant carries only the code its
 // batches reach, which keeps register pressure (and spills) down.
-template <int NMBMAX, bool XL, bool FULL, bool WIDE, int NQ2 = kFullTiles / 2>
+template <int NMBMAX, bool XL, bool FULL, bool WIDE, int NQ2 = kFullTiles / 2, bool NORM = false>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(NMBMAX == 1 || WIDE ? 2 : 1))) moe_decode_kernel(Params arg) {
   KParams& p = *(const CONSTANT Params*)__builtin_amdgcn_kernarg_segment_ptr();
   (void)arg;
@@ -2014,9 +2145,16 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
   // Small batch: the whole layer input is kept in LDS, loaded before the
   // first item that reads it (the router reads x from global memory, so the
   // copy overlaps the routing wait).
+  // NORM: x is xn, whose rows are written by the prologue (every read of
+  // it waits for the rows it needs first).
   bool x_staged = !XL;
-  auto ensure_x = [&]() __attribute__((always_inline)) {
-    if (x_staged) return;
+  bool rows_all = !NORM;        // every xn row seen ready by this workgroup
+  auto ensure_x = [&]() __attribute__((always_inline)) -> bool {
+    if (x_staged) return true;
+    if constexpr (NORM) {
+      if (!wait_rows(p, 0, p.T, L.misc + 1)) return false;
+      rows_all = true;
+    }
     const int per_row = p.H / 8;
     batched_copy<u32x4>(
         p.T * per_row, [&](int i) { return ld((const u32x4*)p.x + i); },
@@ -2026,6 +2164,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
         });
     __syncthreads();
     x_staged = true;
+    return true;
   };
   bool routed = false;          // routing and placement are in LDS
   int i_rgu_end = 0, i_sdn_end = 0, i_rdn_end = 0, i_total = 0, n_mr = 0;
@@ -2045,6 +2184,8 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
       store_agent(q + off, 0);
     }
   }
+
+  if constexpr (NORM) norm_rows(p, L.red);
 
   // optional timeline of this workgroup (thread 0 writes it)
   long long* trace = (p.trace && (int)blockIdx.x < p.trace_blocks)
@@ -2196,7 +2337,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
   it = blockIdx.x;
   for (;;) {
     if (!dyn && it >= p.i_pre_end) {
-      ensure_x();
+      if (!ensure_x()) break;
       if (!ensure_routing()) break;
       // every gate/up item is static: a claimed one could be queued behind
       // the busy workgroup that claimed it while an idle one takes a down
@@ -2216,6 +2357,19 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
     t_got = t_ready = tl_clock(p);
     if (it < p.i_router_end) {
       kind = 0;
+      if constexpr (NORM) {
+        // the router item's rows of xn
+        int t0, nt;
+        if (!FULL && p.router_tiles) {
+          const int n_et = (p.E + kRouterTile - 1) / kRouterTile;
+          t0 = (it / p.router_ks / n_et) * kRouterTile;
+          nt = min(kRouterTile, p.T - t0);
+        } else {
+          t0 = (it / p.E) * kRouterRows;
+          nt = min(kRouterRows, p.T - t0);
+        }
+        if (!rows_all && !wait_rows(p, t0, nt, L.misc + 1)) break;
+      }
       if (!FULL && p.router_tiles) {
         if constexpr (!FULL) router_tile_item(p, L, it);
       } else {
@@ -2226,10 +2380,12 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
       }
     } else if (it >= p.i_topk_end && it < p.i_pre_end) {
       kind = 1;
-      ensure_x();
+      if (!ensure_x()) break;
       const int i = it - p.i_topk_end;
       const int mr = i / p.n_gu_mr, rb = i % p.n_gu_mr;
       const int r0 = mr * p.mrange;
+      if constexpr (NORM && !XL)
+        if (!rows_all && !wait_rows(p, r0, min(p.mrange, p.T - r0), L.misc + 1)) break;
       run_gu(p.E, p.T * p.K, r0, min(p.mrange, p.T - r0), rb, true);
     } else if (!FULL && it < p.i_topk_end) {
       kind = 2;
@@ -2238,12 +2394,18 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
       publish_done(p.ctr + kCtrTopkDone, p.n_topk, p.ctr + kCtrTopkGo);
     } else {
       kind = 6;
-      ensure_x();
+      if (!ensure_x()) break;
       if (!ensure_routing()) break;
       t_ready = tl_clock(p);
       if (it >= i_total) break;
       if (it < i_rgu_end) {
         kind = 4;
+        if constexpr (NORM && !XL) {
+          if (!rows_all) {
+            if (!wait_rows(p, 0, p.T, L.misc + 1)) break;
+            rows_all = true;
+          }
+        }
         const int i = it - p.i_pre_end;
         const int m = i / p.n_gu_mr, rb = i % p.n_gu_mr;
         const int e = L.mrlist[m];
@@ -2294,9 +2456,10 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
         const int rc = p.wide ? c % n_rc : c / p.n_rg, rg = p.wide ? c / n_rc : c % p.n_rg;
         bool ok;
         if constexpr (WIDE) {
-          ok = p.cmb_rows == 8 ? combine_item<4, 9>(p, L, rc, rg, n_mr) : combine_item<2, kMaxTopK + 1>(p, L, rc, rg, n_mr);
+          ok = p.cmb_rows == 8 ? combine_item<4, 9, NORM>(p, L, rc, rg, n_mr)
+                               : combine_item<2, kMaxTopK + 1, NORM>(p, L, rc, rg, n_mr);
         } else {
-          ok = combine_item<2, kMaxTopK + 1>(p, L, rc, rg, n_mr);
+          ok = combine_item<2, kMaxTopK + 1, NORM>(p, L, rc, rg, n_mr);
         }
         if (!ok) break;
         t_ready = *(SHARED long long*)(L.misc + 12);
@@ -2407,12 +2570,17 @@ struct moe_decode_handle {
   uint64_t* h_scr = nullptr;
   uint64_t* o_scr = nullptr;
   int* ctr = nullptr;
+  // pre-norm block runs (moe_decode_set_input_norm)
+  float* norm_w = nullptr;       // [H]
+  uint16_t* xn = nullptr;        // [max_tokens][H] bf16
+  int* norm_ready = nullptr;     // [max_tokens]
+  float norm_eps = 0.f;
   uint32_t epoch = 0;            // tag of the last run (0: none yet)
   hipStream_t last_stream = nullptr;
   std::mutex mu;
-  // occupancy cache, by (kernel variant, LDS bytes)
-  int occ_lds[6] = {-1, -1, -1, -1, -1, -1};
-  int occ_blocks[6] = {0, 0, 0, 0, 0, 0};
+  // occupancy cache, by (kernel variant + 6 for block runs, LDS bytes)
+  int occ_lds[12] = {-1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1};
+  int occ_blocks[12] = {};
 };
 
 namespace {
@@ -2593,7 +2761,7 @@ void moe_decode_destroy(moe_decode_handle* h) {
   (void)hipSetDevice(h->device);
   (void)hipDeviceSynchronize();
   void* ptrs[] = {h->router_w, h->router_wt, h->router_b, h->w13p, h->s13p, h->w2p, h->s2p, h->lgt,
-                  h->topk_idx, h->topk_w, h->h_scr, h->o_scr, h->ctr};
+                  h->topk_idx, h->topk_w, h->h_scr, h->o_scr, h->ctr, h->norm_w, h->xn, h->norm_ready};
   for (void* q : ptrs)
     if (q) (void)hipFree(q);
   (void)hipSetDevice(prev);
@@ -2679,9 +2847,15 @@ moe_status moe_decode_create(const moe_decode_config* cfg, const moe_decode_weig
   return MOE_OK;
 }
 
-moe_status moe_decode_run(moe_decode_handle* h, const void* x, int32_t T, void* y,
-                          const moe_decode_debug* dbg, void* hip_stream) {
+}  // extern "C"
+
+namespace {
+
+// One layer call (norm = false) or pre-norm block call (norm = true).
+moe_status run_impl(moe_decode_handle* h, const void* x, int32_t T, void* y,
+                    const moe_decode_debug* dbg, void* hip_stream, bool norm) {
   if (!h) return MOE_ERR_INVALID_ARG;
+  if (norm && !h->xn) return MOE_ERR_INVALID_ARG;
   if (T < 0 || T > h->cfg.max_tokens) return MOE_ERR_INVALID_ARG;
   if (T == 0) return MOE_OK;
   if (!x || !y) return MOE_ERR_INVALID_ARG;
@@ -2693,6 +2867,15 @@ moe_status moe_decode_run(moe_decode_handle* h, const void* x, int32_t T, void* 
   Params p = make_params(h, T);
   p.x = (const uint16_t*)x;
   p.y = (uint16_t*)y;
+  if (norm) {
+    p.x_in = (const uint16_t*)x;
+    p.x = h->xn;
+    p.xn = h->xn;
+    p.norm_w = h->norm_w;
+    p.norm_ready = h->norm_ready;
+    p.norm_eps = h->norm_eps;
+    if (dbg) p.dbg_norm = (uint16_t*)dbg->norm_x;
+  }
   if (dbg) {
     p.dbg_idx = dbg->topk_idx;
     p.dbg_w = dbg->topk_w;
@@ -2720,7 +2903,8 @@ moe_status moe_decode_run(moe_decode_handle* h, const void* x, int32_t T, void* 
     if (hipMemsetAsync(h->lgt, 0, h->lgt_bytes, stream) != hipSuccess ||
         hipMemsetAsync(h->h_scr, 0, rows * (c.intermediate / 2) * 8, stream) != hipSuccess ||
         hipMemsetAsync(h->o_scr, 0, rows * c.hidden * 8, stream) != hipSuccess ||
-        hipMemsetAsync(h->ctr, 0, 2 * (size_t)kCtrHead * 4, stream) != hipSuccess) {
+        hipMemsetAsync(h->ctr, 0, 2 * (size_t)kCtrHead * 4, stream) != hipSuccess ||
+        (h->norm_ready && hipMemsetAsync(h->norm_ready, 0, (size_t)c.max_tokens * 4, stream) != hipSuccess)) {
       if (prev != h->device) (void)hipSetDevice(prev);
       return MOE_ERR_HIP;
     }
@@ -2740,23 +2924,35 @@ moe_status moe_decode_run(moe_decode_handle* h, const void* x, int32_t T, void* 
   const bool full = p.xs_stride > 0 && p.hs_stride > 0 && p.n_q13 == 4 * kFullTiles &&
                     (p.n_q2 == kFullTiles / 2 || p.n_q2 == kFullTiles / 2 + 1) && p.local_topk && !p.router_tiles;
   const int variant = p.wide ? 4 : full ? (p.n_q2 == kFullTiles / 2 ? 3 : 5) : p.xs_stride > 0 ? 0 : (T > kMBlock ? 2 : 1);
-  const void* fn = variant == 4   ? (const void*)moe_decode_kernel<2, false, false, true>
-                   : variant == 3 ? (const void*)moe_decode_kernel<1, true, true, false>
-                   : variant == 5 ? (const void*)moe_decode_kernel<1, true, true, false, kFullTiles / 2 + 1>
-                   : variant == 0 ? (const void*)moe_decode_kernel<1, true, false, false>
-                   : variant == 1 ? (const void*)moe_decode_kernel<1, false, false, false>
-                                  : (const void*)moe_decode_kernel<4, false, false, false>;
-  if (h->occ_lds[variant] != p.lds_bytes) {
+  const void* fn;
+  if (!norm) {
+    fn = variant == 4   ? (const void*)moe_decode_kernel<2, false, false, true>
+         : variant == 3 ? (const void*)moe_decode_kernel<1, true, true, false>
+         : variant == 5 ? (const void*)moe_decode_kernel<1, true, true, false, kFullTiles / 2 + 1>
+         : variant == 0 ? (const void*)moe_decode_kernel<1, true, false, false>
+         : variant == 1 ? (const void*)moe_decode_kernel<1, false, false, false>
+                        : (const void*)moe_decode_kernel<4, false, false, false>;
+  } else {
+    constexpr int q = kFullTiles / 2;
+    fn = variant == 4   ? (const void*)moe_decode_kernel<2, false, false, true, q, true>
+         : variant == 3 ? (const void*)moe_decode_kernel<1, true, true, false, q, true>
+         : variant == 5 ? (const void*)moe_decode_kernel<1, true, true, false, q + 1, true>
+         : variant == 0 ? (const void*)moe_decode_kernel<1, true, false, false, q, true>
+         : variant == 1 ? (const void*)moe_decode_kernel<1, false, false, false, q, true>
+                        : (const void*)moe_decode_kernel<4, false, false, false, q, true>;
+  }
+  const int slot = variant + (norm ? 6 : 0);
+  if (h->occ_lds[slot] != p.lds_bytes) {
     int nb = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fn, kThreads, p.lds_bytes) != hipSuccess ||
         nb < 1) {
       if (prev != h->device) (void)hipSetDevice(prev);
       return MOE_ERR_HIP;
     }
-    h->occ_lds[variant] = p.lds_bytes;
-    h->occ_blocks[variant] = nb;
+    h->occ_lds[slot] = p.lds_bytes;
+    h->occ_blocks[slot] = nb;
   }
-  const int grid = h->n_cu * h->occ_blocks[variant];
+  const int grid = h->n_cu * h->occ_blocks[slot];
   // The grid is sized to what the device holds at once, so all workgroups
   // are resident together on an otherwise idle device; every wait has a
   // deadline for the case where they are not.
@@ -2765,6 +2961,55 @@ moe_status moe_decode_run(moe_decode_handle* h, const void* x, int32_t T, void* 
   h->last_stream = stream;
   if (prev != h->device) (void)hipSetDevice(prev);
   return err == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_decode_run(moe_decode_handle* h, const void* x, int32_t T, void* y,
+                          const moe_decode_debug* dbg, void* hip_stream) {
+  return run_impl(h, x, T, y, dbg, hip_stream, false);
+}
+
+moe_status moe_decode_set_input_norm(moe_decode_handle* h, const float* norm_w, float eps) {
+  if (!h || !norm_w || !(eps > 0.f && eps < 1e30f)) return MOE_ERR_INVALID_ARG;
+  std::lock_guard<std::mutex> lock(h->mu);
+  int prev = 0;
+  HIP_TRY(hipGetDevice(&prev));
+  if (prev != h->device) HIP_TRY(hipSetDevice(h->device));
+  moe_status rc = MOE_OK;
+  const size_t H = h->cfg.hidden, Tm = h->cfg.max_tokens;
+  do {
+    // earlier runs may still read the weight being replaced
+    if (h->last_stream != nullptr && hipStreamSynchronize(h->last_stream) != hipSuccess) { rc = MOE_ERR_HIP; break; }
+    if (!h->xn) {
+      if (hipMalloc((void**)&h->norm_w, H * 4) != hipSuccess ||
+          hipMalloc((void**)&h->xn, Tm * H * 2) != hipSuccess ||
+          hipMalloc((void**)&h->norm_ready, Tm * 4) != hipSuccess) {
+        rc = MOE_ERR_OUT_OF_MEMORY;
+      } else if (hipMemset(h->norm_ready, 0, Tm * 4) != hipSuccess) {
+        rc = MOE_ERR_HIP;
+      }
+      if (rc != MOE_OK) {
+        for (void* q : {(void*)h->norm_w, (void*)h->xn, (void*)h->norm_ready})
+          if (q) (void)hipFree(q);
+        h->norm_w = nullptr;
+        h->xn = nullptr;
+        h->norm_ready = nullptr;
+        break;
+      }
+    }
+    if (hipMemcpy(h->norm_w, norm_w, H * 4, hipMemcpyDeviceToDevice) != hipSuccess) { rc = MOE_ERR_HIP; break; }
+    h->norm_eps = eps;
+  } while (0);
+  if (prev != h->device) (void)hipSetDevice(prev);
+  return rc;
+}
+
+moe_status moe_decode_run_block(moe_decode_handle* h, const void* x, int32_t T, void* y,
+                                const moe_decode_debug* dbg, void* hip_stream) {
+  return run_impl(h, x, T, y, dbg, hip_stream, true);
 }
 
 moe_status moe_decode_check(moe_decode_handle* h) {

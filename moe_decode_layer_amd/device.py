@@ -40,6 +40,8 @@ def make_layer(inp: Inputs, max_tokens: int | None = None, device: int = 0,
     w = upload_weights(inp, dev)
     cfg = binding.make_config(max_tokens or wl.T, wl.H, wl.E, wl.K, wl.I, wl.S, deadline_us)
     layer = binding.MoeDecode(cfg, w, device)
+    if wl.prenorm:
+        layer.set_input_norm(to_device(inp.norm_w, dev), wl.norm_eps)
     if free_weights:
         del w
         torch.cuda.empty_cache()
@@ -57,14 +59,20 @@ def debug_buffers(T: int, E: int, K: int, dev) -> dict:
 
 
 def run_once(layer: binding.MoeDecode, x_bits: np.ndarray, E: int, K: int, device: int = 0,
-             debug: bool = True) -> dict:
-    """One synchronous call; returns y (bf16 bits, uint16) and the debug copies."""
+             debug: bool = True, block: bool = False) -> dict:
+    """One synchronous call (a pre-norm block call with ``block``); returns y
+    (bf16 bits, uint16) and the debug copies."""
     dev = torch.device("cuda", device)
     T, H = x_bits.shape
     x = to_device(x_bits, dev)
     y = torch.full((T, H), -1, dtype=torch.int16, device=dev)
     dbg = debug_buffers(T, E, K, dev) if debug else None
-    layer.run(x, y, T, dbg)
+    if block:
+        if dbg is not None:
+            dbg["norm_x"] = torch.full((T, H), -1, dtype=torch.int16, device=dev)
+        layer.run_block(x, y, T, dbg)
+    else:
+        layer.run(x, y, T, dbg)
     st = layer.check()
     if st != binding.MOE_OK:
         raise binding.MoeDecodeError("moe_decode_check", st)
@@ -72,4 +80,6 @@ def run_once(layer: binding.MoeDecode, x_bits: np.ndarray, E: int, K: int, devic
     if dbg:
         for k, v in dbg.items():
             out[k] = v.cpu().numpy()
+        if "norm_x" in out:
+            out["norm_x"] = out["norm_x"].view(np.uint16)
     return out

@@ -57,7 +57,7 @@ def run(workload: str, calls: int) -> None:
     scrub = torch.ones(1 << 28, dtype=torch.int32, device=dev)
     for _ in range(calls):
         scrub.amax()
-        layer.run(x, y, wl.T)
+        (layer.run_block if wl.prenorm else layer.run)(x, y, wl.T)
     torch.cuda.synchronize()
     assert layer.check() == 0
     src = torch.ones(COPY_BYTES // 4, dtype=torch.int32, device=dev)

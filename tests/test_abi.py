@@ -29,7 +29,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert binding.moe_decode_abi_version() == 1
+    assert binding.moe_decode_abi_version() == 2
     for st in range(6):
         assert binding.moe_decode_status_string(st) != "unknown status"
     assert binding.moe_decode_status_string(99) == "unknown status"
@@ -77,5 +77,13 @@ def test_null_arguments_are_rejected_before_any_device_call():
     assert L.moe_decode_create(ctypes.byref(bad), ctypes.byref(w), 0, ctypes.byref(h)) == \
         binding.MOE_ERR_UNSUPPORTED
     assert L.moe_decode_run(None, None, 1, None, None, None) == binding.MOE_ERR_INVALID_ARG
+    assert L.moe_decode_run_block(None, None, 1, None, None, None) == binding.MOE_ERR_INVALID_ARG
+    assert L.moe_decode_set_input_norm(None, None, 1e-6) == binding.MOE_ERR_INVALID_ARG
     assert L.moe_decode_check(None) == binding.MOE_ERR_INVALID_ARG
     L.moe_decode_destroy(None)
+
+
+def test_debug_struct_layout_matches_the_header():
+    # the pointer appended for block runs sits after the three int32 fields
+    assert binding.moe_decode_debug.norm_x.offset == 6 * 8 + 3 * 4 + 4
+    assert ctypes.sizeof(binding.moe_decode_debug) == 6 * 8 + 3 * 4 + 4 + 8
