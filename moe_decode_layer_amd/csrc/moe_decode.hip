@@ -873,6 +873,10 @@ __device__ __forceinline__ void router_tile_item(KParams& p, const Lds& L, int i
 // With stage_x (the item covers every row), the x values it loads are also
 // written to the workgroup's LDS copy of x, which later items read.
 // Returns (timeline only) when this workgroup's partial sums were complete.
+// NORM (pre-norm block runs): x is xn; the first pass's weights are
+// requested before the wait for the item's rows.  LLONG_MIN: the wait failed.
+__device__ bool wait_rows(KParams& p, int t0, int n, SHARED int* lds_flag);
+template <bool NORM = false>
 __device__ __forceinline__ long long router_item(KParams& p, const Lds& L, int item, bool stage_x) {
   const int w = wave_id(), lane = lane_id();
   const int e = item % p.E;
@@ -898,6 +902,9 @@ __device__ __forceinline__ long long router_item(KParams& p, const Lds& L, int i
     u32x4 xv[kRouterRows][2];
 #pragma unroll
     for (int i = 0; i < 4; ++i) wv[i] = ld(wr + 4 * c + i);
+    if constexpr (NORM) {
+      if (c0 == 0 && !wait_rows(p, t0, nt, L.misc + 1)) return LLONG_MIN;
+    }
 #pragma unroll
     for (int j = 0; j < kRouterRows; ++j) {
       xv[j][0] = ld(xg[j] + 2 * c);
@@ -2017,8 +2024,8 @@ __device__ __forceinline__ bool dn_item_wide(KParams& p, const Lds& L, int slot,
 
 // ----------------------------------------------------------------------------
 // Pre-norm block runs: the input RMSNorm in the kernel's prologue, rows handed
-// on one by one as they become ready.  Workgroup g normalises rows g, g + G,
-// ...: xn[t][h] = bf16(x[t][h] r_t gamma[h]), r_t = 1 / sqrt(mean_h x[t][h]^2
+// on one by one as they become ready.  Workgroup G - 1 - g normalises rows g,
+// g + G, ...: xn[t][h] = bf16(x[t][h] r_t gamma[h]), r_t = 1 / sqrt(mean_h x[t][h]^2
 // + eps), the mean in fp32 in a fixed order.  The row goes out with
 // device-scope stores (to the device coherence point, past this XCD's L2);
 // once every wave's stores are acknowledged, thread 0 sets the row's ready
@@ -2034,7 +2041,9 @@ __device__ __forceinline__ void st_coh64(uint64_t* p, uint64_t v) {
 }
 __device__ __forceinline__ void norm_rows(KParams& p, SHARED float* red) {
   const int n8 = p.H / 8;
-  for (int t = blockIdx.x; t < p.T; t += gridDim.x) {
+  // the last workgroups take the rows: the first ones start the router items,
+  // which wait for every row anyway
+  for (int t = gridDim.x - 1 - blockIdx.x; t < p.T; t += gridDim.x) {
     const u32x4* src = (const u32x4*)(p.x_in + (size_t)t * p.H);
     const f32x4* gw = (const f32x4*)p.norm_w;
     u32x4 v[kNormChunks];
@@ -2357,25 +2366,20 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
     t_got = t_ready = tl_clock(p);
     if (it < p.i_router_end) {
       kind = 0;
-      if constexpr (NORM) {
-        // the router item's rows of xn
-        int t0, nt;
-        if (!FULL && p.router_tiles) {
-          const int n_et = (p.E + kRouterTile - 1) / kRouterTile;
-          t0 = (it / p.router_ks / n_et) * kRouterTile;
-          nt = min(kRouterTile, p.T - t0);
-        } else {
-          t0 = (it / p.E) * kRouterRows;
-          nt = min(kRouterRows, p.T - t0);
-        }
-        if (!rows_all && !wait_rows(p, t0, nt, L.misc + 1)) break;
+      if (NORM && !FULL && p.router_tiles) {
+        // the router tile's rows of xn (small router items wait inside,
+        // after requesting their first weights)
+        const int n_et = (p.E + kRouterTile - 1) / kRouterTile;
+        const int t0 = (it / p.router_ks / n_et) * kRouterTile;
+        if (!rows_all && !wait_rows(p, t0, min(kRouterTile, p.T - t0), L.misc + 1)) break;
       }
       if (!FULL && p.router_tiles) {
         if constexpr (!FULL) router_tile_item(p, L, it);
       } else {
         // a small batch's router item reads all of x: it fills the LDS copy too
         const bool stage = !x_staged && p.T <= kRouterRows;
-        t_ready = router_item(p, L, it, stage);
+        t_ready = router_item<NORM>(p, L, it, stage);
+        if (NORM && t_ready == LLONG_MIN) break;
         x_staged = x_staged || stage;
       }
     } else if (it >= p.i_topk_end && it < p.i_pre_end) {
