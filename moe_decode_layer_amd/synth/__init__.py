@@ -54,6 +54,8 @@ class Workload:
     # from ``norm_weight``) before the layer and added back to its output
     prenorm: bool = False
     norm_eps: float = 1e-6
+    # clipped SwiGLU limit (None: no clipping)
+    swiglu_limit: float | None = None
 
     @property
     def router_std(self) -> float:

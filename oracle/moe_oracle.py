@@ -34,7 +34,11 @@ definitions, else the plainest reading):
     renormalised to sum to 1.
   * top-k order: score descending, ties to the lower expert id.
   * SwiGLU: h = silu(g) * u with silu(g) = g * sigmoid(g); gate rows come
-    first in the fused gate/up matrix; no clipping.
+    first in the fused gate/up matrix.  Clipped SwiGLU ("Beyond Day-0 ...",
+    section 3.1, Marlin MoE bullet; no formula or constant given): with a
+    caller's limit L, h = silu(min(g, L)) * clamp(u, -L, L), the gate capped
+    from above only (silu is bounded below), the rounding of h unchanged;
+    no clipping without a limit.
   * h is rounded to bf16 (nearest even) before the down projection.
   * y = shared + sum_k w_k * o_k in that order, rounded to bf16 from fp64.
   * FP8 is OCP e4m3fn (bias 7, max 448, S.1111.111 is NaN, no infinities);
@@ -189,13 +193,17 @@ def place(idx: np.ndarray, E: int) -> Placement:
 # --------------------------------------------------------------------------
 # Expert FFN and combine
 # --------------------------------------------------------------------------
-def expert_ffn(X: np.ndarray, w13q, s13, w2q, s2) -> np.ndarray:
+def expert_ffn(X: np.ndarray, w13q, s13, w2q, s2, limit=None) -> np.ndarray:
     """One expert on rows X [n][H]: g/u from the fused gate/up matrix (gate
-    rows [0, I), up rows [I, 2I)), h = bf16(silu(g) * u), o = h @ W2^T."""
+    rows [0, I), up rows [I, 2I)), h = bf16(silu(g) * u), o = h @ W2^T.
+    With a limit L: g -> min(g, L), u -> clamp(u, -L, L) first."""
     I = w13q.shape[0] // 2
     W13 = dequant(w13q, s13)
     g = X @ W13[:I].T
     u = X @ W13[I:].T
+    if limit is not None:
+        g = np.minimum(g, float(limit))
+        u = np.clip(u, -float(limit), float(limit))
     h = bf16_round(g * sigmoid(g) * u)
     return h @ dequant(w2q, s2).T
 
@@ -236,7 +244,8 @@ def forward(inp, rows=None) -> Result:
         if S:
             need.setdefault(E, []).append(int(t))
     for e, ts in need.items():
-        out = expert_ffn(X[ts], inp.w13[e], inp.s13[e], inp.w2[e], inp.s2[e])
+        out = expert_ffn(X[ts], inp.w13[e], inp.s13[e], inp.w2[e], inp.s2[e],
+                         getattr(wl, "swiglu_limit", None))
         for i, t in enumerate(ts):
             o[(t, e)] = out[i]
     y = np.zeros((len(rows), H), np.float64)
