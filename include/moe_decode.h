@@ -11,10 +11,13 @@
  *                  without a sort (per-expert row bitmaps + population counts)
  *   per selected expert e (and the shared expert, slot E, for every row):
  *       g = W_gate[e] x,  u = W_up[e] x,  h = bf16(silu(g) * u),  o_e = W_down[e] h
+ *       (g and u clipped first when a limit is set: moe_decode_set_swiglu_limit)
  *       (FP8 e4m3fn weights, one fp32 scale per 32 contiguous K elements)
  *   y[t] = bf16( o_shared[t] + sum_k w[t][k] * o_{idx[t][k]}[t] )
  *
- * in ONE persistent kernel launch.  Sources (page titles and sections):
+ * in ONE persistent kernel launch (moe_decode_run_block runs the same layer as a
+ * pre-norm block: input RMSNorm before it, residual added after it, same
+ * launch).  Sources (page titles and sections):
  *   - "SGLang's Low-Latency Mode Boosts DeepSeek-V4.1-Flash Speed by 1.56x on
  *     AMD": section "NVIDIA overlaps the dependency chain" (routing without
  *     sorting: 8-row tiles, bitmap and population counts, top-k preserved);
@@ -196,6 +199,18 @@ moe_status moe_decode_set_input_norm(moe_decode_handle* h, const float* norm_w, 
  */
 moe_status moe_decode_run_block(moe_decode_handle* h, const void* x, int32_t T, void* y,
                                 const moe_decode_debug* dbg, void* hip_stream);
+
+/*
+ * Clipped SwiGLU, for the runs enqueued after this call (both forms):
+ *   h = bf16( silu(min(g, L)) * clamp(u, -L, L) )
+ * for every expert, routed and shared, with the rounding of h unchanged.
+ * Source: "Beyond Day-0: Optimizing DeepSeek-V4.1 Flash in SGLang", section
+ * 3.1 (fused clipped SwiGLU that keeps the original intermediate rounding;
+ * the page gives neither the formula nor the limit, so the caller supplies L).
+ * L > 0; L = +inf (the default) turns clipping off.  MOE_ERR_INVALID_ARG
+ * for a NULL handle, L <= 0 or NaN.  No device work.
+ */
+moe_status moe_decode_set_swiglu_limit(moe_decode_handle* h, float limit);
 
 /*
  * Wait for the last run's stream and report its in-kernel status:

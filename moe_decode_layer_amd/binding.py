@@ -27,6 +27,7 @@ EXPORTS = (
     "moe_decode_run",
     "moe_decode_set_input_norm",
     "moe_decode_run_block",
+    "moe_decode_set_swiglu_limit",
     "moe_decode_check",
     "moe_decode_destroy",
     "moe_decode_status_string",
@@ -103,6 +104,8 @@ def lib() -> ctypes.CDLL:
         L.moe_decode_set_input_norm.argtypes = [P, P, ctypes.c_float]
         L.moe_decode_run_block.restype = ctypes.c_int32
         L.moe_decode_run_block.argtypes = [P, P, ctypes.c_int32, P, ctypes.POINTER(moe_decode_debug), P]
+        L.moe_decode_set_swiglu_limit.restype = ctypes.c_int32
+        L.moe_decode_set_swiglu_limit.argtypes = [P, ctypes.c_float]
         L.moe_decode_check.restype = ctypes.c_int32
         L.moe_decode_check.argtypes = [P]
         L.moe_decode_destroy.restype = None
@@ -146,6 +149,10 @@ def moe_decode_run_block(h, x_ptr: int, T: int, y_ptr: int, dbg: moe_decode_debu
                          stream: int) -> int:
     return lib().moe_decode_run_block(h, x_ptr, T, y_ptr,
                                       ctypes.byref(dbg) if dbg is not None else None, stream)
+
+
+def moe_decode_set_swiglu_limit(h, limit: float) -> int:
+    return lib().moe_decode_set_swiglu_limit(h, limit)
 
 
 def moe_decode_check(h) -> int:
@@ -214,6 +221,12 @@ class MoeDecode:
         st = moe_decode_set_input_norm(self.handle, norm_w.data_ptr(), eps)
         if st != MOE_OK:
             raise MoeDecodeError("moe_decode_set_input_norm", st)
+
+    def set_swiglu_limit(self, limit: float) -> None:
+        """Clipped SwiGLU limit of later runs (+inf: no clipping)."""
+        st = moe_decode_set_swiglu_limit(self.handle, limit)
+        if st != MOE_OK:
+            raise MoeDecodeError("moe_decode_set_swiglu_limit", st)
 
     def run_block(self, x, y, T: int | None = None, debug: dict | None = None, stream=None) -> None:
         """Enqueue one pre-norm block call: y = x + layer(RMSNorm(x)), [T][H] bf16."""

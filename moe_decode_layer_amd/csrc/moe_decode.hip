@@ -224,6 +224,7 @@ struct Params {
   int* norm_ready;         // [T] epoch of the run that last wrote each xn row
   uint16_t* dbg_norm;      // [T][H] copy of xn (nullable)
   float norm_eps;
+  float swiglu_limit;      // clipped SwiGLU: g -> min(g, L), u -> clamp(u, -L, L); +inf: no clip
 };
 // The kernel reads its parameters in place, from the constant kernel-argument
 // segment, so the compiler can reload a field with a scalar load instead of
@@ -1485,7 +1486,8 @@ __device__ __forceinline__ void gu_item(KParams& p, const Lds& L, int slot, int 
     for (int i = 0; i < 4; ++i) {
       const float g = s[i];
       const float u = dpp<kDppRowRor8>(s[i]);
-      const uint32_t hb = f32_to_bf16(g / (1.0f + __expf(-g)) * u);
+      const float gc = fminf(g, p.swiglu_limit), uc = fminf(fmaxf(u, -p.swiglu_limit), p.swiglu_limit);
+      const uint32_t hb = f32_to_bf16(gc / (1.0f + __expf(-gc)) * uc);
       const uint32_t hb_next = dpp<kDppRowShl1>(hb);          // column n + 1
       const int r = mb * kMBlock + 4 * kq + i;
       if (n < 8 && (n & 1) == 0 && r < nrows)
@@ -1682,7 +1684,8 @@ __device__ __forceinline__ void gu_item_full(KParams& p, const Lds& L, int slot,
     for (int i = 0; i < 4; ++i) {
       const float g = s[i];
       const float u = dpp<kDppRowRor8>(s[i]);
-      const uint32_t hb = f32_to_bf16(g / (1.0f + __expf(-g)) * u);
+      const float gc = fminf(g, p.swiglu_limit), uc = fminf(fmaxf(u, -p.swiglu_limit), p.swiglu_limit);
+      const uint32_t hb = f32_to_bf16(gc / (1.0f + __expf(-gc)) * uc);
       const uint32_t hb_next = dpp<kDppRowShl1>(hb);
       const int r = 4 * kq + i;
       if (n < 8 && (n & 1) == 0 && r < nrows)
@@ -1907,7 +1910,8 @@ __device__ __forceinline__ void gu_item_wide(KParams& p, const Lds& L, int slot,
       for (int i = 0; i < 4; ++i) {
         const float g = s[i];
         const float u = dpp<kDppRowRor8>(s[i]);
-        const uint32_t hb = f32_to_bf16(g / (1.0f + __expf(-g)) * u);
+        const float gc = fminf(g, p.swiglu_limit), uc = fminf(fmaxf(u, -p.swiglu_limit), p.swiglu_limit);
+        const uint32_t hb = f32_to_bf16(gc / (1.0f + __expf(-gc)) * uc);
         const uint32_t hb_next = dpp<kDppRowShl1>(hb);          // column n + 1
         const int r = mb * kMBlock + 4 * kq + i;
         if (n < 8 && (n & 1) == 0 && r < nrows)
@@ -2579,6 +2583,7 @@ struct moe_decode_handle {
   uint16_t* xn = nullptr;        // [max_tokens][H] bf16
   int* norm_ready = nullptr;     // [max_tokens]
   float norm_eps = 0.f;
+  float swiglu_limit = INFINITY; // moe_decode_set_swiglu_limit
   uint32_t epoch = 0;            // tag of the last run (0: none yet)
   hipStream_t last_stream = nullptr;
   std::mutex mu;
@@ -2636,6 +2641,7 @@ Params make_params(const moe_decode_handle* h, int T) {
   p.status = h->ctr + 2 * (size_t)kCtrHead;
   const long long dl = c.deadline_us > 0 ? c.deadline_us : 1000000;
   p.deadline_ticks = dl * 100;   // wall clock runs at 100 MHz
+  p.swiglu_limit = h->swiglu_limit;
   p.router_tiles = T > kMBlock ? 1 : 0;
   p.local_topk = p.router_tiles ? 0 : 1;
   p.n_rb13 = p.I / 8;
@@ -3014,6 +3020,13 @@ moe_status moe_decode_set_input_norm(moe_decode_handle* h, const float* norm_w, 
 moe_status moe_decode_run_block(moe_decode_handle* h, const void* x, int32_t T, void* y,
                                 const moe_decode_debug* dbg, void* hip_stream) {
   return run_impl(h, x, T, y, dbg, hip_stream, true);
+}
+
+moe_status moe_decode_set_swiglu_limit(moe_decode_handle* h, float limit) {
+  if (!h || !(limit > 0.f)) return MOE_ERR_INVALID_ARG;   // NaN fails the test too
+  std::lock_guard<std::mutex> lock(h->mu);
+  h->swiglu_limit = limit;
+  return MOE_OK;
 }
 
 moe_status moe_decode_check(moe_decode_handle* h) {

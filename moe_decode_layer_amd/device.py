@@ -42,6 +42,8 @@ def make_layer(inp: Inputs, max_tokens: int | None = None, device: int = 0,
     layer = binding.MoeDecode(cfg, w, device)
     if wl.prenorm:
         layer.set_input_norm(to_device(inp.norm_w, dev), wl.norm_eps)
+    if wl.swiglu_limit is not None:
+        layer.set_swiglu_limit(wl.swiglu_limit)
     if free_weights:
         del w
         torch.cuda.empty_cache()

@@ -79,6 +79,7 @@ def test_null_arguments_are_rejected_before_any_device_call():
     assert L.moe_decode_run(None, None, 1, None, None, None) == binding.MOE_ERR_INVALID_ARG
     assert L.moe_decode_run_block(None, None, 1, None, None, None) == binding.MOE_ERR_INVALID_ARG
     assert L.moe_decode_set_input_norm(None, None, 1e-6) == binding.MOE_ERR_INVALID_ARG
+    assert L.moe_decode_set_swiglu_limit(None, 1.0) == binding.MOE_ERR_INVALID_ARG
     assert L.moe_decode_check(None) == binding.MOE_ERR_INVALID_ARG
     L.moe_decode_destroy(None)
 
