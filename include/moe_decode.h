@@ -161,7 +161,10 @@ moe_status moe_decode_create(const moe_decode_config* cfg, const moe_decode_weig
  * [T][H] bf16, 16-byte aligned, not overlapping; dbg may be NULL.  T = 0 is a
  * no-op.  Asynchronous: no allocation, no host synchronisation, one kernel
  * launch.  Runs on one handle must be ordered on one stream (they share the
- * workspace).  A wait that passes the deadline makes the kernel exit early
+ * workspace).  Each call gives its launch a fresh run tag, which every
+ * hand-off inside the kernel is checked against; a graph that captured a
+ * call would replay the same tag and accept the previous replay's words, so
+ * captured calls must not be replayed: call this function for every run.  A wait that passes the deadline makes the kernel exit early
  * (y is then undefined) and is reported by moe_decode_check.
  */
 moe_status moe_decode_run(moe_decode_handle* h, const void* x, int32_t T, void* y,
