@@ -164,8 +164,9 @@ moe_status moe_decode_create(const moe_decode_config* cfg, const moe_decode_weig
  * workspace).  Each call gives its launch a fresh run tag, which every
  * hand-off inside the kernel is checked against; a graph that captured a
  * call would replay the same tag and accept the previous replay's words, so
- * captured calls must not be replayed: call this function for every run.  A wait that passes the deadline makes the kernel exit early
- * (y is then undefined) and is reported by moe_decode_check.
+ * captured calls must not be replayed: call this function for every run.
+ * A wait that passes the deadline makes the kernel exit early (y is then
+ * undefined) and is reported by moe_decode_check.
  */
 moe_status moe_decode_run(moe_decode_handle* h, const void* x, int32_t T, void* y,
                           const moe_decode_debug* dbg, void* hip_stream);
