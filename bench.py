@@ -11,6 +11,8 @@ reduction over a scratch tensor) evicts the weights from L2 and the 256 MB
 Infinity Cache and leaves them holding clean lines, as the read-only weights
 of the layers in between would; so each call streams its experts from HBM.
 Each step is bracketed by HIP events on the stream the kernel is launched on.
+The other workloads time the same way; a ``*_prenorm`` workload times the
+pre-norm block form (input RMSNorm + layer + residual, still one launch).
 
 Prints one JSON line: value = expert-weight bytes (FP8 + fp32 group scales of
 every touched expert, each read once) / mean latency, as GB/s; the roofline
