@@ -37,6 +37,12 @@
 // (tagged words), so a producer never waits for its own stores: it bumps a
 // counter and moves on.
 //
+// Pre-norm block runs (the NORM instantiations) add a prologue before the
+// list: the input RMSNorm, one row per workgroup, each row handed on by a
+// ready word (norm_rows, wait_rows); the combine then adds the residual.
+// Clipped SwiGLU caps g and clamps u at a caller-set limit in every gate/up
+// epilogue (+inf by default).
+//
 // Expert weights are re-laid out once, at create time, into 1 KiB tiles of
 // 16 weight rows x 64 K: lane l of a wave reads bytes [16 l, 16 l + 16) of a
 // tile, so every wave-wide weight load is one contiguous KiB.  Lane l =
