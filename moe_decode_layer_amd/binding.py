@@ -190,7 +190,46 @@ class MoeDecode:
         if st != MOE_OK:
             raise MoeDecodeError("moe_decode_create", st)
         self.cfg = cfg
+        self.device = device
         self.handle = h
+
+    def _check_rows(self, name: str, t, T: int) -> None:
+        """x and y: 2-byte elements, contiguous, on the handle's device, at
+        least T rows of H.  A short or misplaced buffer would make the kernel
+        read or write past it, so the call is refused here instead."""
+        if t is None:
+            raise ValueError(f"{name} is required")
+        if t.element_size() != 2 or not t.is_cuda or t.device.index != self.device:
+            raise ValueError(f"{name}: need a 2-byte (bf16) tensor on cuda:{self.device}, "
+                             f"got {t.dtype} on {t.device}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        if t.numel() < T * self.cfg.hidden:
+            raise ValueError(f"{name} holds {t.numel()} elements, fewer than T*H = "
+                             f"{T} * {self.cfg.hidden}")
+
+    def _check_debug(self, debug: dict | None, T: int) -> None:
+        """Each debug buffer is contiguous, on the device, with 4-byte (or,
+        for norm_x, 2-byte; trace: 8-byte) elements, at least as large as
+        its field needs."""
+        if not debug:
+            return
+        K, E, H = self.cfg.top_k, self.cfg.num_experts, self.cfg.hidden
+        need = {"topk_idx": (T * K, 4), "topk_w": (T * K, 4), "pair_rank": (T * K, 4),
+                "expert_count": (E, 4), "logits": (T * E, 4), "norm_x": (T * H, 2)}
+        for name, (n, size) in need.items():
+            t = debug.get(name)
+            if t is None:
+                continue
+            if (not t.is_cuda or t.device.index != self.device or not t.is_contiguous()
+                    or t.element_size() != size or t.numel() < n):
+                raise ValueError(f"debug buffer {name}: need >= {n} contiguous {size}-byte "
+                                 f"elements on cuda:{self.device}")
+        tr = debug.get("trace")
+        if tr is not None:
+            if (not tr.is_cuda or tr.device.index != self.device or not tr.is_contiguous()
+                    or tr.element_size() != 8 or tr.dim() != 3 or tr.shape[1] < 2 or tr.shape[2] != 4):
+                raise ValueError("debug trace: need a contiguous int64 [blocks][1 + cap][4] tensor")
 
     @staticmethod
     def _debug(debug: dict | None):
@@ -209,6 +248,10 @@ class MoeDecode:
         import torch
         if T is None:
             T = x.shape[0]
+        if T > 0:
+            self._check_rows("x", x, T)
+            self._check_rows("y", y, T)
+            self._check_debug(debug, T)
         s = stream if stream is not None else torch.cuda.current_stream()
         st = moe_decode_run(self.handle, x.data_ptr(), T, y.data_ptr(), self._debug(debug),
                             s.cuda_stream)
@@ -233,6 +276,10 @@ class MoeDecode:
         import torch
         if T is None:
             T = x.shape[0]
+        if T > 0:
+            self._check_rows("x", x, T)
+            self._check_rows("y", y, T)
+            self._check_debug(debug, T)
         s = stream if stream is not None else torch.cuda.current_stream()
         st = moe_decode_run_block(self.handle, x.data_ptr(), T, y.data_ptr(), self._debug(debug),
                                   s.cuda_stream)

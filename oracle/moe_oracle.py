@@ -284,7 +284,14 @@ def forward_block(inp, rows=None) -> BlockResult:
     xn = rmsnorm_bf16(inp.x, inp.norm_w, inp.workload.norm_eps)
     res = forward(dataclasses.replace(inp, x=xn), rows)
     y = bf16_bits_to_f64(inp.x)[res.rows] + res.y
-    return BlockResult(xn, res, y, bf16_round(y))
+    return BlockResult(xn, res, y, residual_add(inp.x[res.rows], res.y))
+
+
+def residual_add(x_bits: np.ndarray, moe: np.ndarray) -> np.ndarray:
+    """The block output bf16(x + moe): the residual row x (bf16 bits) plus the
+    layer's unrounded output, rounded once to bf16 from the exact fp64 sum
+    (the residual stream is rounded once, not after a rounded MoE output)."""
+    return bf16_round(bf16_bits_to_f64(x_bits) + np.asarray(moe, np.float64))
 
 
 # --------------------------------------------------------------------------

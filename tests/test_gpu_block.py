@@ -14,7 +14,7 @@ import torch
 from moe_decode_layer_amd import binding, device, synth
 from oracle import moe_oracle as O
 
-from checks import MAX_REL, MEAN_REL, check_placement
+from block_checks import check_against_plain_run, check_block, rolled, run_block
 
 pytestmark = pytest.mark.gpu
 
@@ -33,70 +33,6 @@ def inputs_for(wl):
     return synth.make_inputs(wl, att)
 
 
-def bf16_half_ulp(v):
-    """Half the bf16 spacing at |v| (the largest rounding error of v)."""
-    _, e = np.frexp(np.abs(v))
-    return np.ldexp(1.0, np.maximum(e - 8, -133) - 1)
-
-
-def check_block(wl, inp, out, rows=None):
-    """The kernel's normalised rows, routing and output against the oracle."""
-    ref = O.forward_block(inp, rows)
-    # xn: fp32 in the kernel, fp64 in the oracle, so an element whose exact
-    # value lies within a few fp32 steps of a bf16 rounding midpoint may round
-    # the other way: at most one bf16 step, on a small fraction of elements
-    got = O.bf16_bits_to_f64(out["norm_x"])
-    want = O.bf16_bits_to_f64(ref.xn)
-    off = got != want
-    assert np.all(np.abs(got - want)[off] <= 2 * bf16_half_ulp(want)[off]), "xn differs by more than one step"
-    assert off.mean() <= 1e-3, f"xn: {off.mean():.2e} of elements differ"
-    m = ref.moe
-    assert np.array_equal(out["topk_idx"], m.idx), "top-k indices differ"
-    assert np.array_equal(out["expert_count"], m.placement.count)
-    assert np.array_equal(out["pair_rank"], m.placement.rank)
-    check_placement(out["topk_idx"], out["pair_rank"], out["expert_count"], wl.E)
-    assert np.abs(out["topk_w"] - m.w).max() <= 1e-5
-    # the router ran on the kernel's xn (pinned above to one step of the
-    # oracle's): its logits are held to the layer's bar against the oracle's
-    # router on those same rows
-    ref_l = O.router_logits(got, inp.router_w, inp.router_b)
-    l_err = np.abs(out["logits"] - ref_l).max() / np.abs(ref_l).max()
-    assert l_err <= 1e-4, f"logits rel err {l_err}"
-    # y = bf16(x + moe): the kernel's y less the exact block output is its own
-    # rounding (half a step of y) plus the layer's error, held to the layer's
-    # bar relative to the MoE output (max and mean)
-    y = O.bf16_bits_to_f64(out["y"])[ref.moe.rows]
-    err = np.abs(y - ref.y) - bf16_half_ulp(y)
-    mx = max(float(err.max()), 0.0) / np.abs(m.y).max()
-    mean = max(float(np.abs(y - ref.y).mean() - bf16_half_ulp(y).mean()), 0.0) / np.abs(m.y).mean()
-    print(f"{wl.name}: xn off {off.mean():.1e}, moe part max_rel {mx:.3e} mean_rel {mean:.3e}")
-    assert mx <= MAX_REL and mean <= MEAN_REL, (mx, mean)
-    return ref
-
-
-def run_plain_on(layer, xn_bits, wl):
-    return device.run_once(layer, xn_bits, wl.E, wl.K)
-
-
-def check_against_plain_run(wl, layer, out):
-    """The plain layer on the kernel's own normalised rows: identical routing
-    bits, and the block's y is x + the plain layer's output up to the two
-    roundings (the MoE sum is the same fp32 value in both)."""
-    plain = run_plain_on(layer, out["norm_x"], wl)
-    for k in ("topk_idx", "topk_w", "pair_rank", "expert_count", "logits"):
-        assert np.array_equal(plain[k], out[k]), k
-    x = O.bf16_bits_to_f64(out["x"])
-    yb = O.bf16_bits_to_f64(out["y"])
-    yp = O.bf16_bits_to_f64(plain["y"])
-    assert np.all(np.abs(yb - (x + yp)) <= bf16_half_ulp(yb) + bf16_half_ulp(yp))
-
-
-def run_block(layer, inp, wl):
-    out = device.run_once(layer, inp.x, wl.E, wl.K, block=True)
-    out["x"] = inp.x
-    return out
-
-
 CASES = synth.PRENORM + [block_of(w) for w in (
     synth.Workload("t9_h4096_e256_k8_s1", T=9, H=4096, E=256, K=8, S=1, I=512),   # x in global memory
     synth.Workload("t20_h128_e8_k8_s1", T=20, H=128, E=8, K=8, S=1, I=64),        # router tiles, K = E
@@ -111,13 +47,16 @@ def test_block_parity(wl):
     inp = inputs_for(wl)
     layer = device.make_layer(inp)
     out = run_block(layer, inp, wl)
-    rows = None
-    if wl.T > 64:
-        rows = np.sort(np.random.default_rng(1).choice(wl.T, 40, replace=False))
-    check_block(wl, inp, out, rows)
-    check_against_plain_run(wl, layer, out)
-    again = run_block(layer, inp, wl)
-    assert np.array_equal(again["y"], out["y"]) and np.array_equal(again["norm_x"], out["norm_x"])
+    check_block(wl, inp, out)
+    check_against_plain_run(wl, inp, layer, out)
+    # a second run with the rows rotated: checked again in full, and its
+    # rows are the first run's rows in other positions
+    if wl.T > 1:
+        inp2 = rolled(inp, 1)
+        out2 = run_block(layer, inp2, wl)
+        check_block(wl, inp2, out2)
+        assert np.array_equal(out2["norm_x"][1:], out["norm_x"][:-1])
+        assert np.array_equal(out2["y"][1:], out["y"][:-1])
     layer.close()
 
 
@@ -125,17 +64,17 @@ def test_block_parity(wl):
                          ids=["small", "wide"])
 def test_block_and_plain_runs_alternate_on_one_handle(base, Ts):
     """Block runs of changing row counts, each followed by a plain run on the
-    same handle: every block run matches the oracle (the row ready words of
-    one run never pass for another's)."""
+    same handle, each block run on a different rotation of the rows: every
+    block run matches the oracle (the row ready words of one run never pass
+    for another's)."""
     wl = synth.PRENORM[base]
     inp = inputs_for(wl)
     layer = device.make_layer(inp, max_tokens=wl.T)
-    for T in Ts:
-        print(f"case {wl.name} T={T}", flush=True)
-        sub = dataclasses.replace(inp, workload=wl.with_rows(T), x=inp.x[:T], attempts=inp.attempts[:T])
+    for i, T in enumerate(Ts):
+        print(f"case {wl.name} T={T} shift {i + 1}", flush=True)
+        sub = rolled(inp, i + 1, T)
         out = run_block(layer, sub, sub.workload)
-        rows = None if T <= 64 else np.sort(np.random.default_rng(T).choice(T, 24, replace=False))
-        check_block(sub.workload, sub, out, rows)
+        check_block(sub.workload, sub, out)
         plain = device.run_once(layer, out["norm_x"], wl.E, wl.K)
         assert np.array_equal(plain["topk_idx"], out["topk_idx"])
     layer.close()
@@ -172,6 +111,6 @@ def test_expired_waits_in_a_block_run_report_timeout_and_the_next_run_recovers()
     print("case expired waits, block run", flush=True)
     layer.run_block(x, y, wl.T, {"expire_waits": 1})
     assert layer.check() == binding.MOE_ERR_TIMEOUT
-    out = run_block(layer, inp, wl)
-    check_block(wl, inp, out)
+    out = run_block(layer, rolled(inp, 2), wl)
+    check_block(wl, rolled(inp, 2), out)
     layer.close()

@@ -99,3 +99,25 @@ def test_block_rows_recipe():
     g = synth.norm_weight(wl)
     assert g.dtype == np.float32 and abs(float(g.mean()) - 1.0) < 0.01
     assert 0.08 < float(g.std()) < 0.12
+
+
+def test_residual_is_rounded_once():
+    # x = 1, moe = 2^-8 + 2^-16: the exact sum lies just above the midpoint
+    # 1 + 2^-8 between the bf16 neighbours 1 and 1 + 2^-7, so one rounding
+    # gives 1 + 2^-7.  Rounding moe first (to 2^-8, a tie resolved to even)
+    # and then the sum (the midpoint, a tie resolved to even) would give 1.
+    x = bits([[1.0, -1.0, 4.0]])
+    moe = np.array([[2.0 ** -8 + 2.0 ** -16, -(2.0 ** -8 + 2.0 ** -16), 2.0 ** -6 + 2.0 ** -14]])
+    got = O.residual_add(x, moe)
+    assert got.tolist() == [[1.0 + 2.0 ** -7, -(1.0 + 2.0 ** -7), 4.0 + 2.0 ** -5]]
+    double = O.bf16_round(O.bf16_bits_to_f64(x) + O.bf16_round(moe))
+    assert double.tolist() == [[1.0, -1.0, 4.0]]
+
+
+def test_block_output_uses_the_single_rounding():
+    # forward_block's y_bf16 is residual_add of its own x and unrounded moe
+    wl = synth.BY_NAME["tiny_t4_h256_e16_k2_prenorm"]
+    inp = synth.make_inputs(wl)
+    res = O.forward_block(inp)
+    assert np.array_equal(res.y_bf16, O.residual_add(inp.x, res.moe.y))
+    assert np.array_equal(res.y, O.bf16_bits_to_f64(inp.x) + res.moe.y)

@@ -160,3 +160,77 @@ def test_workload_routing_margins_and_invariants(i):
     check_placement(idx, plc.rank, plc.count, wl.E)
     if wl.zipf_s is not None:
         assert plc.count.max() > 8            # hot experts need several tiles
+
+
+# --------------------------------------------------------------------------
+# The input selection: margins among the top K+1 scores and the redraw loop
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("row,accepted", [
+    # the gap at the K/K+1 boundary is 5e-4: the top-2 set is ambiguous
+    ([0.9, 0.8, 0.7995, 0.1], False),
+    # the gap inside the top 2 is 5e-4: the order of the pair is ambiguous
+    ([0.9, 0.8995, 0.5, 0.1], False),
+    # the only small gap lies past the K+1-th score: irrelevant to the top 2
+    ([0.9, 0.8, 0.7, 0.6995], True),
+    # the same three rows with the experts in another order (the gaps are
+    # taken between scores in rank order, not between neighbouring ids)
+    ([0.7995, 0.1, 0.9, 0.8], False),
+    ([0.5, 0.8995, 0.1, 0.9], False),
+    ([0.6995, 0.7, 0.8, 0.9], True),
+])
+def test_topk_margins_hand_built_rows(row, accepted):
+    s = np.array([row], np.float64)
+    m = O.topk_margins(s, 2)
+    assert (m[0] >= O.MARGIN) == accepted
+    gaps = {(0.9, 0.8, 0.7995, 0.1): 0.0005, (0.9, 0.8995, 0.5, 0.1): 0.0005, (0.9, 0.8, 0.7, 0.6995): 0.1}
+    assert m[0] == pytest.approx(gaps[tuple(sorted(row, reverse=True))], abs=1e-12)
+
+
+def test_topk_margins_when_k_equals_e_uses_the_top_k():
+    # K = E: every expert is selected, only the order among them matters
+    s = np.array([[0.3, 0.9, 0.6]])
+    assert O.topk_margins(s, 3)[0] == pytest.approx(0.3)
+    assert O.topk_margins(np.array([[0.5]]), 1)[0] == np.inf
+
+
+def _stub_workload(T, K):
+    return synth.Workload("stub", T=T, H=3, E=3, K=K, S=0, I=32)
+
+
+def _stub_rows(table):
+    """x_rows stand-in: row t of attempt a is table[t][a] (fp64 values, stored
+    as bf16 bits).  With the one-hot router below, logits equal x."""
+    def rows(att):
+        return np.stack([O.bf16_value_to_bits(np.asarray(table[t][min(int(a), len(table[t]) - 1)],
+                                                         np.float64))
+                         for t, a in enumerate(att)])
+    return rows
+
+
+def test_choose_attempts_redraws_tied_rows_only():
+    eye = np.eye(3, dtype=np.float32)         # logits = x
+    # row 0: attempt 0 ties experts 0 and 1 at the top, attempt 1 does not;
+    # row 1: attempt 0 is already clear; row 2 needs two redraws
+    table = [
+        [[1.0, 1.0, 0.0], [2.0, 1.0, 0.0]],
+        [[0.0, 1.0, 2.0]],
+        [[1.0, 0.0, 1.0], [0.5, 0.5, -1.0], [3.0, 0.0, -2.0]],
+    ]
+    att = O.choose_attempts(_stub_workload(3, 1), _stub_rows(table), eye, None)
+    assert att.tolist() == [1, 0, 2]
+
+
+def test_choose_attempts_fails_loudly_after_max_attempts():
+    eye = np.eye(3, dtype=np.float32)
+    table = [[[1.0, 1.0, 0.0]]]               # every attempt ties
+    with pytest.raises(RuntimeError):
+        O.choose_attempts(_stub_workload(1, 1), _stub_rows(table), eye, None, max_attempts=5)
+
+
+def test_choose_attempts_checks_the_k_plus_1_boundary():
+    # K = 2: attempt 0 has a clear top 2 but the 2nd and 3rd scores tie,
+    # so the selected set is ambiguous and the row is redrawn
+    eye = np.eye(3, dtype=np.float32)
+    table = [[[2.0, 1.0, 1.0], [2.0, 1.0, -1.0]]]
+    att = O.choose_attempts(_stub_workload(1, 2), _stub_rows(table), eye, None)
+    assert att.tolist() == [1]
