@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define MOE_DECODE_ABI_VERSION 2
+#define MOE_DECODE_ABI_VERSION 3
 
 typedef int32_t moe_status;
 #define MOE_OK                0  /* success */
@@ -64,7 +64,12 @@ typedef struct moe_decode_config {
   int32_t hidden;        /* H; multiple of 64, <= 16384 */
   int32_t num_experts;   /* E routed experts; 1..256 */
   int32_t top_k;         /* K experts per row; 1..min(E, 16) */
-  int32_t intermediate;  /* I per expert; multiple of 64, <= 8192 */
+  int32_t intermediate;  /* I per expert; multiple of 32, <= 8192.  A width that is
+                            not a multiple of 64 runs padded to the next one: the
+                            padding rows and columns get zero weights, so results are
+                            those of width I (the per-GPU width 288 of TP8 padded to
+                            320: "Beyond Day-0: Optimizing DeepSeek-V4.1 Flash in
+                            SGLang", section 3.1) */
   int32_t num_shared;    /* S always-on shared experts; 0 or 1 */
   int32_t deadline_us;   /* bound on every in-kernel wait, microseconds; 0 = 1 s */
   uint32_t flags;        /* reserved; must be 0 */
@@ -159,12 +164,24 @@ moe_status moe_decode_create(const moe_decode_config* cfg, const moe_decode_weig
 /*
  * Runtime: enqueue one layer call on hip_stream.  x and y are device pointers to
  * [T][H] bf16, 16-byte aligned, not overlapping; dbg may be NULL.  T = 0 is a
- * no-op.  Asynchronous: no allocation, no host synchronisation, one kernel
- * launch.  Runs on one handle must be ordered on one stream (they share the
- * workspace).  Each call gives its launch a fresh run tag, which every
- * hand-off inside the kernel is checked against; a graph that captured a
- * call would replay the same tag and accept the previous replay's words, so
- * captured calls must not be replayed: call this function for every run.
+ * no-op; T > cfg.max_tokens gives MOE_ERR_UNSUPPORTED (the Guard's answer),
+ * T < 0 MOE_ERR_INVALID_ARG, in both cases before any launch.
+ * Asynchronous: no allocation, no host synchronisation, one kernel launch.
+ * Runs on one handle must be ordered on one stream (they share the
+ * workspace).
+ *
+ * Graph capture and replay: the launch carries no per-run state.  The run's
+ * tag (checked by every hand-off inside the kernel) and its counter block
+ * come from arrival counters in the handle's workspace that each launch
+ * advances by a fixed amount, so a HIP graph that captured this call (or any
+ * sequence of calls) can be replayed any number of times; each replay reads
+ * x and writes y at the captured addresses, with the captured T.  Replays
+ * must also be stream-ordered with every other run on the handle.  Source:
+ * "SGLang's Low-Latency Mode Boosts DeepSeek-V4.1-Flash Speed by 1.56x on
+ * AMD", section "AMD keeps the layer resident" (decode under HIP graphs).
+ * Tags repeat after 2^32 - 1 runs of a handle; a hand-off word that no run
+ * wrote for exactly that many runs would then pass as current.
+ *
  * A wait that passes the deadline makes the kernel exit early (y is then
  * undefined) and is reported by moe_decode_check.
  */

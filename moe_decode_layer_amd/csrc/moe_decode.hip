@@ -114,14 +114,27 @@ constexpr int kCtrTopkDone = 1 * kLine;     // distributed top-k items done
 constexpr int kClaimGroups = 8;             // claim counters (workgroup index mod 8)
 constexpr int kCtrTicket = 4 * kLine;       // [kClaimGroups] next unclaimed dynamic item of each group
 constexpr int kCtrHReady = (4 + kClaimGroups) * kLine;   // [E+S] gate/up publications per expert (E+S <= 257)
+constexpr int kMaxRowGroups = 128;          // down column groups: H / 128 <= 128
 constexpr int kCtrRgDone = kCtrHReady + 257 * kLine;   // [H/128] down-wave publications (<= 128)
 // "go" flag raised once by the last distributed top-k item, polled by every
 // workgroup: kGoLines copies, 1 KiB apart, so the pollers spread over memory
 // channels
 constexpr int kGoLines = 64;
 constexpr int kGoStride = 256;              // words
-constexpr int kCtrTopkGo = kCtrRgDone + 128 * kLine;
+constexpr int kCtrTopkGo = kCtrRgDone + kMaxRowGroups * kLine;
 constexpr int kCtrHead = kCtrTopkGo + kGoLines * kGoStride;
+
+// Arrival counters (64-bit, outside the counter blocks, never cleared).
+// Workgroup b adds to counter b mod kArriveGroups; the workgroups of a group
+// together add exactly kRunUnits per run (the group's first workgroup adds
+// kRunUnits minus the rest of the group, every other one 1), so every value
+// a run's fetch-add returns lies in [n kRunUnits, (n + 1) kRunUnits) for the
+// run's index n, whatever order the workgroups arrive in.  The run's tag and
+// counter block follow from n, so no per-run value travels in the kernel
+// arguments and a captured graph can replay a launch as it stands.
+constexpr int kArriveGroups = 8;
+constexpr int kRunUnitsLog2 = 16;           // grids of up to 2^16 workgroups
+constexpr unsigned long long kRunUnits = 1ull << kRunUnitsLog2;
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -174,10 +187,11 @@ struct Params {
   float* topk_w;       // [T][K]
   uint64_t* h_scr;     // [T*K + T*S][I/2] two bf16 of h | epoch, rows grouped by expert
   uint64_t* o_scr;     // [T*K + T*S][H] expert outputs (fp32 bits | epoch)
-  int* ctr;            // this run's counter block
-  int* ctr_next;       // the other block: cleared during this run for the next one
+  int* ctr_base;       // two counter blocks: a run uses block (run index & 1)
+                       // and clears the other one for the next run
   int* status;         // in-kernel status word (0 = ok), outside the blocks
-  uint32_t epoch;      // this run's tag, never 0 (the workspace starts zeroed)
+  unsigned long long* arrive;  // [kArriveGroups] arrival counters, kLine ints apart:
+                               // each run adds exactly kRunUnits to every one
   // debug copies (nullable)
   int* dbg_idx;
   float* dbg_w;
@@ -360,6 +374,18 @@ __device__ __forceinline__ long long tl_cycles(KParams& p) {
   return p.trace ? (long long)__builtin_amdgcn_s_memtime() : 0;
 }
 
+// This workgroup's view of the run -- its tag (epoch) and counter block --
+// is resolved at kernel entry from the arrival counters (see kArriveGroups)
+// and carried in Lds (below) as uniform values.  Run n has epoch
+// (n mod (2^32 - 1)) + 1 (never 0, the value of a cleared word) and uses
+// counter block n & 1.
+struct RunCtx {
+  uint32_t epoch;
+  uint32_t pad;
+  int* ctr;
+};
+__shared__ RunCtx s_run;
+
 // Tagged hand-offs.  Logits, h and expert outputs travel as 64-bit words:
 // 32 bits of payload, and the run's epoch in the high half.  A 64-bit store
 // is single-copy atomic, so a reader that sees the current epoch sees the
@@ -393,17 +419,17 @@ __device__ __forceinline__ void wait_vm_older_than() {
 // issued its own loads (N of them): waiting then for everything older costs
 // nothing.  Items that issue no loads first flush with a full wait.
 template <int N>
-__device__ __forceinline__ void flush_pending(KParams& p, int& pend) {
+__device__ __forceinline__ void flush_pending(int* ctr, int& pend) {
   if (pend >= 0) {
     wait_vm_older_than<N>();
-    if (lane_id() == 0) count_done(p.ctr + kCtrRgDone + pend * kLine);
+    if (lane_id() == 0) count_done(ctr + kCtrRgDone + pend * kLine);
     pend = -1;
   }
 }
-__device__ __forceinline__ void flush_pending_now(KParams& p, int& pend) {
+__device__ __forceinline__ void flush_pending_now(int* ctr, int& pend) {
   if (pend >= 0) {
     wait_stores();
-    if (lane_id() == 0) count_done(p.ctr + kCtrRgDone + pend * kLine);
+    if (lane_id() == 0) count_done(ctr + kCtrRgDone + pend * kLine);
     pend = -1;
   }
 }
@@ -579,6 +605,8 @@ struct Lds {
   SHARED uint16_t* xs;            // [T][xs_stride] the layer input (small batches)
   SHARED uint16_t* hs;            // [16][hs_stride] h rows of the current down item
   SHARED float* lg;               // [T][E] router logits (small batches)
+  uint32_t epoch;                 // this run's tag
+  int* ctr;                       // this run's counter block
 };
 
 __device__ Lds lds_view(KParams& p, SHARED char* smem) {
@@ -634,7 +662,7 @@ __device__ __forceinline__ bool gather_tagged(KParams& p, const Lds& L, int n, L
       for (int b = 0; b < kBatch; ++b) {
         const int i = i0 + b * kThreads;
         if (i < n && (m >> b & 1u) && want(i)) {
-          if (tag_ok(v[b], p.epoch)) {
+          if (tag_ok(v[b], L.epoch)) {
             take(i, (uint32_t)v[b]);
             if (j < 8) todo &= ~(1ull << (kBatch * j + b));
           } else {
@@ -684,7 +712,7 @@ __device__ __forceinline__ bool gather_small(KParams& p, const Lds& L, int n, Lo
       for (int b = 0; b < kBatch; ++b) v[b] = load(min((int)threadIdx.x + b * kThreads, n - 1));
 #pragma unroll
       for (int b = 0; b < kBatch; ++b) {
-        const bool ok = (need >> b & 1u) && tag_ok(v[b], p.epoch);
+        const bool ok = (need >> b & 1u) && tag_ok(v[b], L.epoch);
         *(ok ? slot((int)threadIdx.x + b * kThreads) : sink) = (uint32_t)v[b];
         need &= ok ? ~(1u << b) : ~0u;
       }
@@ -871,7 +899,7 @@ __device__ __forceinline__ void router_tile_item(KParams& p, const Lds& L, int i
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = 4 * kq + i;
-      if (r < nt && n < ne) st_tag(out + (size_t)(t0 + r) * p.E + e0 + n, __float_as_uint(s[i] + bias), p.epoch);
+      if (r < nt && n < ne) st_tag(out + (size_t)(t0 + r) * p.E + e0 + n, __float_as_uint(s[i] + bias), L.epoch);
     }
   }
   __syncthreads();                             // the partials area is free again
@@ -882,7 +910,7 @@ __device__ __forceinline__ void router_tile_item(KParams& p, const Lds& L, int i
 // Returns (timeline only) when this workgroup's partial sums were complete.
 // NORM (pre-norm block runs): x is xn; the first pass's weights are
 // requested before the wait for the item's rows.  LLONG_MIN: the wait failed.
-__device__ bool wait_rows(KParams& p, int t0, int n, SHARED int* lds_flag);
+__device__ bool wait_rows(KParams& p, const Lds& L, int t0, int n);
 template <bool NORM = false>
 __device__ __forceinline__ long long router_item(KParams& p, const Lds& L, int item, bool stage_x) {
   const int w = wave_id(), lane = lane_id();
@@ -910,7 +938,7 @@ __device__ __forceinline__ long long router_item(KParams& p, const Lds& L, int i
 #pragma unroll
     for (int i = 0; i < 4; ++i) wv[i] = ld(wr + 4 * c + i);
     if constexpr (NORM) {
-      if (c0 == 0 && !wait_rows(p, t0, nt, L.misc + 1)) return LLONG_MIN;
+      if (c0 == 0 && !wait_rows(p, L, t0, nt)) return LLONG_MIN;
     }
 #pragma unroll
     for (int j = 0; j < kRouterRows; ++j) {
@@ -967,7 +995,7 @@ __device__ __forceinline__ long long router_item(KParams& p, const Lds& L, int i
     for (int ww = 1; ww < kWaves; ++ww) s += part[ww * kRouterRows + j];
     s += bias;
     if (j < nt && c < p.lg_copies)
-      st_tag(p.lgt + (((size_t)c * p.E + e) << p.lg_tp_log2) + t0 + j, __float_as_uint(s), p.epoch);
+      st_tag(p.lgt + (((size_t)c * p.E + e) << p.lg_tp_log2) + t0 + j, __float_as_uint(s), L.epoch);
     if (j < nt && c == 0 && p.dbg_logits) st(p.dbg_logits + (size_t)(t0 + j) * p.E + e, s);
   }
   __syncthreads();                             // the partials area is free again
@@ -1310,7 +1338,7 @@ __device__ __forceinline__ bool combine_item(KParams& p, const Lds& L, int rc, i
   // a few items poll the outputs' tags directly, re-reading only stale words.
   if (p.n_cmb > 128) {
     const int target = (n_mr + p.n_mr_sh) * down_waves_in_group(p, rg);
-    if (!wait_geq(p, p.ctr + kCtrRgDone + rg * kLine, target, L.misc + 1)) return false;
+    if (!wait_geq(p, L.ctr + kCtrRgDone + rg * kLine, target, L.misc + 1)) return false;
   }
   int tt[kOut];
   bool live[kOut];
@@ -1342,7 +1370,7 @@ __device__ __forceinline__ bool combine_item(KParams& p, const Lds& L, int rc, i
   // A thread missing any of its inputs reads all of them again (no
   // per-word branches; the conditions on k are uniform).
   uint64_t v[kOut][kIn];
-  const uint64_t fresh = (uint64_t)p.epoch << 32;   // tag-only stand-in for a missing shared expert
+  const uint64_t fresh = (uint64_t)L.epoch << 32;   // tag-only stand-in for a missing shared expert
 #pragma unroll
   for (int j = 0; j < kOut; ++j)
 #pragma unroll
@@ -1359,7 +1387,7 @@ __device__ __forceinline__ bool combine_item(KParams& p, const Lds& L, int rc, i
 #pragma unroll
       for (int j = 0; j < kOut; ++j)
 #pragma unroll
-        for (int k = 0; k < kIn; ++k) need |= live[j] && !tag_ok(v[j][k], p.epoch);
+        for (int k = 0; k < kIn; ++k) need |= live[j] && !tag_ok(v[j][k], L.epoch);
     }
     if (!block_any(need, L.misc + 8)) break;
     if (!poll_round(p, &t_end, &rounds, L.misc + 1)) return false;
@@ -1398,7 +1426,7 @@ struct GuStage {
 template <int NMB, bool XL, int NMBMAX>
 __device__ __forceinline__ void gu_item(KParams& p, const Lds& L, int slot, int sbase, int r0, int nrows,
                         int rb, bool shared, int parity, int& pend) {
-  flush_pending_now(p, pend);
+  flush_pending_now(L.ctr, pend);
   using Stage = GuStage<NMB, XL>;
   constexpr int D = Stage::D;
   const int w = wave_id(), lane = lane_id();
@@ -1497,10 +1525,10 @@ __device__ __forceinline__ void gu_item(KParams& p, const Lds& L, int slot, int 
       const uint32_t hb_next = dpp<kDppRowShl1>(hb);          // column n + 1
       const int r = mb * kMBlock + 4 * kq + i;
       if (n < 8 && (n & 1) == 0 && r < nrows)
-        st_tag(p.h_scr + (size_t)(sbase + r0 + r) * (p.I / 2) + (8 * rb + n) / 2, hb | (hb_next << 16), p.epoch);
+        st_tag(p.h_scr + (size_t)(sbase + r0 + r) * (p.I / 2) + (8 * rb + n) / 2, hb | (hb_next << 16), L.epoch);
     }
     // each wave that stored h rows counts them in (one per 16-row block)
-    if (lane == 0) count_done(p.ctr + kCtrHReady + slot * kLine);
+    if (lane == 0) count_done(L.ctr + kCtrHReady + slot * kLine);
   }
 }
 
@@ -1521,7 +1549,7 @@ struct DnStage {
 template <int NMB, bool HL>
 __device__ __forceinline__ bool down_item(KParams& p, const Lds& L, int slot, int sbase, int r0, int nrows,
                           int rg, int h_target, int& pend) {
-  flush_pending_now(p, pend);
+  flush_pending_now(L.ctr, pend);
   using Stage = DnStage<NMB, HL>;
   constexpr int D = Stage::D;
   const int w = wave_id(), lane = lane_id();
@@ -1605,14 +1633,14 @@ __device__ __forceinline__ bool down_item(KParams& p, const Lds& L, int slot, in
   Stage A, B;
   if (!HL) {
     // h is read in the pipeline below: it must be complete first
-    if (!wait_geq(p, p.ctr + kCtrHReady + slot * kLine, h_target, L.misc + 1)) return false;
+    if (!wait_geq(p, L.ctr + kCtrHReady + slot * kLine, h_target, L.misc + 1)) return false;
     if (!verify_h_rows(p, L, sbase + r0, nrows)) return false;
   }
   load(A, 0);                                 // weights first: they need no input
   if (HL) {
     // stage the item's h rows while the first weights are in flight (the
     // barrier inside the wait keeps the previous item's readers safe)
-    if (!wait_geq(p, p.ctr + kCtrHReady + slot * kLine, h_target, L.misc + 1)) return false;
+    if (!wait_geq(p, L.ctr + kCtrHReady + slot * kLine, h_target, L.misc + 1)) return false;
     if (!stage_h_rows(p, L, sbase + r0, nrows)) return false;
     __syncthreads();
   }
@@ -1633,7 +1661,7 @@ __device__ __forceinline__ bool down_item(KParams& p, const Lds& L, int slot, in
         for (int i = 0; i < 4; ++i) {
           const int r = mb * kMBlock + 4 * kq + i;
           if (r < nrows)
-            st_tag(p.o_scr + (size_t)(sbase + r0 + r) * p.H + rb * kTileRows + n, __float_as_uint(acc[j][mb][i]), p.epoch);
+            st_tag(p.o_scr + (size_t)(sbase + r0 + r) * p.H + rb * kTileRows + n, __float_as_uint(acc[j][mb][i]), L.epoch);
         }
     }
   }
@@ -1663,7 +1691,7 @@ __device__ __forceinline__ void gu_item_full(KParams& p, const Lds& L, int slot,
     wv[j] = ld_stream(wt + (size_t)j * kWaves * kWave);
     sv[j] = ld_stream(sc + (size_t)j * kWaves * kTileRows);
   }
-  flush_pending<2 * NJ>(p, pend);
+  flush_pending<2 * NJ>(L.ctr, pend);
   const bool aval = n < nrows;
   const int tok = shared ? (r0 + (aval ? n : 0)) : (int)L.rows[sbase + r0 + (aval ? n : 0)];
   const SHARED uint16_t* arow = L.xs + (size_t)tok * p.xs_stride + 8 * kq + kTileK * w;
@@ -1695,9 +1723,9 @@ __device__ __forceinline__ void gu_item_full(KParams& p, const Lds& L, int slot,
       const uint32_t hb_next = dpp<kDppRowShl1>(hb);
       const int r = 4 * kq + i;
       if (n < 8 && (n & 1) == 0 && r < nrows)
-        st_tag(p.h_scr + (size_t)(sbase + r0 + r) * (p.I / 2) + (8 * rb + n) / 2, hb | (hb_next << 16), p.epoch);
+        st_tag(p.h_scr + (size_t)(sbase + r0 + r) * (p.I / 2) + (8 * rb + n) / 2, hb | (hb_next << 16), L.epoch);
     }
-    if (lane == 0) count_done(p.ctr + kCtrHReady + slot * kLine);
+    if (lane == 0) count_done(L.ctr + kCtrHReady + slot * kLine);
   }
 }
 
@@ -1738,8 +1766,8 @@ __device__ __forceinline__ bool down_item_full(KParams& p, const Lds& L, int slo
   }
   // the 4 NQ weight and scale loads, then at least one h batch: waiting for
   // all but the last 4 NQ + 1 operations covers the older stores
-  if (fast) flush_pending<4 * NQ + 1>(p, pend);
-  else flush_pending<4 * NQ>(p, pend);
+  if (fast) flush_pending<4 * NQ + 1>(L.ctr, pend);
+  else flush_pending<4 * NQ>(L.ctr, pend);
   // the previous item's readers of the h area are done past this barrier
   __syncthreads();
   bool stale = !fast;
@@ -1750,7 +1778,7 @@ __device__ __forceinline__ bool down_item_full(KParams& p, const Lds& L, int slo
 #pragma unroll
     for (int b = 0; b < kHFast; ++b) {
       const int i = threadIdx.x + b * kThreads;
-      const bool ok = tag_ok(hv[b], p.epoch);
+      const bool ok = tag_ok(hv[b], L.epoch);
       const int r = (int)fdiv((uint32_t)i, p.fd_h2.m, p.fd_h2.s);
       SHARED uint32_t* const d = (SHARED uint32_t*)(L.hs + (size_t)r * p.hs_stride + 2 * (i - r * per_row));
       *(i < nh && ok ? d : sink) = (uint32_t)hv[b];
@@ -1759,7 +1787,7 @@ __device__ __forceinline__ bool down_item_full(KParams& p, const Lds& L, int slo
   }
   if (block_any(stale, L.misc + 8)) {
     // h not complete yet (or too many rows): wait for the count, then gather
-    if (!wait_geq(p, p.ctr + kCtrHReady + slot * kLine, h_target, L.misc + 1)) return false;
+    if (!wait_geq(p, L.ctr + kCtrHReady + slot * kLine, h_target, L.misc + 1)) return false;
     if (!stage_h_rows(p, L, sbase + r0, nrows)) return false;
   } else if (threadIdx.x == 0) {
     *(SHARED long long*)(L.misc + 12) = tl_clock(p);   // inputs ready (timeline)
@@ -1790,7 +1818,7 @@ __device__ __forceinline__ bool down_item_full(KParams& p, const Lds& L, int slo
       for (int i = 0; i < 4; ++i) {
         const int r = 4 * kq + i;
         if (r < nrows)
-          st_tag(p.o_scr + (size_t)(sbase + r0 + r) * p.H + (rb0 + j) * kTileRows + n, __float_as_uint(acc[j][i]), p.epoch);
+          st_tag(p.o_scr + (size_t)(sbase + r0 + r) * p.H + (rb0 + j) * kTileRows + n, __float_as_uint(acc[j][i]), L.epoch);
       }
     }
   }
@@ -1857,7 +1885,7 @@ __device__ __forceinline__ void gu_item_wide(KParams& p, const Lds& L, int slot,
   };
 #pragma unroll
   for (int j = 0; j < P; ++j) load(S[j], j);
-  flush_pending<P * (2 * NMB + 2 * kWideRb)>(p, pend);
+  flush_pending<P * (2 * NMB + 2 * kWideRb)>(L.ctr, pend);
   const u32x4 zero4 = {0u, 0u, 0u, 0u};
   f32x4 acc[kWideRb][NMB];
 #pragma unroll
@@ -1921,12 +1949,12 @@ __device__ __forceinline__ void gu_item_wide(KParams& p, const Lds& L, int slot,
         const uint32_t hb_next = dpp<kDppRowShl1>(hb);          // column n + 1
         const int r = mb * kMBlock + 4 * kq + i;
         if (n < 8 && (n & 1) == 0 && r < nrows)
-          st_tag(p.h_scr + (size_t)(sbase + r0 + r) * (p.I / 2) + (8 * rb + n) / 2, hb | (hb_next << 16), p.epoch);
+          st_tag(p.h_scr + (size_t)(sbase + r0 + r) * (p.I / 2) + (8 * rb + n) / 2, hb | (hb_next << 16), L.epoch);
       }
     }
   }
   // one publication per wave and item: an M-range counts n_rb13 in all
-  if (lane == 0) count_done(p.ctr + kCtrHReady + slot * kLine);
+  if (lane == 0) count_done(L.ctr + kCtrHReady + slot * kLine);
 }
 
 // ----------------------------------------------------------------------------
@@ -1962,9 +1990,9 @@ __device__ __forceinline__ bool dn_item_wide(KParams& p, const Lds& L, int slot,
   };
 #pragma unroll
   for (int t = 0; t < P; ++t) load(t, t);
-  flush_pending<2 * P>(p, pend);
+  flush_pending<2 * P>(L.ctr, pend);
   // the barriers of the wait also end the previous item's reads of the area
-  if (!wait_geq(p, p.ctr + kCtrHReady + slot * kLine, h_target, L.misc + 1)) return false;
+  if (!wait_geq(p, L.ctr + kCtrHReady + slot * kLine, h_target, L.misc + 1)) return false;
   if (!stage_h_rows(p, L, sbase + r0, nrows)) return false;
   __syncthreads();
   const u32x4 zero4 = {0u, 0u, 0u, 0u};
@@ -2026,7 +2054,7 @@ __device__ __forceinline__ bool dn_item_wide(KParams& p, const Lds& L, int slot,
         const int r = mb * kMBlock + 4 * kq + i;
         if (r < nrows)
           st_tag(p.o_scr + (size_t)(sbase + r0 + r) * p.H + (grp * NB + b) * kTileRows + n,
-                 __float_as_uint(acc[b][mb][i]), p.epoch);
+                 __float_as_uint(acc[b][mb][i]), L.epoch);
       }
   pend = grp;
   return true;
@@ -2049,7 +2077,8 @@ constexpr int kNormChunks = 16384 / 8 / kThreads;   // 16-byte words per thread 
 __device__ __forceinline__ void st_coh64(uint64_t* p, uint64_t v) {
   __hip_atomic_store((GLOBAL uint64_t*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ void norm_rows(KParams& p, SHARED float* red) {
+__device__ __forceinline__ void norm_rows(KParams& p, const Lds& L) {
+  SHARED float* const red = L.red;
   const int n8 = p.H / 8;
   // the last workgroups take the rows: the first ones start the router items,
   // which wait for every row anyway
@@ -2105,21 +2134,22 @@ __device__ __forceinline__ void norm_rows(KParams& p, SHARED float* red) {
     }
     wait_stores();
     __syncthreads();
-    if (threadIdx.x == 0) store_agent(p.norm_ready + t, (int)p.epoch);
+    if (threadIdx.x == 0) store_agent(p.norm_ready + t, (int)L.epoch);
   }
 }
 
 // Workgroup-wide wait until rows [t0, t0 + n) of xn are ready: the lanes of
 // wave 0 poll one ready word each, under the deadline.  false: deadline
 // passed or another workgroup reported an error.
-__device__ bool wait_rows(KParams& p, int t0, int n, SHARED int* lds_flag) {
+__device__ bool wait_rows(KParams& p, const Lds& L, int t0, int n) {
+  SHARED int* const lds_flag = L.misc + 1;
   if ((int)threadIdx.x < kWave) {
     uint32_t bad = 0;
     long long t_end = 0;
     bool timed = false;
     for (int r = threadIdx.x; r < n && !bad; r += kWave) {
       int spins = 0;
-      while (load_agent(p.norm_ready + t0 + r) != (int)p.epoch) {
+      while (load_agent(p.norm_ready + t0 + r) != (int)L.epoch) {
         if (!timed) {
           t_end = (long long)wall_clock64() + (p.expire_waits ? 0 : p.deadline_ticks);
           timed = true;
@@ -2158,7 +2188,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
   KParams& p = *(const CONSTANT Params*)__builtin_amdgcn_kernarg_segment_ptr();
   (void)arg;
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  const Lds L = lds_view(p, (SHARED char*)smem);
+  Lds L = lds_view(p, (SHARED char*)smem);
   const int tid = threadIdx.x;
   const int G = gridDim.x;
   // Small batch: the whole layer input is kept in LDS, loaded before the
@@ -2171,7 +2201,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
   auto ensure_x = [&]() __attribute__((always_inline)) -> bool {
     if (x_staged) return true;
     if constexpr (NORM) {
-      if (!wait_rows(p, 0, p.T, L.misc + 1)) return false;
+      if (!wait_rows(p, L, 0, p.T)) return false;
       rows_all = true;
     }
     const int per_row = p.H / 8;
@@ -2188,23 +2218,44 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
   bool routed = false;          // routing and placement are in LDS
   int i_rgu_end = 0, i_sdn_end = 0, i_rdn_end = 0, i_total = 0, n_mr = 0;
 
+  // Arrival: this run's index, hence its tag and counter block (see
+  // kArriveGroups).  Every workgroup arrives before anything else, so the
+  // counters advance by exactly kRunUnits per run even when a wait fails.
+  if (tid == 0) {
+    const int cg = (int)blockIdx.x % kArriveGroups;
+    const int in_group = (G - 1 - cg) / kArriveGroups + 1;
+    const unsigned long long add = (int)blockIdx.x < kArriveGroups ? kRunUnits - (unsigned)(in_group - 1) : 1ull;
+    const unsigned long long v = __hip_atomic_fetch_add((GLOBAL unsigned long long*)(p.arrive + cg * (kLine / 2)), add,
+                                                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const unsigned long long n = v >> kRunUnitsLog2;
+    s_run.epoch = (uint32_t)(n % 0xffffffffull) + 1u;
+    s_run.ctr = p.ctr_base + (size_t)(n & 1) * kCtrHead;
+  }
+  __syncthreads();
+  L.epoch = __builtin_amdgcn_readfirstlane(s_run.epoch);
+  {
+    const uint64_t a = (uint64_t)s_run.ctr;
+    L.ctr = (int*)(((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32)) << 32) |
+                   (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a));
+  }
   // The last workgroup clears the other counter block for the next run (no
-  // one uses it during this run).
+  // one uses it during this run): every counter any shape can use.
   if ((int)blockIdx.x == G - 1) {
-    int* q = p.ctr_next;
-    const int n_words = 1 + kClaimGroups + (p.E + p.S) + p.n_rg + kGoLines;
+    int* q = p.ctr_base + (L.ctr == p.ctr_base ? kCtrHead : 0);
+    constexpr int n_words = 1 + kClaimGroups + (kMaxExperts + 1) + kMaxRowGroups + kGoLines;
     for (int i = tid; i < n_words; i += kThreads) {
       int off;
       if (i < 1) off = kCtrTopkDone;
       else if (i < 1 + kClaimGroups) off = kCtrTicket + (i - 1) * kLine;
-      else if (i < 1 + kClaimGroups + p.E + p.S) off = kCtrHReady + (i - 1 - kClaimGroups) * kLine;
-      else if (i < 1 + kClaimGroups + p.E + p.S + p.n_rg) off = kCtrRgDone + (i - 1 - kClaimGroups - p.E - p.S) * kLine;
-      else off = kCtrTopkGo + (i - 1 - kClaimGroups - p.E - p.S - p.n_rg) * kGoStride;
+      else if (i < 1 + kClaimGroups + kMaxExperts + 1) off = kCtrHReady + (i - 1 - kClaimGroups) * kLine;
+      else if (i < 1 + kClaimGroups + kMaxExperts + 1 + kMaxRowGroups)
+        off = kCtrRgDone + (i - 1 - kClaimGroups - kMaxExperts - 1) * kLine;
+      else off = kCtrTopkGo + (i - 1 - kClaimGroups - kMaxExperts - 1 - kMaxRowGroups) * kGoStride;
       store_agent(q + off, 0);
     }
   }
 
-  if constexpr (NORM) norm_rows(p, L.red);
+  if constexpr (NORM) norm_rows(p, L);
 
   // optional timeline of this workgroup (thread 0 writes it)
   long long* trace = (p.trace && (int)blockIdx.x < p.trace_blocks)
@@ -2259,7 +2310,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
       }
       if (touch == 0x9e3779b9u) L.misc[15] = 1;   // keeps the page touches alive
     } else if constexpr (!FULL) {
-      if (!wait_geq(p, go_flag(p.ctr + kCtrTopkGo), 1, L.misc + 1, 1 << 20)) return false;
+      if (!wait_geq(p, go_flag(L.ctr + kCtrTopkGo), 1, L.misc + 1, 1 << 20)) return false;
       // indices, then weights, kBatch loads in flight per thread
       const int tk = p.T * p.K;
       batched_copy<int>(
@@ -2352,7 +2403,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
   bool dyn = false;
   int i_dyn = INT_MAX;          // S, once routed
   const int cgroup = blockIdx.x % kClaimGroups;
-  int* const claim_ctr = p.ctr + kCtrTicket + cgroup * kLine;
+  int* const claim_ctr = L.ctr + kCtrTicket + cgroup * kLine;
   it = blockIdx.x;
   for (;;) {
     if (!dyn && it >= p.i_pre_end) {
@@ -2381,7 +2432,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
         // after requesting their first weights)
         const int n_et = (p.E + kRouterTile - 1) / kRouterTile;
         const int t0 = (it / p.router_ks / n_et) * kRouterTile;
-        if (!rows_all && !wait_rows(p, t0, min(kRouterTile, p.T - t0), L.misc + 1)) break;
+        if (!rows_all && !wait_rows(p, L, t0, min(kRouterTile, p.T - t0))) break;
       }
       if (!FULL && p.router_tiles) {
         if constexpr (!FULL) router_tile_item(p, L, it);
@@ -2399,13 +2450,13 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
       const int mr = i / p.n_gu_mr, rb = i % p.n_gu_mr;
       const int r0 = mr * p.mrange;
       if constexpr (NORM && !XL)
-        if (!rows_all && !wait_rows(p, r0, min(p.mrange, p.T - r0), L.misc + 1)) break;
+        if (!rows_all && !wait_rows(p, L, r0, min(p.mrange, p.T - r0))) break;
       run_gu(p.E, p.T * p.K, r0, min(p.mrange, p.T - r0), rb, true);
     } else if (!FULL && it < p.i_topk_end) {
       kind = 2;
       if (!topk_item(p, L, it - p.i_router_end)) break;
       t_ready = *(SHARED long long*)(L.misc + 12);
-      publish_done(p.ctr + kCtrTopkDone, p.n_topk, p.ctr + kCtrTopkGo);
+      publish_done(L.ctr + kCtrTopkDone, p.n_topk, L.ctr + kCtrTopkGo);
     } else {
       kind = 6;
       if (!ensure_x()) break;
@@ -2416,7 +2467,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
         kind = 4;
         if constexpr (NORM && !XL) {
           if (!rows_all) {
-            if (!wait_rows(p, 0, p.T, L.misc + 1)) break;
+            if (!wait_rows(p, L, 0, p.T)) break;
             rows_all = true;
           }
         }
@@ -2462,7 +2513,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
         t_ready = *(SHARED long long*)(L.misc + 12);
       } else {
         kind = 7;
-        flush_pending_now(p, pend_rg);
+        flush_pending_now(L.ctr, pend_rg);
         // combine items: by column group for wide items (the order their
         // down items complete in), else by row group
         const int c = it - i_rdn_end;
@@ -2502,19 +2553,27 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
   }
 
   // a deferred column-group count still has to be given
-  flush_pending_now(p, pend_rg);
+  flush_pending_now(L.ctr, pend_rg);
 }
 
 // ----------------------------------------------------------------------------
 // Weight re-layout (create time): standard [rows][K] FP8 + [rows][K/32] fp32
 // scales -> 1 KiB tiles (see the top of this file).  For the gate/up matrix
 // row block rb holds gate rows 8 rb .. 8 rb + 7 then up rows I + 8 rb ..
-// I + 8 rb + 7.
+// I + 8 rb + 7.  An intermediate width I that is a multiple of 32 but not of
+// 64 is padded to the next multiple of 64 (I_p): the padding gate and up rows
+// and the padding down-projection columns get zero weights and zero scales,
+// so their g, u and h are exactly 0 and they add nothing to any sum ("Beyond
+// Day-0: Optimizing DeepSeek-V4.1 Flash in SGLang", section 3.1: the
+// per-GPU width 288 of TP8 is padded to 320 after sharding).
+//   rows_p, K_p   : packed rows and K (multiples of 16 and 64)
+//   rows_s, K_s   : the caller's rows and K (K_s a multiple of 32)
+//   half_p, half_s: gate/up matrix: I_p and I (0 for the down projection)
 // ----------------------------------------------------------------------------
 __global__ void pack_kernel(const uint8_t* __restrict__ w, const float* __restrict__ s,
-                            u32x4* __restrict__ wp, float* __restrict__ sp, int slots, int rows,
-                            int K, int interleave_half) {
-  const int nrb = rows / kTileRows, nq = K / kTileK, G = K / kGroup;
+                            u32x4* __restrict__ wp, float* __restrict__ sp, int slots, int rows_p,
+                            int K_p, int rows_s, int K_s, int half_p, int half_s) {
+  const int nrb = rows_p / kTileRows, nq = K_p / kTileK, G_s = K_s / kGroup;
   const size_t total = (size_t)slots * nrb * nq * kWave;
   for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < total;
        i += (size_t)gridDim.x * blockDim.x) {
@@ -2526,19 +2585,28 @@ __global__ void pack_kernel(const uint8_t* __restrict__ w, const float* __restri
     const int slot = (int)(blk / nrb);
     const int n = lane & 15, kq = lane >> 4;
     int row;
-    if (interleave_half > 0)
-      row = n < 8 ? 8 * rb + n : interleave_half + 8 * rb + (n - 8);
-    else
+    bool rvalid = true;
+    if (half_p > 0) {
+      const int ii = 8 * rb + (n & 7);       // intermediate column of this gate or up row
+      rvalid = ii < half_s;
+      row = n < 8 ? ii : half_s + ii;
+    } else {
       row = kTileRows * rb + n;
-    const uint8_t* src = w + ((size_t)slot * rows + row) * K + kTileK * q + 8 * kq;
-    const u32x2 a = *(const u32x2*)src;
-    const u32x2 b = *(const u32x2*)(src + kGroup);
+    }
+    const int k0 = kTileK * q + 8 * kq;      // group 0 of the tile; group 1 is 32 further
+    const bool v0 = rvalid && k0 < K_s, v1 = rvalid && k0 + kGroup < K_s;
+    const size_t r_s = (size_t)slot * rows_s + (rvalid ? row : 0);
+    const uint8_t* src = w + r_s * K_s;
+    const u32x2 zero2 = {0u, 0u};
+    const u32x2 a = v0 ? *(const u32x2*)(src + k0) : zero2;
+    const u32x2 b = v1 ? *(const u32x2*)(src + k0 + kGroup) : zero2;
     wp[i] = (u32x4){a.x, a.y, b.x, b.y};
     if (kq == 0) {
-      const float* ss = s + ((size_t)slot * rows + row) * G + 2 * q;
+      const int g0 = kTileK * q / kGroup;
+      const float* ss = s + r_s * G_s;
       float* d = sp + (tile * kTileRows + n) * 2;
-      d[0] = ss[0];
-      d[1] = ss[1];
+      d[0] = rvalid && g0 < G_s ? ss[g0] : 0.f;
+      d[1] = rvalid && g0 + 1 < G_s ? ss[g0 + 1] : 0.f;
     }
   }
 }
@@ -2590,7 +2658,6 @@ struct moe_decode_handle {
   int* norm_ready = nullptr;     // [max_tokens]
   float norm_eps = 0.f;
   float swiglu_limit = INFINITY; // moe_decode_set_swiglu_limit
-  uint32_t epoch = 0;            // tag of the last run (0: none yet)
   hipStream_t last_stream = nullptr;
   std::mutex mu;
   // occupancy cache, by (kernel variant + 6 for block runs, LDS bytes)
@@ -2608,12 +2675,16 @@ moe_status check_config(const moe_decode_config* c) {
     return MOE_ERR_INVALID_ARG;
   if (c->max_tokens > kMaxTokens) return MOE_ERR_UNSUPPORTED;
   if (c->hidden % kTileK != 0 || c->hidden > 16384) return MOE_ERR_UNSUPPORTED;
-  if (c->intermediate % kTileK != 0 || c->intermediate > 8192) return MOE_ERR_UNSUPPORTED;
+  if (c->intermediate % kGroup != 0 || c->intermediate > 8192) return MOE_ERR_UNSUPPORTED;
   if (c->num_experts > kMaxExperts) return MOE_ERR_UNSUPPORTED;
   if (c->top_k > kMaxTopK || c->top_k > c->num_experts) return MOE_ERR_UNSUPPORTED;
   if (c->num_shared > 1) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
+
+// The intermediate width the kernel runs: I rounded up to whole 64-K tiles
+// (the padding is zero weights, see pack_kernel).
+int padded_intermediate(const moe_decode_config& c) { return (c.intermediate + kTileK - 1) / kTileK * kTileK; }
 
 Params make_params(const moe_decode_handle* h, int T) {
   const moe_decode_config& c = h->cfg;
@@ -2624,7 +2695,7 @@ Params make_params(const moe_decode_handle* h, int T) {
   p.E = c.num_experts;
   p.K = c.top_k;
   p.S = c.num_shared;
-  p.I = c.intermediate;
+  p.I = padded_intermediate(c);
   p.router_w = h->router_w;
   p.router_wt = h->router_wt;
   p.router_b = h->router_b ? h->router_b : h->router_w;
@@ -2644,7 +2715,9 @@ Params make_params(const moe_decode_handle* h, int T) {
   p.topk_w = h->topk_w;
   p.h_scr = h->h_scr;
   p.o_scr = h->o_scr;
+  p.ctr_base = h->ctr;
   p.status = h->ctr + 2 * (size_t)kCtrHead;
+  p.arrive = (unsigned long long*)(h->ctr + 2 * (size_t)kCtrHead + kLine);
   const long long dl = c.deadline_us > 0 ? c.deadline_us : 1000000;
   p.deadline_ticks = dl * 100;   // wall clock runs at 100 MHz
   p.swiglu_limit = h->swiglu_limit;
@@ -2808,11 +2881,13 @@ moe_status moe_decode_create(const moe_decode_config* cfg, const moe_decode_weig
     if (hipGetDeviceProperties(&prop, device) != hipSuccess) { rc = MOE_ERR_HIP; break; }
     h->n_cu = prop.multiProcessorCount;
     h->coop = prop.cooperativeLaunch;
+    // I: the packed (padded) width; I_s: the caller's
     const size_t E = cfg->num_experts, S = cfg->num_shared, H = cfg->hidden,
-                 I = cfg->intermediate, K = cfg->top_k, Tm = cfg->max_tokens;
+                 I = padded_intermediate(*cfg), I_s = cfg->intermediate, K = cfg->top_k, Tm = cfg->max_tokens;
     const size_t slots = E + S;
     const size_t scr_rows = Tm * K + Tm * S;
-    const size_t ctr_words = 2 * (size_t)kCtrHead + kLine;   // two blocks + the status line
+    // two counter blocks, the status line, the arrival counters
+    const size_t ctr_words = 2 * (size_t)kCtrHead + kLine + (size_t)kArriveGroups * kLine;
     struct A { void** p; size_t bytes; } allocs[] = {
         {(void**)&h->router_w, E * H * 4},
         {(void**)&h->router_b, w->router_bias ? E * 4 : 0},
@@ -2847,10 +2922,10 @@ moe_status moe_decode_create(const moe_decode_config* cfg, const moe_decode_weig
       if (hipGetLastError() != hipSuccess) { rc = MOE_ERR_HIP; break; }
     }
     hipLaunchKernelGGL(pack_kernel, dim3(4096), dim3(256), 0, 0, w->w13, w->s13, h->w13p, h->s13p,
-                       (int)slots, (int)(2 * I), (int)H, (int)I);
+                       (int)slots, (int)(2 * I), (int)H, (int)(2 * I_s), (int)H, (int)I, (int)I_s);
     if (hipGetLastError() != hipSuccess) { rc = MOE_ERR_HIP; break; }
     hipLaunchKernelGGL(pack_kernel, dim3(4096), dim3(256), 0, 0, w->w2, w->s2, h->w2p, h->s2p,
-                       (int)slots, (int)H, (int)I, 0);
+                       (int)slots, (int)H, (int)I, (int)H, (int)I_s, 0, 0);
     if (hipGetLastError() != hipSuccess) { rc = MOE_ERR_HIP; break; }
     if (hipDeviceSynchronize() != hipSuccess) { rc = MOE_ERR_HIP; break; }
   } while (0);
@@ -2872,7 +2947,8 @@ moe_status run_impl(moe_decode_handle* h, const void* x, int32_t T, void* y,
                     const moe_decode_debug* dbg, void* hip_stream, bool norm) {
   if (!h) return MOE_ERR_INVALID_ARG;
   if (norm && !h->xn) return MOE_ERR_INVALID_ARG;
-  if (T < 0 || T > h->cfg.max_tokens) return MOE_ERR_INVALID_ARG;
+  if (T < 0) return MOE_ERR_INVALID_ARG;
+  if (T > h->cfg.max_tokens) return MOE_ERR_UNSUPPORTED;   // as the Guard answers for it
   if (T == 0) return MOE_OK;
   if (!x || !y) return MOE_ERR_INVALID_ARG;
   if (((uintptr_t)x | (uintptr_t)y) & 15u) return MOE_ERR_INVALID_ARG;
@@ -2910,27 +2986,6 @@ moe_status run_impl(moe_decode_handle* h, const void* x, int32_t T, void* y,
   int prev = 0;
   HIP_TRY(hipGetDevice(&prev));
   if (prev != h->device) HIP_TRY(hipSetDevice(h->device));
-  // A new tag for this run.  After 2^32 - 1 runs the tag would come back to
-  // values that old words may still carry: then every tagged buffer and both
-  // counter blocks are zeroed (on the stream) and the tags start over at 1.
-  if (h->epoch + 1 == 0) {
-    const moe_decode_config& c = h->cfg;
-    const size_t rows = (size_t)c.max_tokens * (c.top_k + c.num_shared);
-    if (hipMemsetAsync(h->lgt, 0, h->lgt_bytes, stream) != hipSuccess ||
-        hipMemsetAsync(h->h_scr, 0, rows * (c.intermediate / 2) * 8, stream) != hipSuccess ||
-        hipMemsetAsync(h->o_scr, 0, rows * c.hidden * 8, stream) != hipSuccess ||
-        hipMemsetAsync(h->ctr, 0, 2 * (size_t)kCtrHead * 4, stream) != hipSuccess ||
-        (h->norm_ready && hipMemsetAsync(h->norm_ready, 0, (size_t)c.max_tokens * 4, stream) != hipSuccess)) {
-      if (prev != h->device) (void)hipSetDevice(prev);
-      return MOE_ERR_HIP;
-    }
-    h->epoch = 0;
-  }
-  h->epoch += 1;
-  p.epoch = h->epoch;
-  // counter block of this run (tag parity) and the one it clears for the next
-  p.ctr = h->ctr + (size_t)(h->epoch & 1) * kCtrHead;
-  p.ctr_next = h->ctr + (size_t)((h->epoch + 1) & 1) * kCtrHead;
   // variants: 0 = x in LDS, 1 = up to 16 rows, 2 = more rows (4 MFMA blocks
   // per item), 3 = x in LDS with full-tile items (H = 64 kFullTiles,
   // I = 32 kFullTiles, h staged in LDS, local routing), 5 = the same at
@@ -2969,6 +3024,10 @@ moe_status run_impl(moe_decode_handle* h, const void* x, int32_t T, void* y,
     h->occ_blocks[slot] = nb;
   }
   const int grid = h->n_cu * h->occ_blocks[slot];
+  if (grid < kArriveGroups || grid > (int)kRunUnits) {   // every arrival counter needs a workgroup each run
+    if (prev != h->device) (void)hipSetDevice(prev);
+    return MOE_ERR_UNSUPPORTED;
+  }
   // The grid is sized to what the device holds at once, so all workgroups
   // are resident together on an otherwise idle device; every wait has a
   // deadline for the case where they are not.

@@ -29,7 +29,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert binding.moe_decode_abi_version() == 2
+    assert binding.moe_decode_abi_version() == 3
     for st in range(6):
         assert binding.moe_decode_status_string(st) != "unknown status"
     assert binding.moe_decode_status_string(99) == "unknown status"
@@ -49,7 +49,10 @@ def cfg(**kw):
     ({}, -1, binding.MOE_ERR_INVALID_ARG),
     ({"H": 4000}, 6, binding.MOE_ERR_UNSUPPORTED),
     ({"I": 576}, 6, binding.MOE_OK),
-    ({"I": 96}, 6, binding.MOE_ERR_UNSUPPORTED),
+    ({"I": 96}, 6, binding.MOE_OK),                  # multiple of 32: padded to 128
+    ({"I": 288}, 6, binding.MOE_OK),                 # the pages' TP8 width, padded to 320
+    ({"I": 80}, 6, binding.MOE_ERR_UNSUPPORTED),
+    ({"H": 4064}, 6, binding.MOE_ERR_UNSUPPORTED),   # H must be a multiple of 64
     ({"K": 17, "E": 32}, 6, binding.MOE_ERR_UNSUPPORTED),
     ({"K": 9, "E": 8}, 6, binding.MOE_ERR_UNSUPPORTED),
     ({"E": 257}, 6, binding.MOE_ERR_UNSUPPORTED),

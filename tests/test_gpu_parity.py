@@ -81,6 +81,11 @@ SMALL = [
     # 32 rows; 384 rows)
     synth.Workload("t64_h4096_e256_k8_s1_i576", T=64, H=4096, E=256, K=8, S=1, I=576, zipf_s=1.2),
     synth.Workload("t384_h4096_e256_k8_s1_i576", T=384, H=4096, E=256, K=8, S=1, I=576),
+    # the per-GPU width of TP8 (not a multiple of 64: run padded to 320 with
+    # zero weights), small and larger batches
+    synth.Workload("t6_h4096_e256_k8_s1_i288", T=6, H=4096, E=256, K=8, S=1, I=288),
+    synth.Workload("t40_h4096_e256_k8_s1_i288", T=40, H=4096, E=256, K=8, S=1, I=288, zipf_s=1.2),
+    synth.Workload("t20_h128_e8_k8_s1_i96", T=20, H=128, E=8, K=8, S=1, I=96),
 ]
 
 
