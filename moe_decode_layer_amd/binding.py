@@ -34,6 +34,7 @@ EXPORTS = (
 )
 
 
+
 class moe_decode_config(ctypes.Structure):
     _fields_ = [
         ("max_tokens", ctypes.c_int32),

@@ -8,14 +8,21 @@ import pytest
 
 from moe_decode_layer_amd import binding
 
-HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include",
-                      "moe_decode.h")
+INCLUDE = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include")
+HEADERS = ("moe_decode.h",)
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(moe_decode_\w+)\s*\(", text, flags=re.M)
+    names = []
+    for h in HEADERS:
+        text = open(os.path.join(INCLUDE, h)).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names += re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(moe_decode_\w+)\s*\(", text, flags=re.M)
+    return names
+
+
+def test_every_header_is_listed():
+    assert sorted(f for f in os.listdir(INCLUDE) if f.endswith(".h")) == sorted(HEADERS)
 
 
 def test_header_declarations_match_binding():
