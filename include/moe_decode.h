@@ -189,6 +189,30 @@ moe_status moe_decode_run(moe_decode_handle* h, const void* x, int32_t T, void* 
                           const moe_decode_debug* dbg, void* hip_stream);
 
 /*
+ * moe_decode_run with no workspace of the handle's: for callers that cannot
+ * allocate device memory at any point of their path (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc) and want the
+ * per-run scratch (counters, logits, top-k, h and expert outputs) to come
+ * from memory the library already holds.  Same arguments, layouts, results
+ * and errors as moe_decode_run; the handle still supplies the weights.
+ *
+ * The workspace is one array of 16 MiB in the library's code object, one
+ * copy per GPU, held until the process ends; the call allocates and frees
+ * nothing.  A run needs 4 * T * (K + S) * (I' + 2 H) bytes of h and output
+ * scratch (I' = I rounded up to 64) plus 0.6 to 1 MiB of counters and
+ * logits: at H 4096, I 512, K 8, S 1 that allows T <= 49.  A larger run
+ * returns MOE_ERR_UNSUPPORTED before any device work.  Every call on a GPU, from any handle, shares that GPU's
+ * array and keeps its contents for the next: the array's own run tags and
+ * counters keep successive calls apart, but calls that overlap in time on
+ * one GPU (two streams, two threads) race and must not be issued.  A
+ * deadline failure sets the array's status word; moe_decode_check on the
+ * same handle reports and clears it, and until then every call on that GPU
+ * that waits gives up early.
+ */
+moe_status moe_decode_run_static(moe_decode_handle* h, const void* x, int32_t T, void* y,
+                                 const moe_decode_debug* dbg, void* hip_stream);
+
+/*
  * Pre-norm block form of the layer: the RMSNorm that feeds the MoE input and
  * the residual add after the combine, fused into the same single launch.
  * Sources: "SGLang's Low-Latency Mode Boosts DeepSeek-V4.1-Flash Speed by

@@ -25,6 +25,7 @@ EXPORTS = (
     "moe_decode_supported",
     "moe_decode_create",
     "moe_decode_run",
+    "moe_decode_run_static",
     "moe_decode_set_input_norm",
     "moe_decode_run_block",
     "moe_decode_set_swiglu_limit",
@@ -101,6 +102,8 @@ def lib() -> ctypes.CDLL:
                                         ctypes.POINTER(P)]
         L.moe_decode_run.restype = ctypes.c_int32
         L.moe_decode_run.argtypes = [P, P, ctypes.c_int32, P, ctypes.POINTER(moe_decode_debug), P]
+        L.moe_decode_run_static.restype = ctypes.c_int32
+        L.moe_decode_run_static.argtypes = [P, P, ctypes.c_int32, P, ctypes.POINTER(moe_decode_debug), P]
         L.moe_decode_set_input_norm.restype = ctypes.c_int32
         L.moe_decode_set_input_norm.argtypes = [P, P, ctypes.c_float]
         L.moe_decode_run_block.restype = ctypes.c_int32
@@ -140,6 +143,12 @@ def moe_decode_run(h, x_ptr: int, T: int, y_ptr: int, dbg: moe_decode_debug | No
                    stream: int) -> int:
     return lib().moe_decode_run(h, x_ptr, T, y_ptr, ctypes.byref(dbg) if dbg is not None else None,
                                 stream)
+
+
+def moe_decode_run_static(h, x_ptr: int, T: int, y_ptr: int, dbg: moe_decode_debug | None,
+                          stream: int) -> int:
+    return lib().moe_decode_run_static(h, x_ptr, T, y_ptr, ctypes.byref(dbg) if dbg is not None else None,
+                                       stream)
 
 
 def moe_decode_set_input_norm(h, norm_w_ptr: int, eps: float) -> int:
@@ -258,6 +267,21 @@ class MoeDecode:
                             s.cuda_stream)
         if st != MOE_OK:
             raise MoeDecodeError("moe_decode_run", st)
+
+    def run_static(self, x, y, T: int | None = None, debug: dict | None = None, stream=None) -> None:
+        """Like run, with the workspace in the library's static array (no allocation)."""
+        import torch
+        if T is None:
+            T = x.shape[0]
+        if T > 0:
+            self._check_rows("x", x, T)
+            self._check_rows("y", y, T)
+            self._check_debug(debug, T)
+        s = stream if stream is not None else torch.cuda.current_stream()
+        st = moe_decode_run_static(self.handle, x.data_ptr(), T, y.data_ptr(), self._debug(debug),
+                                   s.cuda_stream)
+        if st != MOE_OK:
+            raise MoeDecodeError("moe_decode_run_static", st)
 
     def set_input_norm(self, norm_w, eps: float) -> None:
         """RMSNorm weight [H] fp32 (torch tensor on the device) and epsilon of block runs."""

@@ -2627,9 +2627,62 @@ __global__ void pack_router_kernel(const float* __restrict__ w, f32x4* __restric
 }
 
 // ----------------------------------------------------------------------------
+// Workspace of moe_decode_run_static: counter blocks, status and arrival
+// counters, logits, top-k, h and expert-output scratch of one run, in one
+// array of fixed size that the code object provides (no allocation).  Each
+// GPU holds its own copy, zero at load (static storage), for the life of the
+// process; host code reaches it only through the address hipGetSymbolAddress
+// returns for the current device.
+// ----------------------------------------------------------------------------
+constexpr size_t kScratchBytes = size_t(16) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+// ----------------------------------------------------------------------------
 // Host side
 // ----------------------------------------------------------------------------
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// Counter words of a workspace: two counter blocks, the status line, the
+// arrival counters.
+constexpr size_t kCtrWords = 2 * (size_t)kCtrHead + kLine + (size_t)kArriveGroups * kLine;
+
+// Byte offsets of a run's workspace in the static array (for T rows on a
+// handle's shape): the same buffers create() allocates, sized for T.
+struct StaticLayout {
+  size_t ctr, lgt, topk_idx, topk_w, h_scr, o_scr, total;
+};
+StaticLayout static_layout(const moe_decode_config& c, int I_p, int T) {
+  const size_t E = c.num_experts, H = c.hidden, K = c.top_k, S = c.num_shared;
+  const size_t rows = (size_t)T * (K + S);
+  StaticLayout L;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { const size_t o = off; off = align_up(off + bytes, 256); return o; };
+  L.ctr = take(kCtrWords * 4);
+  L.lgt = take(std::max((size_t)T * E * kRouterKsMax, (size_t)kLgCopies * E * 16) * 8);
+  L.topk_idx = take((size_t)T * K * 4);
+  L.topk_w = take((size_t)T * K * 4);
+  L.h_scr = take(rows * (I_p / 2) * 8);
+  L.o_scr = take(rows * H * 8);
+  L.total = off;
+  return L;
+}
+
+// The static array's device address, per device, looked up once (with the
+// device current).
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+unsigned char* g_scratch_ptr[kMaxDevices] = {};
+moe_status scratch_address(int device, unsigned char** out) {
+  if (device < 0 || device >= kMaxDevices) return MOE_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[device]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return MOE_ERR_HIP;
+    g_scratch_ptr[device] = (unsigned char*)ptr;
+  }
+  *out = g_scratch_ptr[device];
+  return MOE_OK;
+}
 
 }  // namespace
 
@@ -2659,6 +2712,7 @@ struct moe_decode_handle {
   float norm_eps = 0.f;
   float swiglu_limit = INFINITY; // moe_decode_set_swiglu_limit
   hipStream_t last_stream = nullptr;
+  int* last_status = nullptr;    // status word of the last run's workspace (handle's or static)
   std::mutex mu;
   // occupancy cache, by (kernel variant + 6 for block runs, LDS bytes)
   int occ_lds[12] = {-1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1};
@@ -2887,7 +2941,7 @@ moe_status moe_decode_create(const moe_decode_config* cfg, const moe_decode_weig
     const size_t slots = E + S;
     const size_t scr_rows = Tm * K + Tm * S;
     // two counter blocks, the status line, the arrival counters
-    const size_t ctr_words = 2 * (size_t)kCtrHead + kLine + (size_t)kArriveGroups * kLine;
+    const size_t ctr_words = kCtrWords;
     struct A { void** p; size_t bytes; } allocs[] = {
         {(void**)&h->router_w, E * H * 4},
         {(void**)&h->router_b, w->router_bias ? E * 4 : 0},
@@ -2944,7 +2998,7 @@ namespace {
 
 // One layer call (norm = false) or pre-norm block call (norm = true).
 moe_status run_impl(moe_decode_handle* h, const void* x, int32_t T, void* y,
-                    const moe_decode_debug* dbg, void* hip_stream, bool norm) {
+                    const moe_decode_debug* dbg, void* hip_stream, bool norm, bool in_static = false) {
   if (!h) return MOE_ERR_INVALID_ARG;
   if (norm && !h->xn) return MOE_ERR_INVALID_ARG;
   if (T < 0) return MOE_ERR_INVALID_ARG;
@@ -2986,6 +3040,25 @@ moe_status run_impl(moe_decode_handle* h, const void* x, int32_t T, void* y,
   int prev = 0;
   HIP_TRY(hipGetDevice(&prev));
   if (prev != h->device) HIP_TRY(hipSetDevice(h->device));
+  if (in_static) {
+    // the whole workspace in the static array of this device
+    const StaticLayout sl = static_layout(h->cfg, p.I, T);
+    unsigned char* base = nullptr;
+    moe_status st = sl.total > kScratchBytes ? MOE_ERR_UNSUPPORTED : scratch_address(h->device, &base);
+    if (st != MOE_OK) {
+      if (prev != h->device) (void)hipSetDevice(prev);
+      return st;
+    }
+    int* ctr = (int*)(base + sl.ctr);
+    p.ctr_base = ctr;
+    p.status = ctr + 2 * (size_t)kCtrHead;
+    p.arrive = (unsigned long long*)(ctr + 2 * (size_t)kCtrHead + kLine);
+    p.lgt = (uint64_t*)(base + sl.lgt);
+    p.topk_idx = (int*)(base + sl.topk_idx);
+    p.topk_w = (float*)(base + sl.topk_w);
+    p.h_scr = (uint64_t*)(base + sl.h_scr);
+    p.o_scr = (uint64_t*)(base + sl.o_scr);
+  }
   // variants: 0 = x in LDS, 1 = up to 16 rows, 2 = more rows (4 MFMA blocks
   // per item), 3 = x in LDS with full-tile items (H = 64 kFullTiles,
   // I = 32 kFullTiles, h staged in LDS, local routing), 5 = the same at
@@ -3034,6 +3107,7 @@ moe_status run_impl(moe_decode_handle* h, const void* x, int32_t T, void* y,
   void* args[] = {&p};
   const hipError_t err = hipLaunchKernel(fn, dim3(grid), dim3(kThreads), args, p.lds_bytes, stream);
   h->last_stream = stream;
+  h->last_status = p.status;
   if (prev != h->device) (void)hipSetDevice(prev);
   return err == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
@@ -3045,6 +3119,11 @@ extern "C" {
 moe_status moe_decode_run(moe_decode_handle* h, const void* x, int32_t T, void* y,
                           const moe_decode_debug* dbg, void* hip_stream) {
   return run_impl(h, x, T, y, dbg, hip_stream, false);
+}
+
+moe_status moe_decode_run_static(moe_decode_handle* h, const void* x, int32_t T, void* y,
+                                 const moe_decode_debug* dbg, void* hip_stream) {
+  return run_impl(h, x, T, y, dbg, hip_stream, false, true);
 }
 
 moe_status moe_decode_set_input_norm(moe_decode_handle* h, const float* norm_w, float eps) {
@@ -3102,13 +3181,14 @@ moe_status moe_decode_check(moe_decode_handle* h) {
   if (prev != h->device) HIP_TRY(hipSetDevice(h->device));
   moe_status rc = MOE_OK;
   int status = 0;
+  int* const sw = h->last_status ? h->last_status : h->ctr + 2 * (size_t)kCtrHead;
   if (hipStreamSynchronize(h->last_stream) != hipSuccess ||
-      hipMemcpy(&status, h->ctr + 2 * (size_t)kCtrHead, 4, hipMemcpyDeviceToHost) != hipSuccess) {
+      hipMemcpy(&status, sw, 4, hipMemcpyDeviceToHost) != hipSuccess) {
     rc = MOE_ERR_HIP;
   } else if (status != 0) {
     rc = MOE_ERR_TIMEOUT;
     const int zero = 0;
-    if (hipMemcpy(h->ctr + 2 * (size_t)kCtrHead, &zero, 4, hipMemcpyHostToDevice) != hipSuccess) rc = MOE_ERR_HIP;
+    if (hipMemcpy(sw, &zero, 4, hipMemcpyHostToDevice) != hipSuccess) rc = MOE_ERR_HIP;
   }
   if (prev != h->device) (void)hipSetDevice(prev);
   return rc;
