@@ -56,6 +56,9 @@ class Workload:
     norm_eps: float = 1e-6
     # clipped SwiGLU limit (None: no clipping)
     swiglu_limit: float | None = None
+    # expert weight format: "fp8" (e4m3fn, fp32 group-32 scales), "mxfp8"
+    # (e4m3fn, E8M0 group-32 scales) or "mxfp4" (E2M1, E8M0 group-32 scales)
+    weight_format: str = "fp8"
 
     @property
     def router_std(self) -> float:
@@ -67,9 +70,13 @@ class Workload:
         return self.E + self.S
 
     def expert_bytes(self) -> int:
-        """FP8 weights plus fp32 group scales of one expert (gate/up + down)."""
+        """Weights plus group scales of one expert (gate/up + down): FP8
+        bytes and fp32 scales, MXFP8 bytes and E8M0 scales, or MXFP4 half
+        bytes and E8M0 scales."""
         H, I = self.H, self.I
-        return 2 * I * H + 2 * I * (H // 32) * 4 + H * I + H * (I // 32) * 4
+        elem = {"fp8": 1.0, "mxfp8": 1.0, "mxfp4": 0.5}[self.weight_format]
+        scale = 4 if self.weight_format == "fp8" else 1
+        return int(3 * I * H * elem) + 3 * I * (H // 32) * scale
 
     def with_rows(self, T: int) -> "Workload":
         return dataclasses.replace(self, T=T, name=f"{self.name}@T{T}")
@@ -91,7 +98,12 @@ WORKLOADS = [
 # around the layer).
 PRENORM = [dataclasses.replace(w, name=w.name + "_prenorm", prenorm=True) for w in WORKLOADS]
 
-BY_NAME = {w.name: w for w in WORKLOADS + PRENORM}
+# The 6-row, 1-row and tiny workloads with MX expert weights (the pages' MoE
+# formats: MXFP4 and MXFP8 with E8M0 group-32 scales).
+MX = [dataclasses.replace(w, name=f"{w.name}_{fmt}", weight_format=fmt)
+      for fmt in ("mxfp4", "mxfp8") for w in (WORKLOADS[1], WORKLOADS[2], WORKLOADS[0])]
+
+BY_NAME = {w.name: w for w in WORKLOADS + PRENORM + MX}
 
 _lib = None
 
@@ -118,6 +130,9 @@ def lib() -> ctypes.CDLL:
         L.synth_x_bf16.argtypes = [u64, u32, i32, i32, f64, vp, vp]
         L.synth_f32.argtypes = [u64, u32, u32, i32, i32, f64, vp]
         L.synth_fp8_g32.argtypes = [u64, u32, u32, i32, i32, f64, vp, vp]
+        L.synth_e2m1_encode.argtypes = [f64]
+        L.synth_e2m1_encode.restype = ctypes.c_uint8
+        L.synth_mx_g32.argtypes = [u64, u32, u32, i32, i32, f64, i32, vp, vp]
         _lib = L
     return _lib
 
@@ -199,19 +214,33 @@ def expert_matrix(w: Workload, tensor: int, slot: int, rows: int, K: int):
 
 
 def expert_weights(w: Workload):
-    """w13 [E+S][2I][H] e4m3fn (gate rows then up rows), s13 [E+S][2I][H/32],
-    w2 [E+S][H][I] e4m3fn, s2 [E+S][H][I/32].  Slot E is the shared expert."""
+    """w13 [E+S][2I][H] (gate rows then up rows), s13 [E+S][2I][H/32],
+    w2 [E+S][H][I], s2 [E+S][H][I/32].  Slot E is the shared expert.
+
+    fp8: e4m3fn codes and fp32 scales; mxfp8: e4m3fn codes and E8M0 codes;
+    mxfp4: the K axis of w13 and w2 holds bytes of two E2M1 codes (K/2
+    bytes), scales are E8M0 codes.  The same normals feed every format."""
     n = w.n_slots
-    w13 = np.empty((n, 2 * w.I, w.H), np.uint8)
-    s13 = np.empty((n, 2 * w.I, w.H // 32), np.float32)
-    w2 = np.empty((n, w.H, w.I), np.uint8)
-    s2 = np.empty((n, w.H, w.I // 32), np.float32)
+    fmt = w.weight_format
+    kb = (lambda K: K // 2) if fmt == "mxfp4" else (lambda K: K)
+    st = np.float32 if fmt == "fp8" else np.uint8
+    w13 = np.empty((n, 2 * w.I, kb(w.H)), np.uint8)
+    s13 = np.empty((n, 2 * w.I, w.H // 32), st)
+    w2 = np.empty((n, w.H, kb(w.I)), np.uint8)
+    s2 = np.empty((n, w.H, w.I // 32), st)
     L = lib()
     for e in range(n):
-        L.synth_fp8_g32(w.seed, TENSOR_W13, e, 2 * w.I, w.H, w.expert_std,
-                        _ptr(w13[e]), _ptr(s13[e]))
-        L.synth_fp8_g32(w.seed, TENSOR_W2, e, w.H, w.I, w.expert_std,
-                        _ptr(w2[e]), _ptr(s2[e]))
+        if fmt == "fp8":
+            L.synth_fp8_g32(w.seed, TENSOR_W13, e, 2 * w.I, w.H, w.expert_std,
+                            _ptr(w13[e]), _ptr(s13[e]))
+            L.synth_fp8_g32(w.seed, TENSOR_W2, e, w.H, w.I, w.expert_std,
+                            _ptr(w2[e]), _ptr(s2[e]))
+        else:
+            code = {"mxfp8": 1, "mxfp4": 2}[fmt]
+            L.synth_mx_g32(w.seed, TENSOR_W13, e, 2 * w.I, w.H, w.expert_std, code,
+                           _ptr(w13[e]), _ptr(s13[e]))
+            L.synth_mx_g32(w.seed, TENSOR_W2, e, w.H, w.I, w.expert_std, code,
+                           _ptr(w2[e]), _ptr(s2[e]))
     return w13, s13, w2, s2
 
 

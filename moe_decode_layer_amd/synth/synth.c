@@ -28,7 +28,7 @@
 #include <omp.h>
 #endif
 
-#define SYNTH_ABI 1
+#define SYNTH_ABI 2
 #define GOLDEN_GAMMA 0x9E3779B97F4A7C15ULL
 
 static inline uint64_t mix64(uint64_t z) {
@@ -95,6 +95,22 @@ uint8_t synth_e4m3fn_encode(double v) {
   int code = ((e - 1 + 7) << 3) + m;  /* m == 8 carries into the next binade */
   if (code > 0x7E) code = 0x7E;
   return sign | (uint8_t)code;
+}
+
+/* fp64 -> OCP FP4 E2M1 code (the MXFP4 element), round to nearest even,
+   saturate to +-6.  Magnitudes of codes 0..7: 0, 0.5, 1, 1.5, 2, 3, 4, 6. */
+uint8_t synth_e2m1_encode(double v) {
+  static const double mag[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+  uint8_t sign = signbit(v) ? 0x8 : 0;
+  double a = fabs(v);
+  if (isnan(v)) return 0x7;             /* no NaN code: the largest value */
+  int best = 0;
+  for (int c = 1; c < 8; ++c) {
+    double d = fabs(a - mag[c]), db = fabs(a - mag[best]);
+    if (d < db || (d == db && (c & 1) == 0)) best = c;   /* ties to the even code */
+  }
+  if (a >= 6.0) best = 7;
+  return sign | (uint8_t)best;
 }
 
 int synth_abi(void) { return SYNTH_ABI; }
@@ -184,6 +200,60 @@ void synth_fp8_g32(uint64_t seed, uint32_t tensor, uint32_t a, int32_t R, int32_
         s[(int64_t)r * G + g] = sc;
         uint8_t* qq = q + (int64_t)r * K + 32 * g;
         for (int j = 0; j < 32; ++j) qq[j] = synth_e4m3fn_encode(std * w[j] / (double)sc);
+      }
+    }
+    free(buf);
+  }
+}
+
+/*
+ * One expert matrix [R][K] of N(0, std^2) weights in an OCP MX format: each
+ * block of 32 contiguous K elements shares the scale 2^X, X = floor(log2
+ * max|w|) - emax of the element format (2 for E2M1, 8 for E4M3), clamped to
+ * [-127, 127] and stored as the E8M0 code X + 127 (an all-zero block: code
+ * 0); each element is w / 2^X encoded with round to nearest even, saturating.
+ * fmt 1: MXFP8, q [R][K] e4m3fn codes; fmt 2: MXFP4, q [R][K/2], element 2j
+ * in the low nibble of byte j.  s [R][K/32] E8M0 codes.  K a multiple of 32.
+ */
+void synth_mx_g32(uint64_t seed, uint32_t tensor, uint32_t a, int32_t R, int32_t K, double std,
+                  int32_t fmt, uint8_t* q, uint8_t* s) {
+  const int32_t G = K / 32;
+  const int emax = fmt == 2 ? 2 : 8;
+#pragma omp parallel
+  {
+    double* buf = (double*)malloc(sizeof(double) * (size_t)K);
+#pragma omp for schedule(static)
+    for (int32_t r = 0; r < R; ++r) {
+      normals(stream_key(seed, tensor, a, (uint32_t)r), K, buf);
+      for (int32_t g = 0; g < G; ++g) {
+        const double* w = buf + 32 * g;
+        double amax = 0.0;
+        for (int j = 0; j < 32; ++j) {
+          double m = fabs(std * w[j]);
+          if (m > amax) amax = m;
+        }
+        int X = -127;
+        if (amax > 0.0) {
+          int e;
+          frexp(amax, &e);               /* amax = f 2^e, f in [0.5, 1): floor(log2) = e - 1 */
+          X = e - 1 - emax;
+          if (X < -127) X = -127;
+          if (X > 127) X = 127;
+        }
+        s[(int64_t)r * G + g] = (uint8_t)(X + 127);
+        const double inv = ldexp(1.0, -X);
+        for (int j = 0; j < 32; ++j) {
+          const double v = std * w[j] * inv;
+          const int64_t k = (int64_t)32 * g + j;
+          if (fmt == 2) {
+            const uint8_t c = synth_e2m1_encode(v);
+            uint8_t* b = q + (int64_t)r * (K / 2) + k / 2;
+            if ((k & 1) == 0) *b = c;
+            else *b = (uint8_t)(*b | (c << 4));
+          } else {
+            q[(int64_t)r * K + k] = synth_e4m3fn_encode(v);
+          }
+        }
       }
     }
     free(buf);

@@ -43,6 +43,13 @@ definitions, else the plainest reading):
   * y = shared + sum_k w_k * o_k in that order, rounded to bf16 from fp64.
   * FP8 is OCP e4m3fn (bias 7, max 448, S.1111.111 is NaN, no infinities);
     dequantised weight = e4m3fn(q) * scale of its 32-element K group.
+  * MX weights ("Beyond Day-0 ...", section 3.1: MoE kernels with MXFP4
+    weights and BF16 activations; section 2.1: group32 FP8 reorganised for
+    MXFP8 kernels), as the OCP Microscaling formats define them: a block of
+    32 contiguous K elements shares one E8M0 scale 2^(e - 127) (0xFF NaN);
+    MXFP4 elements are E2M1 (bias 1, values 0, 0.5, 1, 1.5, 2, 3, 4, 6 and
+    their negatives), two per byte, the lower K index in the low nibble;
+    MXFP8 elements are e4m3fn.  Dequantised weight = element * block scale.
 
 The pre-norm block form (input RMSNorm before the router, residual added
 after the combine) follows "SGLang's Low-Latency Mode Boosts DeepSeek-V4.1-
@@ -89,6 +96,28 @@ def e4m3fn_value(code: int) -> float:
 
 E4M3FN = np.array([e4m3fn_value(c) for c in range(256)], dtype=np.float64)
 
+
+def e2m1_value(code: int) -> float:
+    """Value of one OCP FP4 E2M1 code (the MXFP4 element): sign bit 3,
+    exponent bits 2..1 with bias 1, mantissa bit 0; exponent 0 is subnormal
+    (m/2); no infinities or NaN."""
+    sign = -1.0 if code & 0x8 else 1.0
+    exp = (code >> 1) & 0x3
+    man = code & 0x1
+    if exp == 0:
+        return sign * man * 0.5
+    return sign * (1.0 + man / 2.0) * 2.0 ** (exp - 1)
+
+
+def e8m0_value(code: int) -> float:
+    """Value of one OCP E8M0 code (the MX block scale): 2^(code - 127);
+    code 0xFF is NaN."""
+    return math.nan if code == 0xFF else 2.0 ** (code - 127)
+
+
+E2M1 = np.array([e2m1_value(c) for c in range(16)], dtype=np.float64)
+E8M0 = np.array([e8m0_value(c) for c in range(256)], dtype=np.float64)
+
 BF16_MAX = (2.0 - 2.0 ** -7) * 2.0 ** 127
 
 
@@ -116,9 +145,24 @@ def bf16_value_to_bits(v: np.ndarray) -> np.ndarray:
     return (f.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
 
 
-def dequant(q: np.ndarray, s: np.ndarray) -> np.ndarray:
-    """FP8 matrix [..., N, K] with scales [..., N, K/32] -> fp64 weights."""
-    return E4M3FN[q] * np.repeat(s.astype(np.float64), GROUP, axis=-1)
+def dequant(q: np.ndarray, s: np.ndarray, fmt: str = "fp8") -> np.ndarray:
+    """Expert matrix [..., N, K] -> fp64 weights, one scale per 32 contiguous K.
+
+    fp8   : q [..., N, K] e4m3fn codes, s [..., N, K/32] fp32 scales
+    mxfp8 : q [..., N, K] e4m3fn codes, s [..., N, K/32] E8M0 codes
+    mxfp4 : q [..., N, K/2] bytes of two E2M1 codes each (element 2j in the
+            low nibble, 2j + 1 in the high one), s [..., N, K/32] E8M0 codes
+    """
+    if fmt == "fp8":
+        return E4M3FN[q] * np.repeat(s.astype(np.float64), GROUP, axis=-1)
+    scale = np.repeat(E8M0[np.asarray(s, np.uint8)], GROUP, axis=-1)
+    if fmt == "mxfp8":
+        return E4M3FN[q] * scale
+    if fmt == "mxfp4":
+        q = np.asarray(q, np.uint8)
+        codes = np.stack([q & 0xF, q >> 4], axis=-1).reshape(*q.shape[:-1], 2 * q.shape[-1])
+        return E2M1[codes] * scale
+    raise ValueError(f"unknown weight format {fmt!r}")
 
 
 def sigmoid(v: np.ndarray) -> np.ndarray:
@@ -193,19 +237,20 @@ def place(idx: np.ndarray, E: int) -> Placement:
 # --------------------------------------------------------------------------
 # Expert FFN and combine
 # --------------------------------------------------------------------------
-def expert_ffn(X: np.ndarray, w13q, s13, w2q, s2, limit=None) -> np.ndarray:
+def expert_ffn(X: np.ndarray, w13q, s13, w2q, s2, limit=None, fmt: str = "fp8") -> np.ndarray:
     """One expert on rows X [n][H]: g/u from the fused gate/up matrix (gate
     rows [0, I), up rows [I, 2I)), h = bf16(silu(g) * u), o = h @ W2^T.
-    With a limit L: g -> min(g, L), u -> clamp(u, -L, L) first."""
+    With a limit L: g -> min(g, L), u -> clamp(u, -L, L) first.  ``fmt``
+    names the weight format (see dequant)."""
     I = w13q.shape[0] // 2
-    W13 = dequant(w13q, s13)
+    W13 = dequant(w13q, s13, fmt)
     g = X @ W13[:I].T
     u = X @ W13[I:].T
     if limit is not None:
         g = np.minimum(g, float(limit))
         u = np.clip(u, -float(limit), float(limit))
     h = bf16_round(g * sigmoid(g) * u)
-    return h @ dequant(w2q, s2).T
+    return h @ dequant(w2q, s2, fmt).T
 
 
 @dataclasses.dataclass
@@ -245,7 +290,7 @@ def forward(inp, rows=None) -> Result:
             need.setdefault(E, []).append(int(t))
     for e, ts in need.items():
         out = expert_ffn(X[ts], inp.w13[e], inp.s13[e], inp.w2[e], inp.s2[e],
-                         getattr(wl, "swiglu_limit", None))
+                         getattr(wl, "swiglu_limit", None), getattr(wl, "weight_format", "fp8"))
         for i, t in enumerate(ts):
             o[(t, e)] = out[i]
     y = np.zeros((len(rows), H), np.float64)
