@@ -12,7 +12,9 @@
  *   per selected expert e (and the shared expert, slot E, for every row):
  *       g = W_gate[e] x,  u = W_up[e] x,  h = bf16(silu(g) * u),  o_e = W_down[e] h
  *       (g and u clipped first when a limit is set: moe_decode_set_swiglu_limit)
- *       (FP8 e4m3fn weights, one fp32 scale per 32 contiguous K elements)
+ *       (expert weights in one of three formats, each with one scale per 32
+ *        contiguous K elements: FP8 e4m3fn with fp32 scales, or the OCP
+ *        microscaling formats MXFP8 (e4m3fn) and MXFP4 (e2m1) with E8M0 scales)
  *   y[t] = bf16( o_shared[t] + sum_k w[t][k] * o_{idx[t][k]}[t] )
  *
  * in ONE persistent kernel launch (moe_decode_run_block runs the same layer as a
@@ -48,7 +50,7 @@
 extern "C" {
 #endif
 
-#define MOE_DECODE_ABI_VERSION 3
+#define MOE_DECODE_ABI_VERSION 4
 
 typedef int32_t moe_status;
 #define MOE_OK                0  /* success */
@@ -65,36 +67,59 @@ typedef struct moe_decode_config {
   int32_t num_experts;   /* E routed experts; 1..256 */
   int32_t top_k;         /* K experts per row; 1..min(E, 16) */
   int32_t intermediate;  /* I per expert; multiple of 32, <= 8192.  A width that is
-                            not a multiple of 64 runs padded to the next one: the
-                            padding rows and columns get zero weights, so results are
-                            those of width I (the per-GPU width 288 of TP8 padded to
-                            320: "Beyond Day-0: Optimizing DeepSeek-V4.1 Flash in
-                            SGLang", section 3.1) */
+                            not a multiple of 64 runs padded to the next one (in
+                            every weight format): the padding rows and columns get
+                            zero weights, so results are those of width I (the
+                            per-GPU width 288 of TP8 padded to 320 for MXFP4
+                            experts: "Beyond Day-0: Optimizing DeepSeek-V4.1 Flash
+                            in SGLang", section 3.1) */
   int32_t num_shared;    /* S always-on shared experts; 0 or 1 */
   int32_t deadline_us;   /* bound on every in-kernel wait, microseconds; 0 = 1 s */
-  uint32_t flags;        /* reserved; must be 0 */
+  uint32_t flags;        /* bits 0-1: expert weight format, MOE_WEIGHTS_*; other
+                            bits reserved, must be 0 (else MOE_ERR_INVALID_ARG) */
 } moe_decode_config;
 
 /*
+ * Expert weight formats (config flags, bits 0-1).  All three quantise the
+ * expert matrices along K (H for gate/up, I for down) in groups of 32
+ * contiguous elements that share one scale; a weight is decode(q) * scale.
+ *   MOE_WEIGHTS_FP8    e4m3fn codes, fp32 scales.
+ *   MOE_WEIGHTS_MXFP8  e4m3fn codes, E8M0 scales (one byte e: 2^(e - 127); 255
+ *                      is NaN and must not occur).  OCP Microscaling (MX)
+ *                      v1.0 formats.
+ *   MOE_WEIGHTS_MXFP4  e2m1 codes (values 0, 0.5, 1, 1.5, 2, 3, 4, 6 and their
+ *                      negatives), two per byte, element 2j in the low nibble
+ *                      of byte j; E8M0 scales.
+ * Sources: "Beyond Day-0: Optimizing DeepSeek-V4.1 Flash in SGLang", section
+ * 2.1 (group-32 FP8 expert weights and scales) and the MXFP4 / MXFP8 expert
+ * weights of the same model's checkpoints that the pages name.
+ */
+#define MOE_WEIGHTS_FP8   0u
+#define MOE_WEIGHTS_MXFP8 1u
+#define MOE_WEIGHTS_MXFP4 2u
+
+/*
  * Weights, all device pointers, row-major and contiguous.  create() reads
- * them once (it re-lays the FP8 matrices out into the kernel's tile order in
- * memory the handle owns), so the caller may free them after create returns.
+ * them once (it re-lays the expert matrices out into the kernel's tile order
+ * in memory the handle owns), so the caller may free them after create
+ * returns.  B = bytes per row of K elements: K (FP8, MXFP8) or K / 2 (MXFP4).
  *   router_w    [E][H]               fp32
  *   router_bias [E]                  fp32, or NULL for no bias
- *   w13         [E+S][2I][H]         FP8 e4m3fn (OCP); rows [0,I) gate, [I,2I) up
- *   s13         [E+S][2I][H/32]      fp32 scale of each 32 contiguous K elements
- *   w2          [E+S][H][I]          FP8 e4m3fn (down projection)
- *   s2          [E+S][H][I/32]       fp32
+ *   w13         [E+S][2I][B(H)]      expert codes; rows [0,I) gate, [I,2I) up
+ *   s13         [E+S][2I][H/32]      scale of each 32 contiguous K elements:
+ *                                    fp32 (FP8) or uint8 E8M0 (MX formats)
+ *   w2          [E+S][H][B(I)]       expert codes (down projection)
+ *   s2          [E+S][H][I/32]       fp32 or uint8 E8M0, as s13
  * Slot E (the last) is the shared expert when S = 1.  A weight's value is
- * e4m3fn(q) * scale; codes 0x7F/0xFF (NaN) must not occur.
+ * decode(q) * scale; e4m3fn codes 0x7F/0xFF (NaN) must not occur.
  */
 typedef struct moe_decode_weights {
   const float* router_w;
   const float* router_bias;
   const uint8_t* w13;
-  const float* s13;
+  const void* s13;
   const uint8_t* w2;
-  const float* s2;
+  const void* s2;
 } moe_decode_weights;
 
 /*

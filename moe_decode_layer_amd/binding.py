@@ -19,6 +19,13 @@ MOE_ERR_HIP = 3
 MOE_ERR_OUT_OF_MEMORY = 4
 MOE_ERR_TIMEOUT = 5
 
+# Expert weight formats (config flags, bits 0-1) and, per format, the bytes
+# of codes per 2 elements and the scale dtype.
+MOE_WEIGHTS_FP8 = 0
+MOE_WEIGHTS_MXFP8 = 1
+MOE_WEIGHTS_MXFP4 = 2
+WEIGHT_FORMATS = {"fp8": MOE_WEIGHTS_FP8, "mxfp8": MOE_WEIGHTS_MXFP8, "mxfp4": MOE_WEIGHTS_MXFP4}
+
 # Functions declared in include/moe_decode.h, in declaration order.
 EXPORTS = (
     "moe_decode_abi_version",
@@ -174,8 +181,24 @@ def moe_decode_destroy(h) -> None:
 
 
 # ---- convenience layer over torch tensors ---------------------------------
-def make_config(T_max, H, E, K, I, S, deadline_us=0) -> moe_decode_config:
-    return moe_decode_config(T_max, H, E, K, I, S, deadline_us, 0)
+def make_config(T_max, H, E, K, I, S, deadline_us=0, weight_format: str = "fp8") -> moe_decode_config:
+    return moe_decode_config(T_max, H, E, K, I, S, deadline_us, WEIGHT_FORMATS[weight_format])
+
+
+def weight_layout(cfg: moe_decode_config, bias: bool = False) -> dict:
+    """Element type name and element count of each weight array the header
+    gives for the config's format: codes one byte per element (MXFP4: two
+    elements per byte), scales fp32 (FP8) or E8M0 bytes (MX), one per 32 K."""
+    fmt = cfg.flags & 3
+    E, S, H, I = cfg.num_experts, cfg.num_shared, cfg.hidden, cfg.intermediate
+    codes = (lambda n: n // 2) if fmt == MOE_WEIGHTS_MXFP4 else (lambda n: n)
+    scale = "float32" if fmt == MOE_WEIGHTS_FP8 else "uint8"
+    out = {"router_w": ("float32", E * H), "w13": ("uint8", (E + S) * 2 * I * codes(H)),
+           "s13": (scale, (E + S) * 2 * I * (H // 32)), "w2": ("uint8", (E + S) * H * codes(I)),
+           "s2": (scale, (E + S) * H * (I // 32))}
+    if bias:
+        out["router_bias"] = ("float32", E)
+    return out
 
 
 def _ptr(t) -> int | None:
@@ -190,9 +213,7 @@ class MoeDecode:
     """
 
     def __init__(self, cfg: moe_decode_config, weights: dict, device: int = 0):
-        for name in ("router_w", "w13", "s13", "w2", "s2"):
-            t = weights[name]
-            assert t.is_cuda and t.is_contiguous(), name
+        self._check_weights(cfg, weights, device)
         w = moe_decode_weights(_ptr(weights["router_w"]), _ptr(weights.get("router_bias")),
                                _ptr(weights["w13"]), _ptr(weights["s13"]),
                                _ptr(weights["w2"]), _ptr(weights["s2"]))
@@ -202,6 +223,18 @@ class MoeDecode:
         self.cfg = cfg
         self.device = device
         self.handle = h
+
+    @staticmethod
+    def _check_weights(cfg: moe_decode_config, weights: dict, device: int) -> None:
+        """Every weight tensor contiguous, on the device, with the element type
+        and count of weight_layout (create reads them whole: a short tensor
+        would be read past its end)."""
+        for name, (dtype, n) in weight_layout(cfg, weights.get("router_bias") is not None).items():
+            t = weights[name]
+            if not (t.is_cuda and t.device.index == device and t.is_contiguous()):
+                raise ValueError(f"{name}: must be a contiguous tensor on cuda:{device}")
+            if str(t.dtype).removeprefix("torch.") != dtype or t.numel() != n:
+                raise ValueError(f"{name}: expected {n} elements of {dtype}, got {t.numel()} of {t.dtype}")
 
     def _check_rows(self, name: str, t, T: int) -> None:
         """x and y: 2-byte elements, contiguous, on the handle's device, at

@@ -43,18 +43,19 @@
 // Clipped SwiGLU caps g and clamps u at a caller-set limit in every gate/up
 // epilogue (+inf by default).
 //
-// Expert weights are re-laid out once, at create time, into 1 KiB tiles of
-// 16 weight rows x 64 K: lane l of a wave reads bytes [16 l, 16 l + 16) of a
-// tile, so every wave-wide weight load is one contiguous KiB.  Lane l =
-// (n, kq), n = l % 16, kq = l / 16, holds row n's K elements [8 kq, 8 kq + 8)
-// of the tile's first 32-element group and the same of its second group:
-// exactly the B operand of v_mfma_f32_16x16x32_bf16, one scale group per
-// instruction.  The fp32 result of each MFMA is multiplied by its group's
-// scale and accumulated.  FP8 e4m3fn -> bf16 is exact
-// (v_cvt_scalef32_pk_bf16_fp8 with scale 1) and bf16 x bf16 products are
-// exact in fp32, so the only rounding before the declared bf16 points is
-// fp32 accumulation.  Activation rows are the A operand; rows past the
-// expert's row count are zero.
+// Expert weights are re-laid out once, at create time, into tiles of 16
+// weight rows x 64 K (1 KiB of FP8 or MXFP8, 512 B of MXFP4): lane l of a
+// wave reads the l-th 16 (MXFP4: 8) bytes of a tile, so every wave-wide
+// weight load is one contiguous block.  Lane l = (n, kq), n = l % 16,
+// kq = l / 16, holds row n's K elements [8 kq, 8 kq + 8) of the tile's first
+// 32-element group and the same of its second group: exactly the B operand
+// of v_mfma_f32_16x16x32_bf16, one scale group per instruction.  The fp32
+// result of each MFMA is multiplied by its group's scale (fp32, or E8M0 as
+// a power of two) and accumulated.  FP8 e4m3fn and FP4 e2m1 -> bf16 are
+// exact (v_cvt_scalef32_pk_bf16_fp8 / _fp4 with scale 1) and bf16 x bf16
+// products are exact in fp32, so the only rounding before the declared bf16
+// points is fp32 accumulation.  Activation rows are the A operand; rows past
+// the expert's row count are zero.
 #include <hip/hip_runtime.h>
 
 #include <limits.h>
@@ -176,10 +177,13 @@ struct Params {
   const float* router_w;
   const float* router_b;   // [E] (without a bias: any readable [E] floats, unused)
   int has_bias;
-  const u32x4* w13p;   // [E+S][2I/16][H/64][64] tiles
-  const float* s13p;   // [E+S][2I/16][H/64][16][2]
-  const u32x4* w2p;    // [E+S][H/16][I/64][64]
-  const float* s2p;    // [E+S][H/16][I/64][16][2]
+  // expert weights in 16 x 64 tiles of the format (WFmt<fmt>::W per lane) and
+  // one WFmt<fmt>::Scale per tile row
+  const void* w13p;    // [E+S][2I/16][H/64][64] tiles
+  const void* s13p;    // [E+S][2I/16][H/64][16]
+  const void* w2p;     // [E+S][H/16][I/64][64]
+  const void* s2p;     // [E+S][H/16][I/64][16]
+  size_t w13_bytes, s13_bytes, w2_bytes, s2_bytes;   // packed sizes (page touching)
   // workspace.  Words handed between workgroups carry the run's epoch in
   // their high half (see "Tagged hand-offs" below).
   uint64_t* lgt;       // [T][E] router logits (fp32 bits | epoch); tiles: [router_ks][T][E] partials
@@ -279,6 +283,49 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint32_t lo, uint32_t hi) {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
+// 8 FP4 E2M1 codes (one dword; byte j holds codes 2j, 2j + 1 in its low and
+// high nibble) -> 8 bf16, exact (v_cvt_scalef32_pk_bf16_fp4 with scale 1).
+__device__ __forceinline__ bf16x8 fp4x8_to_bf16(uint32_t v) {
+  bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, 1.0f, 0);
+  bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, 1.0f, 1);
+  bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, 1.0f, 2);
+  bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, 1.0f, 3);
+  bf16x8 r = {a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+  return r;
+}
+
+// E8M0 block scale 2^(e - 127) as fp32 (exact; e = 0 is the fp32 subnormal
+// 2^-127, e = 255 NaN).
+__device__ __forceinline__ float e8m0_to_f32(uint32_t e) {
+  return __uint_as_float(e == 0u ? 0x00400000u : e == 255u ? 0x7fc00000u : e << 23);
+}
+
+// Expert weight formats (fixed at create).  Every format tiles a matrix into
+// 16 rows x 64 K (two scale groups of 32); lane (n, kq) of a wave holds row
+// n's K [32 g + 8 kq, 32 g + 8 kq + 8) of both groups g: the B operand of one
+// v_mfma_f32_16x16x32_bf16 per group.  A wave-wide load of a tile is one
+// contiguous block (1 KiB, MXFP4 512 B).
+//   0 FP8: e4m3fn, one fp32 scale per group     (16 bytes per lane; scales f32x2 per row)
+//   1 MXFP8: e4m3fn, one E8M0 scale per group   (16 bytes per lane; scales 2 bytes per row)
+//   2 MXFP4: E2M1, one E8M0 scale per group     (8 bytes per lane; scales 2 bytes per row)
+// Elements decode exactly to bf16; the group's scale multiplies the fp32
+// result of its MFMA (a power of two for E8M0: exact).
+constexpr int kFmtFp8 = 0, kFmtMxfp8 = 1, kFmtMxfp4 = 2;
+template <int FMT> struct WFmt;
+template <> struct WFmt<kFmtFp8> { typedef u32x4 W; typedef f32x2 Scale; };
+template <> struct WFmt<kFmtMxfp8> { typedef u32x4 W; typedef uint16_t Scale; };
+template <> struct WFmt<kFmtMxfp4> { typedef u32x2 W; typedef uint16_t Scale; };
+
+template <int FMT>
+__device__ __forceinline__ bf16x8 wdecode(const typename WFmt<FMT>::W& w, int g) {
+  if constexpr (FMT == kFmtMxfp4) return fp4x8_to_bf16(w[g]);
+  else return fp8x8_to_bf16(w[2 * g], w[2 * g + 1]);
+}
+// Scale of group g of an MX tile row.  (The FP8 format's fp32 scales are
+// read at each use directly: routed through a helper, even an inlined one,
+// they cost the items registers and spills.)
+__device__ __forceinline__ float mx_scale(uint32_t s, int g) { return e8m0_to_f32((s >> (8 * g)) & 0xffu); }
+
 __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b) {
   const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, zero, 0, 0, 0);
@@ -295,6 +342,12 @@ __device__ __forceinline__ u32x4 ld_stream(const u32x4* p) {
 // ones in a read-only sweep on this GPU).
 __device__ __forceinline__ f32x2 ld_stream(const f32x2* p) {
   return __builtin_nontemporal_load((const GLOBAL f32x2*)p);
+}
+__device__ __forceinline__ uint16_t ld_stream(const uint16_t* p) {
+  return __builtin_nontemporal_load((const GLOBAL uint16_t*)p);
+}
+__device__ __forceinline__ u32x2 ld_stream(const u32x2* p) {
+  return __builtin_nontemporal_load((const GLOBAL u32x2*)p);
 }
 template <typename T>
 __device__ __forceinline__ void st(T* p, T v) { *(GLOBAL T*)p = v; }
@@ -1146,9 +1199,7 @@ constexpr size_t kPageBytes = size_t(1) << 21;
 __device__ __forceinline__ uint32_t touch_weight_pages(KParams& p, int i, int n) {
   const int per = n / 8, r = i / 8;
   if (per < 1 || r >= per) return 0;
-  const size_t slots = (size_t)p.E + p.S;
-  const size_t b13 = slots * 2 * p.I * p.H, b2 = slots * p.H * p.I;
-  const size_t bs13 = b13 / 32 * 4, bs2 = b2 / 32 * 4;
+  const size_t b13 = p.w13_bytes, b2 = p.w2_bytes, bs13 = p.s13_bytes, bs2 = p.s2_bytes;
   const size_t n13 = (b13 + kPageBytes - 1) / kPageBytes, n2 = (b2 + kPageBytes - 1) / kPageBytes;
   const size_t ns13 = (bs13 + kPageBytes - 1) / kPageBytes, ns2 = (bs2 + kPageBytes - 1) / kPageBytes;
   uint32_t acc = 0;
@@ -1414,28 +1465,30 @@ __device__ __forceinline__ bool combine_item(KParams& p, const Lds& L, int rc, i
 // columns.  XL: the activation rows are read from LDS (small batches),
 // otherwise from global memory in the same pipeline as the weights.
 // ----------------------------------------------------------------------------
-template <int NMB, bool XL>
+template <int NMB, bool XL, int FMT>
 struct GuStage {
   // tiles per stage (two stages are in flight)
   static constexpr int D = XL ? 4 : (NMB == 1 ? 2 : 1);
-  u32x4 w[D];
-  f32x2 s[D];
+  typename WFmt<FMT>::W w[D];
+  typename WFmt<FMT>::Scale s[D];
   u32x4 a[XL ? 1 : D][2][NMB];
 };
 
-template <int NMB, bool XL, int NMBMAX>
+template <int NMB, bool XL, int NMBMAX, int FMT>
 __device__ __forceinline__ void gu_item(KParams& p, const Lds& L, int slot, int sbase, int r0, int nrows,
                         int rb, bool shared, int parity, int& pend) {
   flush_pending_now(L.ctr, pend);
-  using Stage = GuStage<NMB, XL>;
+  using Stage = GuStage<NMB, XL, FMT>;
+  using Wt = typename WFmt<FMT>::W;
+  using Sc = typename WFmt<FMT>::Scale;
   constexpr int D = Stage::D;
   const int w = wave_id(), lane = lane_id();
   const int n = lane & 15, kq = lane >> 4;
   const int nq = p.n_q13;
   const int nj = (nq - w + kWaves - 1) / kWaves;     // tiles of this wave
   const size_t blk = (size_t)slot * p.n_rb13 + rb;
-  const u32x4* wt = p.w13p + blk * nq * kWave + lane;
-  const f32x2* sc = (const f32x2*)p.s13p + blk * nq * kTileRows + n;
+  const Wt* wt = (const Wt*)p.w13p + blk * nq * kWave + lane;
+  const Sc* sc = (const Sc*)p.s13p + blk * nq * kTileRows + n;
 
   // A operand rows: token of expert row r0 + mb*16 + n.  Rows past nrows read
   // row r0 (always valid) and are zeroed before the MFMA, so every load is
@@ -1480,8 +1533,10 @@ __device__ __forceinline__ void gu_item(KParams& p, const Lds& L, int slot, int 
         const int q = w + kWaves * (j0 + u);
 #pragma unroll
         for (int g = 0; g < 2; ++g) {
-          const bf16x8 b = fp8x8_to_bf16(S.w[u][2 * g], S.w[u][2 * g + 1]);
-          const float s = g ? S.s[u].y : S.s[u].x;
+          const bf16x8 b = wdecode<FMT>(S.w[u], g);
+          float s;
+          if constexpr (FMT == kFmtFp8) s = g ? S.s[u].y : S.s[u].x;
+          else s = mx_scale(S.s[u], g);
 #pragma unroll
           for (int mb = 0; mb < NMB; ++mb) {
             u32x4 a;
@@ -1538,19 +1593,21 @@ __device__ __forceinline__ void gu_item(KParams& p, const Lds& L, int slot, int 
 // the item's h rows (<= 16) are staged in LDS first; otherwise they are read
 // from global memory in the weight pipeline.
 // ----------------------------------------------------------------------------
-template <int NMB, bool HL>
+template <int NMB, bool HL, int FMT>
 struct DnStage {
   static constexpr int D = HL ? 4 : (NMB == 1 ? 2 : 1);
-  u32x4 w[D][2];
-  f32x2 s[D][2];
+  typename WFmt<FMT>::W w[D][2];
+  typename WFmt<FMT>::Scale s[D][2];
   u32x4 a[HL ? 1 : D][2][NMB];
 };
 
-template <int NMB, bool HL>
+template <int NMB, bool HL, int FMT>
 __device__ __forceinline__ bool down_item(KParams& p, const Lds& L, int slot, int sbase, int r0, int nrows,
                           int rg, int h_target, int& pend) {
   flush_pending_now(L.ctr, pend);
-  using Stage = DnStage<NMB, HL>;
+  using Stage = DnStage<NMB, HL, FMT>;
+  using Wt = typename WFmt<FMT>::W;
+  using Sc = typename WFmt<FMT>::Scale;
   constexpr int D = Stage::D;
   const int w = wave_id(), lane = lane_id();
   const int n = lane & 15, kq = lane >> 4;
@@ -1573,13 +1630,13 @@ __device__ __forceinline__ bool down_item(KParams& p, const Lds& L, int slot, in
   }
   // a wave with a single row block (last group of a ragged H) loads that
   // block twice and stores only the first copy
-  const u32x4* wt[2];
-  const f32x2* sc[2];
+  const Wt* wt[2];
+  const Sc* sc[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const size_t blk = (size_t)slot * p.n_rb2 + min(rb0 + min(j, nrb_eff - 1), p.n_rb2 - 1);
-    wt[j] = p.w2p + blk * nq * kWave + lane;
-    sc[j] = (const f32x2*)p.s2p + blk * nq * kTileRows + n;
+    wt[j] = (const Wt*)p.w2p + blk * nq * kWave + lane;
+    sc[j] = (const Sc*)p.s2p + blk * nq * kTileRows + n;
   }
   auto load = [&](Stage& S, int q0) __attribute__((always_inline)) {
 #pragma unroll
@@ -1621,8 +1678,10 @@ __device__ __forceinline__ bool down_item(KParams& p, const Lds& L, int slot, in
           }
 #pragma unroll
           for (int j = 0; j < 2; ++j) {
-            const bf16x8 b = fp8x8_to_bf16(S.w[u][j][2 * g], S.w[u][j][2 * g + 1]);
-            const float s = g ? S.s[u][j].y : S.s[u][j].x;
+            const bf16x8 b = wdecode<FMT>(S.w[u][j], g);
+            float s;
+            if constexpr (FMT == kFmtFp8) s = g ? S.s[u][j].y : S.s[u][j].x;
+            else s = mx_scale(S.s[u][j], g);
 #pragma unroll
             for (int mb = 0; mb < NMB; ++mb) acc[j][mb] += s * mfma16(as_bf16x8(a[mb]), b);
           }
@@ -1675,17 +1734,19 @@ __device__ __forceinline__ bool down_item(KParams& p, const Lds& L, int slot, in
 // start of the item (16 KiB in flight per wave), then consumed in order, so
 // each MFMA waits only for its own tile.
 // ----------------------------------------------------------------------------
-template <int NJ>
+template <int NJ, int FMT>
 __device__ __forceinline__ void gu_item_full(KParams& p, const Lds& L, int slot, int sbase, int r0, int nrows,
                              int rb, bool shared, int parity, int& pend) {
+  using Wt = typename WFmt<FMT>::W;
+  using Sc = typename WFmt<FMT>::Scale;
   const int w = wave_id(), lane = lane_id();
   const int n = lane & 15, kq = lane >> 4;
   const int nq = p.n_q13;                            // == 4 * NJ
   const size_t blk = (size_t)slot * p.n_rb13 + rb;
-  const u32x4* wt = p.w13p + (blk * nq + w) * kWave + lane;
-  const f32x2* sc = (const f32x2*)p.s13p + (blk * nq + w) * kTileRows + n;
-  u32x4 wv[NJ];
-  f32x2 sv[NJ];
+  const Wt* wt = (const Wt*)p.w13p + (blk * nq + w) * kWave + lane;
+  const Sc* sc = (const Sc*)p.s13p + (blk * nq + w) * kTileRows + n;
+  Wt wv[NJ];
+  Sc sv[NJ];
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
     wv[j] = ld_stream(wt + (size_t)j * kWaves * kWave);
@@ -1703,8 +1764,11 @@ __device__ __forceinline__ void gu_item_full(KParams& p, const Lds& L, int slot,
     for (int g = 0; g < 2; ++g) {
       u32x4 a = *(const SHARED u32x4*)(arow + kTileK * kWaves * j + kGroup * g);
       a = aval ? a : zero4;
-      const bf16x8 b = fp8x8_to_bf16(wv[j][2 * g], wv[j][2 * g + 1]);
-      acc += (g ? sv[j].y : sv[j].x) * mfma16(as_bf16x8(a), b);
+      const bf16x8 b = wdecode<FMT>(wv[j], g);
+      float s;
+      if constexpr (FMT == kFmtFp8) s = g ? sv[j].y : sv[j].x;
+      else s = mx_scale(sv[j], g);
+      acc += s * mfma16(as_bf16x8(a), b);
     }
   }
   SHARED f32x4* red = (SHARED f32x4*)L.red + (parity & 1) * kWaves * kWave;
@@ -1729,9 +1793,11 @@ __device__ __forceinline__ void gu_item_full(KParams& p, const Lds& L, int slot,
   }
 }
 
-template <int NQ>
+template <int NQ, int FMT>
 __device__ __forceinline__ bool down_item_full(KParams& p, const Lds& L, int slot, int sbase, int r0, int nrows,
                                int rg, int h_target, int& pend) {
+  using Wt = typename WFmt<FMT>::W;
+  using Sc = typename WFmt<FMT>::Scale;
   const int w = wave_id(), lane = lane_id();
   const int n = lane & 15, kq = lane >> 4;
   const int rb0 = rg * (kDownRows / kTileRows) + 2 * w;
@@ -1744,13 +1810,13 @@ __device__ __forceinline__ bool down_item_full(KParams& p, const Lds& L, int slo
   const int nh = nrows * per_row;
   const bool fast = nh <= kHFast * kThreads;
   const uint64_t* hsrc = p.h_scr + (size_t)(sbase + r0) * per_row;
-  u32x4 wv[2][NQ];
-  f32x2 sv[2][NQ];
+  Wt wv[2][NQ];
+  Sc sv[2][NQ];
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const size_t blk = (size_t)slot * p.n_rb2 + min(rb0 + j, p.n_rb2 - 1);
-    const u32x4* wt = p.w2p + blk * NQ * kWave + lane;
-    const f32x2* sc = (const f32x2*)p.s2p + blk * NQ * kTileRows + n;
+    const Wt* wt = (const Wt*)p.w2p + blk * NQ * kWave + lane;
+    const Sc* sc = (const Sc*)p.s2p + blk * NQ * kTileRows + n;
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
       wv[j][q] = ld_stream(wt + (size_t)q * kWave);
@@ -1806,8 +1872,11 @@ __device__ __forceinline__ bool down_item_full(KParams& p, const Lds& L, int slo
       a = aval ? a : zero4;
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        const bf16x8 b = fp8x8_to_bf16(wv[j][q][2 * g], wv[j][q][2 * g + 1]);
-        acc[j] += (g ? sv[j][q].y : sv[j][q].x) * mfma16(as_bf16x8(a), b);
+        const bf16x8 b = wdecode<FMT>(wv[j][q], g);
+        float s;
+        if constexpr (FMT == kFmtFp8) s = g ? sv[j][q].y : sv[j][q].x;
+        else s = mx_scale(sv[j][q], g);
+        acc[j] += s * mfma16(as_bf16x8(a), b);
       }
     }
   }
@@ -1852,7 +1921,7 @@ __device__ __forceinline__ void gu_item_wide(KParams& p, const Lds& L, int slot,
 #pragma unroll
   for (int r = 0; r < kWideRb; ++r) {
     const size_t blk = (size_t)slot * p.n_rb13 + kWideRb * rg + r;
-    wt[r] = p.w13p + (blk * nq + q0) * kWave + lane;
+    wt[r] = (const u32x4*)p.w13p + (blk * nq + q0) * kWave + lane;
     sc[r] = (const f32x2*)p.s13p + (blk * nq + q0) * kTileRows + n;
   }
   // A operand rows: rows past nrows read row r0 and are zeroed before the MFMA
@@ -1976,7 +2045,7 @@ __device__ __forceinline__ bool dn_item_wide(KParams& p, const Lds& L, int slot,
   const int n = lane & 15, kq = lane >> 4;
   const int grp = rg * kWaves + w;             // this wave's 128-column group
   const size_t blk0 = (size_t)slot * p.n_rb2 + (size_t)grp * NB;
-  const u32x4* wt = p.w2p + blk0 * NQ * kWave + lane;
+  const u32x4* wt = (const u32x4*)p.w2p + blk0 * NQ * kWave + lane;
   const f32x2* sc = (const f32x2*)p.s2p + blk0 * NQ * kTileRows + n;
   // tile t = NB q + b is K tile q of row block b
   static_assert(P % NB == 0 && NT % P == 0, "tile ring");
@@ -2180,11 +2249,14 @@ __device__ bool wait_rows(KParams& p, const Lds& L, int t0, int n) {
 // The persistent kernel
 // ----------------------------------------------------------------------------
 // FULL: the variant for x in LDS with the full-tile gate/up and down items
-// (H = 64 kFullTiles, I = 32 kFullTiles) and local routing only; the other
-// variants hold the general code.  Each variant carries only the code its
-// batches reach, which keeps register pressure (and spills) down.
-template <int NMBMAX, bool XL, bool FULL, bool WIDE, int NQ2 = kFullTiles / 2, bool NORM = false>
+// (H = 64 kFullTiles, I = 32 kFullTiles or, NQ2 = kFullTiles / 2 + 1, 576)
+// and local routing only; the other variants hold the general code.  Each variant
+// carries only the code its batches reach, which keeps register pressure
+// (and spills) down.  FMT: the expert weight format (WFmt); the wide items
+// exist for FP8 only.
+template <int NMBMAX, bool XL, bool FULL, bool WIDE, int NQ2 = kFullTiles / 2, bool NORM = false, int FMT = kFmtFp8>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(NMBMAX == 1 || WIDE ? 2 : 1))) moe_decode_kernel(Params arg) {
+  static_assert(!WIDE || FMT == kFmtFp8, "wide items read FP8 tiles");
   KParams& p = *(const CONSTANT Params*)__builtin_amdgcn_kernarg_segment_ptr();
   (void)arg;
   extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -2363,11 +2435,11 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
     if constexpr (WIDE) {
       if (nmb <= 1) gu_item_wide<1>(p, L, slot, sbase, r0, nrows, rb, shared, pend_rg);
       else gu_item_wide<2>(p, L, slot, sbase, r0, nrows, rb, shared, pend_rg);
-    } else if constexpr (FULL) gu_item_full<kFullTiles>(p, L, slot, sbase, r0, nrows, rb, shared, par, pend_rg);
-    else if (NMBMAX == 1 || nmb <= 1) gu_item<1, XL, NMBMAX>(p, L, slot, sbase, r0, nrows, rb, shared, par, pend_rg);
-    else if (nmb == 2) gu_item<NMBMAX >= 2 ? 2 : 1, XL, NMBMAX>(p, L, slot, sbase, r0, nrows, rb, shared, par, pend_rg);
-    else if (nmb == 3) gu_item<NMBMAX >= 3 ? 3 : 1, XL, NMBMAX>(p, L, slot, sbase, r0, nrows, rb, shared, par, pend_rg);
-    else gu_item<NMBMAX >= 4 ? 4 : 1, XL, NMBMAX>(p, L, slot, sbase, r0, nrows, rb, shared, par, pend_rg);
+    } else if constexpr (FULL) gu_item_full<kFullTiles, FMT>(p, L, slot, sbase, r0, nrows, rb, shared, par, pend_rg);
+    else if (NMBMAX == 1 || nmb <= 1) gu_item<1, XL, NMBMAX, FMT>(p, L, slot, sbase, r0, nrows, rb, shared, par, pend_rg);
+    else if (nmb == 2) gu_item<NMBMAX >= 2 ? 2 : 1, XL, NMBMAX, FMT>(p, L, slot, sbase, r0, nrows, rb, shared, par, pend_rg);
+    else if (nmb == 3) gu_item<NMBMAX >= 3 ? 3 : 1, XL, NMBMAX, FMT>(p, L, slot, sbase, r0, nrows, rb, shared, par, pend_rg);
+    else gu_item<NMBMAX >= 4 ? 4 : 1, XL, NMBMAX, FMT>(p, L, slot, sbase, r0, nrows, rb, shared, par, pend_rg);
   };
   // a down item waits (after issuing its first weight loads) until its
   // expert's gate/up items have counted in ht publications
@@ -2376,12 +2448,12 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
     if constexpr (WIDE) {
       if (nmb <= 1) return dn_item_wide<1>(p, L, slot, sbase, r0, nrows, rg, ht, pend_rg);
       return dn_item_wide<2>(p, L, slot, sbase, r0, nrows, rg, ht, pend_rg);
-    } else if constexpr (FULL) return down_item_full<NQ2>(p, L, slot, sbase, r0, nrows, rg, ht, pend_rg);
-    else if (XL && p.hs_stride > 0) return down_item<1, XL>(p, L, slot, sbase, r0, nrows, rg, ht, pend_rg);
-    else if (NMBMAX == 1 || nmb <= 1) return down_item<1, false>(p, L, slot, sbase, r0, nrows, rg, ht, pend_rg);
-    else if (nmb == 2) return down_item<NMBMAX >= 2 ? 2 : 1, false>(p, L, slot, sbase, r0, nrows, rg, ht, pend_rg);
-    else if (nmb == 3) return down_item<NMBMAX >= 3 ? 3 : 1, false>(p, L, slot, sbase, r0, nrows, rg, ht, pend_rg);
-    else return down_item<NMBMAX >= 4 ? 4 : 1, false>(p, L, slot, sbase, r0, nrows, rg, ht, pend_rg);
+    } else if constexpr (FULL) return down_item_full<NQ2, FMT>(p, L, slot, sbase, r0, nrows, rg, ht, pend_rg);
+    else if (XL && p.hs_stride > 0) return down_item<1, XL, FMT>(p, L, slot, sbase, r0, nrows, rg, ht, pend_rg);
+    else if (NMBMAX == 1 || nmb <= 1) return down_item<1, false, FMT>(p, L, slot, sbase, r0, nrows, rg, ht, pend_rg);
+    else if (nmb == 2) return down_item<NMBMAX >= 2 ? 2 : 1, false, FMT>(p, L, slot, sbase, r0, nrows, rg, ht, pend_rg);
+    else if (nmb == 3) return down_item<NMBMAX >= 3 ? 3 : 1, false, FMT>(p, L, slot, sbase, r0, nrows, rg, ht, pend_rg);
+    else return down_item<NMBMAX >= 4 ? 4 : 1, false, FMT>(p, L, slot, sbase, r0, nrows, rg, ht, pend_rg);
   };
   // gate/up publications an expert's down items wait for: per gate/up row
   // block, one per 16-row MFMA block (wide items: one per 32-row M-range)
@@ -2557,23 +2629,29 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
 }
 
 // ----------------------------------------------------------------------------
-// Weight re-layout (create time): standard [rows][K] FP8 + [rows][K/32] fp32
-// scales -> 1 KiB tiles (see the top of this file).  For the gate/up matrix
-// row block rb holds gate rows 8 rb .. 8 rb + 7 then up rows I + 8 rb ..
-// I + 8 rb + 7.  An intermediate width I that is a multiple of 32 but not of
-// 64 is padded to the next multiple of 64 (I_p): the padding gate and up rows
-// and the padding down-projection columns get zero weights and zero scales,
-// so their g, u and h are exactly 0 and they add nothing to any sum ("Beyond
-// Day-0: Optimizing DeepSeek-V4.1 Flash in SGLang", section 3.1: the
-// per-GPU width 288 of TP8 is padded to 320 after sharding).
+// Weight re-layout (create time): standard row-major weights and group-32
+// scales -> 16 x 64 tiles of the format (WFmt).  Source rows: FP8 and MXFP8 one
+// byte per element, MXFP4 two elements per byte (element 2j in the low nibble
+// of byte j); scales [rows][K/32] fp32 (FP8) or E8M0 bytes (MX).  For the
+// gate/up matrix row block rb holds gate rows 8 rb .. 8 rb + 7 then up rows
+// I + 8 rb .. I + 8 rb + 7.  An intermediate width I that is a multiple of 32
+// but not of 64 is padded to the next multiple of 64 (I_p): the padding
+// gate and up rows and the padding down-projection columns get zero weights
+// and zero scales (E8M0 byte 0), so their g, u and h are exactly 0 and they
+// add nothing to any sum ("Beyond Day-0: Optimizing DeepSeek-V4.1 Flash in
+// SGLang", section 3.1: the per-GPU width 288 of TP8 is padded to 320 after
+// sharding).
 //   rows_p, K_p   : packed rows and K (multiples of 16 and 64)
 //   rows_s, K_s   : the caller's rows and K (K_s a multiple of 32)
 //   half_p, half_s: gate/up matrix: I_p and I (0 for the down projection)
 // ----------------------------------------------------------------------------
-__global__ void pack_kernel(const uint8_t* __restrict__ w, const float* __restrict__ s,
-                            u32x4* __restrict__ wp, float* __restrict__ sp, int slots, int rows_p,
+template <int FMT>
+__global__ void pack_kernel(const uint8_t* __restrict__ w, const void* __restrict__ s,
+                            void* __restrict__ wp, void* __restrict__ sp, int slots, int rows_p,
                             int K_p, int rows_s, int K_s, int half_p, int half_s) {
+  using Sc = typename WFmt<FMT>::Scale;
   const int nrb = rows_p / kTileRows, nq = K_p / kTileK, G_s = K_s / kGroup;
+  const size_t row_bytes = FMT == kFmtMxfp4 ? (size_t)K_s / 2 : (size_t)K_s;
   const size_t total = (size_t)slots * nrb * nq * kWave;
   for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < total;
        i += (size_t)gridDim.x * blockDim.x) {
@@ -2593,20 +2671,36 @@ __global__ void pack_kernel(const uint8_t* __restrict__ w, const float* __restri
     } else {
       row = kTileRows * rb + n;
     }
-    const int k0 = kTileK * q + 8 * kq;      // group 0 of the tile; group 1 is 32 further
-    const bool v0 = rvalid && k0 < K_s, v1 = rvalid && k0 + kGroup < K_s;
     const size_t r_s = (size_t)slot * rows_s + (rvalid ? row : 0);
-    const uint8_t* src = w + r_s * K_s;
-    const u32x2 zero2 = {0u, 0u};
-    const u32x2 a = v0 ? *(const u32x2*)(src + k0) : zero2;
-    const u32x2 b = v1 ? *(const u32x2*)(src + k0 + kGroup) : zero2;
-    wp[i] = (u32x4){a.x, a.y, b.x, b.y};
+    const uint8_t* src = w + r_s * row_bytes;
+    uint32_t o[4];
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      const int k = kTileK * q + kGroup * g + 8 * kq;   // this lane's 8 elements of group g
+      const bool v = rvalid && k < K_s;
+      if constexpr (FMT == kFmtMxfp4) {
+        o[g] = v ? *(const uint32_t*)(src + k / 2) : 0u;
+      } else {
+        const u32x2 x = v ? *(const u32x2*)(src + k) : (u32x2){0u, 0u};
+        o[2 * g] = x.x;
+        o[2 * g + 1] = x.y;
+      }
+    }
+    if constexpr (FMT == kFmtMxfp4) ((u32x2*)wp)[i] = (u32x2){o[0], o[1]};
+    else ((u32x4*)wp)[i] = (u32x4){o[0], o[1], o[2], o[3]};
     if (kq == 0) {
       const int g0 = kTileK * q / kGroup;
-      const float* ss = s + r_s * G_s;
-      float* d = sp + (tile * kTileRows + n) * 2;
-      d[0] = rvalid && g0 < G_s ? ss[g0] : 0.f;
-      d[1] = rvalid && g0 + 1 < G_s ? ss[g0 + 1] : 0.f;
+      Sc* d = (Sc*)sp + tile * kTileRows + n;
+      if constexpr (FMT == kFmtFp8) {
+        const float* ss = (const float*)s + r_s * G_s;
+        *d = (f32x2){rvalid && g0 < G_s ? ss[g0] : 0.f, rvalid && g0 + 1 < G_s ? ss[g0 + 1] : 0.f};
+      } else {
+        const uint8_t* ss = (const uint8_t*)s + r_s * G_s;
+        uint32_t v = 0;
+#pragma unroll
+        for (int g = 0; g < 2; ++g) v |= (uint32_t)(rvalid && g0 + g < G_s ? ss[g0 + g] : 0) << (8 * g);
+        *d = (Sc)v;
+      }
     }
   }
 }
@@ -2694,10 +2788,12 @@ struct moe_decode_handle {
   float* router_w = nullptr;
   f32x4* router_wt = nullptr;
   float* router_b = nullptr;
-  u32x4* w13p = nullptr;
-  float* s13p = nullptr;
-  u32x4* w2p = nullptr;
-  float* s2p = nullptr;
+  int fmt = kFmtFp8;              // expert weight format (config flags)
+  void* w13p = nullptr;
+  void* s13p = nullptr;
+  void* w2p = nullptr;
+  void* s2p = nullptr;
+  size_t w13_bytes = 0, s13_bytes = 0, w2_bytes = 0, s2_bytes = 0;
   uint64_t* lgt = nullptr;
   size_t lgt_bytes = 0;   // tile path: [ks][T][E]; small batches: [copy][E][8 or 16]
   int* topk_idx = nullptr;
@@ -2721,9 +2817,12 @@ struct moe_decode_handle {
 
 namespace {
 
+// Expert weight format of a config (its flags' low two bits).
+int weight_format(const moe_decode_config& c) { return (int)(c.flags & 3u); }
+
 moe_status check_config(const moe_decode_config* c) {
   if (!c) return MOE_ERR_INVALID_ARG;
-  if (c->flags != 0 || c->deadline_us < 0) return MOE_ERR_INVALID_ARG;
+  if ((c->flags & ~3u) != 0 || weight_format(*c) == 3 || c->deadline_us < 0) return MOE_ERR_INVALID_ARG;
   if (c->max_tokens < 1 || c->hidden < 1 || c->num_experts < 1 || c->top_k < 1 ||
       c->intermediate < 1 || c->num_shared < 0)
     return MOE_ERR_INVALID_ARG;
@@ -2758,6 +2857,10 @@ Params make_params(const moe_decode_handle* h, int T) {
   p.s13p = h->s13p;
   p.w2p = h->w2p;
   p.s2p = h->s2p;
+  p.w13_bytes = h->w13_bytes;
+  p.s13_bytes = h->s13_bytes;
+  p.w2_bytes = h->w2_bytes;
+  p.s2_bytes = h->s2_bytes;
   p.lgt = h->lgt;
   p.lg_copies = kLgCopies;
   p.lg_tp_log2 = T <= 8 ? 3 : 4;
@@ -2783,7 +2886,7 @@ Params make_params(const moe_decode_handle* h, int T) {
   p.n_q2 = p.I / kTileK;
   p.n_rg = (p.H + kDownRows - 1) / kDownRows;
   p.nch = (T + 63) / 64;
-  p.wide = T > kMBlock && p.n_q13 == kWaves * kWideTiles && p.n_q2 == kWideQ2;
+  p.wide = h->fmt == kFmtFp8 && T > kMBlock && p.n_q13 == kWaves * kWideTiles && p.n_q2 == kWideQ2;
   p.mrange = p.wide ? kWideRows : kMRange;
   p.n_gu_mr = p.wide ? p.n_rb13 / kWideRb : p.n_rb13;
   p.n_dn_mr = p.wide ? p.H / (kWaves * kWideDnBlocks * kTileRows) : p.n_rg;
@@ -2929,6 +3032,7 @@ moe_status moe_decode_create(const moe_decode_config* cfg, const moe_decode_weig
   if (!h) return MOE_ERR_OUT_OF_MEMORY;
   h->cfg = *cfg;
   h->device = device;
+  h->fmt = weight_format(*cfg);
   moe_status rc = MOE_OK;
   do {
     hipDeviceProp_t prop;
@@ -2940,15 +3044,22 @@ moe_status moe_decode_create(const moe_decode_config* cfg, const moe_decode_weig
                  I = padded_intermediate(*cfg), I_s = cfg->intermediate, K = cfg->top_k, Tm = cfg->max_tokens;
     const size_t slots = E + S;
     const size_t scr_rows = Tm * K + Tm * S;
+    // packed weights: FP8 and MXFP8 one byte per element, MXFP4 half a byte;
+    // scales one fp32 (FP8) or one E8M0 byte (MX) per 32 elements
+    const size_t w_num = h->fmt == kFmtMxfp4 ? 1 : 2, s_bytes = h->fmt == kFmtFp8 ? 4 : 1;
+    h->w13_bytes = slots * 2 * I * H * w_num / 2;
+    h->s13_bytes = slots * 2 * I * (H / 32) * s_bytes;
+    h->w2_bytes = slots * H * I * w_num / 2;
+    h->s2_bytes = slots * H * (I / 32) * s_bytes;
     // two counter blocks, the status line, the arrival counters
     const size_t ctr_words = kCtrWords;
     struct A { void** p; size_t bytes; } allocs[] = {
         {(void**)&h->router_w, E * H * 4},
         {(void**)&h->router_b, w->router_bias ? E * 4 : 0},
-        {(void**)&h->w13p, slots * 2 * I * H},
-        {(void**)&h->s13p, slots * 2 * I * (H / 32) * 4},
-        {(void**)&h->w2p, slots * H * I},
-        {(void**)&h->s2p, slots * H * (I / 32) * 4},
+        {(void**)&h->w13p, h->w13_bytes},
+        {(void**)&h->s13p, h->s13_bytes},
+        {(void**)&h->w2p, h->w2_bytes},
+        {(void**)&h->s2p, h->s2_bytes},
         {(void**)&h->lgt, h->lgt_bytes = std::max(Tm * E * kRouterKsMax, (size_t)kLgCopies * E * 16) * 8},
         {(void**)&h->topk_idx, Tm * K * 4},
         {(void**)&h->topk_w, Tm * K * 4},
@@ -2975,10 +3086,12 @@ moe_status moe_decode_create(const moe_decode_config* cfg, const moe_decode_weig
       hipLaunchKernelGGL(pack_router_kernel, dim3(1024), dim3(256), 0, 0, h->router_w, h->router_wt, (int)E, (int)H);
       if (hipGetLastError() != hipSuccess) { rc = MOE_ERR_HIP; break; }
     }
-    hipLaunchKernelGGL(pack_kernel, dim3(4096), dim3(256), 0, 0, w->w13, w->s13, h->w13p, h->s13p,
+    auto pack = h->fmt == kFmtMxfp4 ? pack_kernel<kFmtMxfp4> : h->fmt == kFmtMxfp8 ? pack_kernel<kFmtMxfp8>
+                                                                                  : pack_kernel<kFmtFp8>;
+    hipLaunchKernelGGL(pack, dim3(4096), dim3(256), 0, 0, w->w13, w->s13, h->w13p, h->s13p,
                        (int)slots, (int)(2 * I), (int)H, (int)(2 * I_s), (int)H, (int)I, (int)I_s);
     if (hipGetLastError() != hipSuccess) { rc = MOE_ERR_HIP; break; }
-    hipLaunchKernelGGL(pack_kernel, dim3(4096), dim3(256), 0, 0, w->w2, w->s2, h->w2p, h->s2p,
+    hipLaunchKernelGGL(pack, dim3(4096), dim3(256), 0, 0, w->w2, w->s2, h->w2p, h->s2p,
                        (int)slots, (int)H, (int)I, (int)H, (int)I_s, 0, 0);
     if (hipGetLastError() != hipSuccess) { rc = MOE_ERR_HIP; break; }
     if (hipDeviceSynchronize() != hipSuccess) { rc = MOE_ERR_HIP; break; }
@@ -2995,6 +3108,34 @@ moe_status moe_decode_create(const moe_decode_config* cfg, const moe_decode_weig
 }  // extern "C"
 
 namespace {
+
+// The kernel of a variant (see run_impl) for weight format FMT; nullptr for
+// the wide variant of an MX format (wide items read FP8 tiles).
+template <int FMT>
+const void* kernel_for(int variant, bool norm) {
+  constexpr int q = kFullTiles / 2;   // down tiles per row block at I = 32 kFullTiles
+  if (variant == 4) {
+    if constexpr (FMT != kFmtFp8) return nullptr;
+    else return norm ? (const void*)moe_decode_kernel<2, false, false, true, q, true, FMT>
+                     : (const void*)moe_decode_kernel<2, false, false, true, q, false, FMT>;
+  }
+  if (norm) {
+    switch (variant) {
+      case 3: return (const void*)moe_decode_kernel<1, true, true, false, q, true, FMT>;
+      case 5: return (const void*)moe_decode_kernel<1, true, true, false, q + 1, true, FMT>;
+      case 0: return (const void*)moe_decode_kernel<1, true, false, false, q, true, FMT>;
+      case 1: return (const void*)moe_decode_kernel<1, false, false, false, q, true, FMT>;
+      default: return (const void*)moe_decode_kernel<4, false, false, false, q, true, FMT>;
+    }
+  }
+  switch (variant) {
+    case 3: return (const void*)moe_decode_kernel<1, true, true, false, q, false, FMT>;
+    case 5: return (const void*)moe_decode_kernel<1, true, true, false, q + 1, false, FMT>;
+    case 0: return (const void*)moe_decode_kernel<1, true, false, false, q, false, FMT>;
+    case 1: return (const void*)moe_decode_kernel<1, false, false, false, q, false, FMT>;
+    default: return (const void*)moe_decode_kernel<4, false, false, false, q, false, FMT>;
+  }
+}
 
 // One layer call (norm = false) or pre-norm block call (norm = true).
 moe_status run_impl(moe_decode_handle* h, const void* x, int32_t T, void* y,
@@ -3061,29 +3202,19 @@ moe_status run_impl(moe_decode_handle* h, const void* x, int32_t T, void* y,
   }
   // variants: 0 = x in LDS, 1 = up to 16 rows, 2 = more rows (4 MFMA blocks
   // per item), 3 = x in LDS with full-tile items (H = 64 kFullTiles,
-  // I = 32 kFullTiles, h staged in LDS, local routing), 5 = the same at
-  // I = 576 (9 K tiles per down row block: the pages' per-GPU width without
-  // padding), 4 = more than 16 rows with wide items (H = 64 kWideTiles,
-  // I = 64 kWideQ2)
+  // I = 32 kFullTiles, h staged in LDS, local routing), 5 = the same with one
+  // more down tile per row block (I = 576 at 64-K tiles: the pages' per-GPU
+  // width without padding), 4 = more than 16 rows with wide items (FP8 only,
+  // H = 64 kWideTiles, I = 64 kWideQ2)
   const bool full = p.xs_stride > 0 && p.hs_stride > 0 && p.n_q13 == 4 * kFullTiles &&
                     (p.n_q2 == kFullTiles / 2 || p.n_q2 == kFullTiles / 2 + 1) && p.local_topk && !p.router_tiles;
   const int variant = p.wide ? 4 : full ? (p.n_q2 == kFullTiles / 2 ? 3 : 5) : p.xs_stride > 0 ? 0 : (T > kMBlock ? 2 : 1);
-  const void* fn;
-  if (!norm) {
-    fn = variant == 4   ? (const void*)moe_decode_kernel<2, false, false, true>
-         : variant == 3 ? (const void*)moe_decode_kernel<1, true, true, false>
-         : variant == 5 ? (const void*)moe_decode_kernel<1, true, true, false, kFullTiles / 2 + 1>
-         : variant == 0 ? (const void*)moe_decode_kernel<1, true, false, false>
-         : variant == 1 ? (const void*)moe_decode_kernel<1, false, false, false>
-                        : (const void*)moe_decode_kernel<4, false, false, false>;
-  } else {
-    constexpr int q = kFullTiles / 2;
-    fn = variant == 4   ? (const void*)moe_decode_kernel<2, false, false, true, q, true>
-         : variant == 3 ? (const void*)moe_decode_kernel<1, true, true, false, q, true>
-         : variant == 5 ? (const void*)moe_decode_kernel<1, true, true, false, q + 1, true>
-         : variant == 0 ? (const void*)moe_decode_kernel<1, true, false, false, q, true>
-         : variant == 1 ? (const void*)moe_decode_kernel<1, false, false, false, q, true>
-                        : (const void*)moe_decode_kernel<4, false, false, false, q, true>;
+  const void* fn = h->fmt == kFmtMxfp4   ? kernel_for<kFmtMxfp4>(variant, norm)
+                   : h->fmt == kFmtMxfp8 ? kernel_for<kFmtMxfp8>(variant, norm)
+                                         : kernel_for<kFmtFp8>(variant, norm);
+  if (!fn) {
+    if (prev != h->device) (void)hipSetDevice(prev);
+    return MOE_ERR_UNSUPPORTED;
   }
   const int slot = variant + (norm ? 6 : 0);
   if (h->occ_lds[slot] != p.lds_bytes) {

@@ -38,7 +38,8 @@ def make_layer(inp: Inputs, max_tokens: int | None = None, device: int = 0,
     wl = inp.workload
     dev = torch.device("cuda", device)
     w = upload_weights(inp, dev)
-    cfg = binding.make_config(max_tokens or wl.T, wl.H, wl.E, wl.K, wl.I, wl.S, deadline_us)
+    cfg = binding.make_config(max_tokens or wl.T, wl.H, wl.E, wl.K, wl.I, wl.S, deadline_us,
+                              wl.weight_format)
     layer = binding.MoeDecode(cfg, w, device)
     if wl.prenorm:
         layer.set_input_norm(to_device(inp.norm_w, dev), wl.norm_eps)

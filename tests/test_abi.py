@@ -36,16 +36,23 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert binding.moe_decode_abi_version() == 3
+    assert binding.moe_decode_abi_version() == 4
     for st in range(6):
         assert binding.moe_decode_status_string(st) != "unknown status"
     assert binding.moe_decode_status_string(99) == "unknown status"
 
 
 def cfg(**kw):
-    base = dict(T_max=384, H=4096, E=256, K=8, I=512, S=1)
+    base = dict(T_max=384, H=4096, E=256, K=8, I=512, S=1, fmt="fp8")
     base.update(kw)
-    return binding.make_config(base["T_max"], base["H"], base["E"], base["K"], base["I"], base["S"])
+    return binding.make_config(base["T_max"], base["H"], base["E"], base["K"], base["I"], base["S"],
+                               weight_format=base["fmt"])
+
+
+def raw_flags(flags, **kw):
+    c = cfg(**kw)
+    c.flags = flags
+    return c
 
 
 @pytest.mark.parametrize("kw,T,want", [
@@ -67,9 +74,41 @@ def cfg(**kw):
     ({"T_max": 513}, 6, binding.MOE_ERR_UNSUPPORTED),
     ({"T_max": 0}, 0, binding.MOE_ERR_INVALID_ARG),
     ({"E": 0}, 1, binding.MOE_ERR_INVALID_ARG),
+    # the MX formats take the same shapes (64-K tiles, I padded to 64)
+    ({"fmt": "mxfp4"}, 6, binding.MOE_OK),
+    ({"fmt": "mxfp4"}, 384, binding.MOE_OK),
+    ({"fmt": "mxfp4", "I": 288}, 6, binding.MOE_OK),
+    ({"fmt": "mxfp8", "I": 576}, 6, binding.MOE_OK),
+    ({"fmt": "mxfp4", "H": 4064}, 6, binding.MOE_ERR_UNSUPPORTED),
+    ({"fmt": "mxfp8", "I": 80}, 6, binding.MOE_ERR_UNSUPPORTED),
 ])
 def test_guard(kw, T, want):
     assert binding.moe_decode_supported(cfg(**kw), T) == want
+
+
+@pytest.mark.parametrize("flags,want", [
+    (0, binding.MOE_OK), (1, binding.MOE_OK), (2, binding.MOE_OK),
+    (3, binding.MOE_ERR_INVALID_ARG),            # no fourth format
+    (4, binding.MOE_ERR_INVALID_ARG),            # reserved bits
+    (0x80000001, binding.MOE_ERR_INVALID_ARG),
+])
+def test_guard_flags(flags, want):
+    assert binding.moe_decode_supported(raw_flags(flags), 6) == want
+
+
+@pytest.mark.parametrize("name", ["tiny_t4_h256_e16_k2", "tiny_t4_h256_e16_k2_mxfp4",
+                                  "tiny_t4_h256_e16_k2_mxfp8"])
+def test_weight_layout_matches_the_generator(name):
+    """The arrays the binding hands to create (checked against weight_layout)
+    are exactly what the input generator writes for each weight format."""
+    from moe_decode_layer_amd import synth
+    wl = synth.BY_NAME[name]
+    c = binding.make_config(wl.T, wl.H, wl.E, wl.K, wl.I, wl.S, weight_format=wl.weight_format)
+    want = binding.weight_layout(c)
+    got = dict(zip(("w13", "s13", "w2", "s2"), synth.expert_weights(wl)))
+    got["router_w"] = synth.router_weights(wl)
+    for key, a in got.items():
+        assert (str(a.dtype), a.size) == want[key], key
 
 
 def test_null_arguments_are_rejected_before_any_device_call():
