@@ -14,8 +14,9 @@ Each step is bracketed by HIP events on the stream the kernel is launched on.
 The other workloads time the same way; a ``*_prenorm`` workload times the
 pre-norm block form (input RMSNorm + layer + residual, still one launch).
 
-Prints one JSON line: value = expert-weight bytes (FP8 + fp32 group scales of
-every touched expert, each read once) / mean latency, as GB/s; the roofline
+Prints one JSON line: value = expert-weight bytes (codes + group scales of
+every touched expert, each read once: FP8 1 byte + 4/32 per weight, MXFP8
+1 + 1/32, MXFP4 1/2 + 1/32) / mean latency, as GB/s; the roofline
 object compares the same figure with the 8 TB/s HBM peak; cpu_baseline times
 the CPU oracle on the host cores.
 """
@@ -35,6 +36,8 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 DEFAULT_WORKLOAD = "verify_t6_h4096_e256_k8_s1"
+WEIGHT_NAMES = {"fp8": "fp8_e4m3fn_group32_fp32_scales", "mxfp8": "mxfp8_e4m3fn_group32_e8m0_scales",
+                "mxfp4": "mxfp4_e2m1_group32_e8m0_scales"}
 KERNEL_SRC = os.path.join(ROOT, "moe_decode_layer_amd", "csrc", "moe_decode.hip")
 
 
@@ -62,27 +65,49 @@ def traffic_for(workload: str):
     return rec.get("hbm_bytes_per_launch")
 
 
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(inp, expert_bytes: int, budget_s: float = 15.0):
-    """The CPU oracle as it stands, timed on the host cores (a reported baseline)."""
-    from threadpoolctl import threadpool_info
+    """The CPU oracle as it stands, timed on the host cores (a reported
+    baseline): full layer calls with the BLAS thread pool as configured, then
+    two with one thread (most of the oracle's time is single-threaded numpy,
+    so both figures are given)."""
+    from threadpoolctl import threadpool_info, threadpool_limits
 
     from oracle import moe_oracle as O
-    times = []
-    t_start = time.perf_counter()
-    while len(times) < 3 or (len(times) < 10 and time.perf_counter() - t_start < budget_s):
-        t0 = time.perf_counter()
-        (O.forward_block if inp.workload.prenorm else O.forward)(inp)
-        times.append(time.perf_counter() - t0)
-    med = float(np.median(times))
+    fwd = O.forward_block if inp.workload.prenorm else O.forward
+
+    def timed(n_min, n_max, budget):
+        out, t_start = [], time.perf_counter()
+        while len(out) < n_min or (len(out) < n_max and time.perf_counter() - t_start < budget):
+            t0 = time.perf_counter()
+            fwd(inp)
+            out.append(time.perf_counter() - t0)
+        return float(np.median(out)), len(out)
+
+    med, n = timed(3, 10, budget_s)
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    with threadpool_limits(1):
+        med1, n1 = timed(2, 2, 0.0)
     return {
         "value": expert_bytes / med / 1e9,
         "unit": "GB/s",
         "cores": int(threads),
         "kind": "oracle",
-        "sample": f"{len(times)} full layer calls of the same workload, median {med * 1e3:.1f} ms "
-                  f"per call (fp64 numpy, BLAS threads {threads}, nproc {os.cpu_count()})",
+        "sample": f"{n} full layer calls of the same workload, median {med * 1e3:.1f} ms per call "
+                  f"(fp64 numpy, BLAS threads {threads}, nproc {os.cpu_count()}, {cpu_model()}); "
+                  f"with one thread: {n1} calls, median {med1 * 1e3:.1f} ms",
         "latency_us": med * 1e6,
+        "latency_us_one_thread": med1 * 1e6,
+        "cpu_model": cpu_model(),
     }
 
 
@@ -171,7 +196,7 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": wl.name, "T": wl.T, "H": wl.H, "E": wl.E, "K": wl.K, "S": wl.S, "I": wl.I,
-            "weights": "fp8_e4m3fn_group32", "experts_streamed": touched,
+            "weights": WEIGHT_NAMES[wl.weight_format], "experts_streamed": touched,
             "expert_bytes": expert_bytes, "router_bytes": router_bytes, "activation_bytes": act_bytes,
             "cache_scrub_between_steps": not args.no_scrub,
             "wall_s_timed_region": wall,

@@ -263,13 +263,9 @@ __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
-// fp32 -> bf16, round to nearest even (overflow to inf, NaN kept NaN).
-__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
-}
+// fp32 -> bf16, round to nearest even (overflow to inf, NaN kept NaN): one
+// v_cvt_pk_bf16_f32 on gfx950.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
 
 // 8 FP8 e4m3fn bytes (two dwords, little-endian) -> 8 bf16, exact.
 __device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint32_t lo, uint32_t hi) {
@@ -1250,8 +1246,11 @@ __device__ __forceinline__ void topk_pair(KParams& p, const SHARED float* lg, in
   for (int k = 0; k < K; ++k) {
     const uint32_t M = half_max_v(uk[0]);
     const unsigned long long bal = __ballot(uk[0] == M);
+    // each half holds its own maximum, so both halves of the ballot are
+    // nonzero; both picks are read and selected per lane (no branch)
     const int wlo = __builtin_ctz((uint32_t)bal), whi = 32 + __builtin_ctz((uint32_t)(bal >> 32));
-    const uint32_t W = lo ? __builtin_amdgcn_readlane(ui[0], wlo) : __builtin_amdgcn_readlane(ui[0], whi);
+    const uint32_t Wlo = __builtin_amdgcn_readlane(ui[0], wlo), Whi = __builtin_amdgcn_readlane(ui[0], whi);
+    const uint32_t W = lo ? Wlo : Whi;
     sel_k = hl == (uint32_t)k ? M : sel_k;
     sel_e = hl == (uint32_t)k ? W : sel_e;
     const bool win = (int)lane_id() == (lo ? wlo : whi);
@@ -1458,6 +1457,25 @@ __device__ __forceinline__ bool combine_item(KParams& p, const Lds& L, int rc, i
 }
 
 // ----------------------------------------------------------------------------
+// Gate/up epilogue of element i of every lane's four values of a 16x16
+// gate/up result: column n < 8 is gate row 8 rb + n, column n + 8 the
+// matching up row, result row 4 kq + i (block-relative; rows from nrows on
+// are not stored).  h = bf16(silu(min(g, L)) * clamp(u, -L, L)) goes out as
+// tagged pairs of adjacent columns (lanes with even n < 8).  All lanes of
+// the wave take part (the DPP reads cross lanes).
+__device__ __forceinline__ void swiglu_out(KParams& p, const Lds& L, float s, int i, int sbase, int r0, int nrows,
+                                           int rb) {
+  const int lane = lane_id(), n = lane & 15, kq = lane >> 4;
+  const float g = s;
+  const float u = dpp<kDppRowRor8>(s);
+  const float gc = fminf(g, p.swiglu_limit), uc = fminf(fmaxf(u, -p.swiglu_limit), p.swiglu_limit);
+  const uint32_t hb = f32_to_bf16(gc * __builtin_amdgcn_rcpf(1.0f + __expf(-gc)) * uc);
+  const uint32_t hb_next = dpp<kDppRowShl1>(hb);             // column n + 1
+  const int r = 4 * kq + i;
+  if (n < 8 && (n & 1) == 0 && r < nrows)
+    st_tag(p.h_scr + (size_t)(sbase + r0 + r) * (p.I / 2) + (8 * rb + n) / 2, hb | (hb_next << 16), L.epoch);
+}
+
 // Expert gate/up: one 16-row block (8 gate rows + 8 up rows) of one expert for
 // up to 64 of its rows.  The 4 waves split the H/64 tiles (wave w takes tiles
 // w, w+4, ...); weight loads run up to two stages ahead of the MFMAs; partial
@@ -1565,23 +1583,16 @@ __device__ __forceinline__ void gu_item(KParams& p, const Lds& L, int slot, int 
 #pragma unroll
   for (int mb = 0; mb < NMB; ++mb) red[(w * NMB + mb) * kWave + lane] = acc[mb];
   __syncthreads();
+  // wave w finishes block w.  (Only the finishing waves store and count:
+  // loads retire in order, so a wave that also stored here would wait for
+  // those stores' acknowledgement before its next item's first MFMA.)
   if (w < NMB && w * kMBlock < nrows) {
     const int mb = w;
     f32x4 s = red[(0 * NMB + mb) * kWave + lane];
 #pragma unroll
     for (int ww = 1; ww < kWaves; ++ww) s += red[(ww * NMB + mb) * kWave + lane];
-    // column n < 8 is gate row 8 rb + n, column n + 8 the matching up row
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float g = s[i];
-      const float u = dpp<kDppRowRor8>(s[i]);
-      const float gc = fminf(g, p.swiglu_limit), uc = fminf(fmaxf(u, -p.swiglu_limit), p.swiglu_limit);
-      const uint32_t hb = f32_to_bf16(gc / (1.0f + __expf(-gc)) * uc);
-      const uint32_t hb_next = dpp<kDppRowShl1>(hb);          // column n + 1
-      const int r = mb * kMBlock + 4 * kq + i;
-      if (n < 8 && (n & 1) == 0 && r < nrows)
-        st_tag(p.h_scr + (size_t)(sbase + r0 + r) * (p.I / 2) + (8 * rb + n) / 2, hb | (hb_next << 16), L.epoch);
-    }
+    for (int i = 0; i < 4; ++i) swiglu_out(p, L, s[i], i, sbase, r0 + mb * kMBlock, nrows - mb * kMBlock, rb);
     // each wave that stored h rows counts them in (one per 16-row block)
     if (lane == 0) count_done(L.ctr + kCtrHReady + slot * kLine);
   }
@@ -1774,21 +1785,13 @@ __device__ __forceinline__ void gu_item_full(KParams& p, const Lds& L, int slot,
   SHARED f32x4* red = (SHARED f32x4*)L.red + (parity & 1) * kWaves * kWave;
   red[w * kWave + lane] = acc;
   __syncthreads();
+  // wave 0 finishes the block (see gu_item on why one wave)
   if (w == 0) {
     f32x4 s = red[lane];
 #pragma unroll
     for (int ww = 1; ww < kWaves; ++ww) s += red[ww * kWave + lane];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float g = s[i];
-      const float u = dpp<kDppRowRor8>(s[i]);
-      const float gc = fminf(g, p.swiglu_limit), uc = fminf(fmaxf(u, -p.swiglu_limit), p.swiglu_limit);
-      const uint32_t hb = f32_to_bf16(gc / (1.0f + __expf(-gc)) * uc);
-      const uint32_t hb_next = dpp<kDppRowShl1>(hb);
-      const int r = 4 * kq + i;
-      if (n < 8 && (n & 1) == 0 && r < nrows)
-        st_tag(p.h_scr + (size_t)(sbase + r0 + r) * (p.I / 2) + (8 * rb + n) / 2, hb | (hb_next << 16), L.epoch);
-    }
+    for (int i = 0; i < 4; ++i) swiglu_out(p, L, s[i], i, sbase, r0, nrows, rb);
     if (lane == 0) count_done(L.ctr + kCtrHReady + slot * kLine);
   }
 }
@@ -2008,18 +2011,8 @@ __device__ __forceinline__ void gu_item_wide(KParams& p, const Lds& L, int slot,
       f32x4 s = red[((0 * kWideRb + w) * NMB + mb) * kWave + lane];
 #pragma unroll
       for (int ww = 1; ww < kWaves; ++ww) s += red[((ww * kWideRb + w) * NMB + mb) * kWave + lane];
-      // column n < 8 is gate row 8 rb + n, column n + 8 the matching up row
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float g = s[i];
-        const float u = dpp<kDppRowRor8>(s[i]);
-        const float gc = fminf(g, p.swiglu_limit), uc = fminf(fmaxf(u, -p.swiglu_limit), p.swiglu_limit);
-        const uint32_t hb = f32_to_bf16(gc / (1.0f + __expf(-gc)) * uc);
-        const uint32_t hb_next = dpp<kDppRowShl1>(hb);          // column n + 1
-        const int r = mb * kMBlock + 4 * kq + i;
-        if (n < 8 && (n & 1) == 0 && r < nrows)
-          st_tag(p.h_scr + (size_t)(sbase + r0 + r) * (p.I / 2) + (8 * rb + n) / 2, hb | (hb_next << 16), L.epoch);
-      }
+      for (int i = 0; i < 4; ++i) swiglu_out(p, L, s[i], i, sbase, r0 + mb * kMBlock, nrows - mb * kMBlock, rb);
     }
   }
   // one publication per wave and item: an M-range counts n_rb13 in all

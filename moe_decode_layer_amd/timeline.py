@@ -105,20 +105,52 @@ def summarise(wl, experts: int, tr: np.ndarray) -> dict:
             "median_wait_us": float(np.median(sel[:, 2] - sel[:, 1])),
             "median_after_ready_us": float(np.median(sel[:, 3] - sel[:, 2])),
         }
-    # routing inside each workgroup (kind 8: start, logits gather begins, top-k begins)
-    r8 = []
+    # routing inside each workgroup: kind 8 = {start, gather begins, top-k
+    # done; placement time}, kind 9 = {logits in LDS, row 0 selected, all
+    # rows selected}
+    # (all workgroups, then split by the kind of the workgroup's first item:
+    # router, shared gate/up, or none before the routing)
+    def routing_of(sel):
+        r8, r9 = [], []
+        for b in sel:
+            n = min(int(tr[b, 0, 2]), tr.shape[1] - 1)
+            for i in range(n):
+                w = tr[b, 1 + i]
+                k = int(w[0] >> 32)
+                if k == 8:
+                    r8.append(((w[1] - t0) * TICK_US, (w[2] - t0) * TICK_US, (w[3] - t0) * TICK_US,
+                               ((w[3] - t0) + (int(w[0]) & 0xffffffff)) * TICK_US))
+                elif k == 9:
+                    # low 16 bits: shader-clock cycles from logits in LDS to all rows selected
+                    r9.append(((w[1] - t0) * TICK_US, (w[2] - t0) * TICK_US, (w[3] - t0) * TICK_US,
+                               int(w[0]) & 0xffff, (w[3] - w[1]) * TICK_US))
+        if not r8:
+            return None
+        r8 = np.array(r8)
+        r = {"workgroups": len(r8), "median_start_us": float(np.median(r8[:, 0])),
+             "median_gather_begins_us": float(np.median(r8[:, 1])),
+             "median_topk_done_us": float(np.median(r8[:, 2])),
+             "median_placement_done_us": float(np.median(r8[:, 3])),
+             "last_placement_done_us": float(r8[:, 3].max())}
+        if r9:
+            r9 = np.array(r9)
+            r.update({"median_logits_in_lds_us": float(np.median(r9[:, 0])),
+                      "median_row0_selected_us": float(np.median(r9[:, 1])),
+                      "median_rows_selected_us": float(np.median(r9[:, 2])),
+                      # top-k span in shader cycles and wall time: their ratio is the clock
+                      "median_topk_cycles": float(np.median(r9[:, 3])),
+                      "median_topk_wall_us": float(np.median(r9[:, 4]))})
+        return r
+
+    first = {}
     for b in range(G):
         n = min(int(tr[b, 0, 2]), tr.shape[1] - 1)
-        for i in range(n):
-            w = tr[b, 1 + i]
-            if int(w[0] >> 32) == 8:
-                r8.append(((w[1] - t0) * TICK_US, (w[3] - t0) * TICK_US,
-                           ((w[3] - t0) + (int(w[0]) & 0xffffffff)) * TICK_US))
-    if r8:
-        r8 = np.array(r8)
-        out["routing"] = {"median_logits_in_lds_us": float(np.median(r8[:, 1])),
-                          "median_placement_done_us": float(np.median(r8[:, 2])),
-                          "last_placement_done_us": float(r8[:, 2].max())}
+        k = int(tr[b, 1, 0] >> 32) if n > 0 else -1
+        first.setdefault({0: "router", 1: "shared gate/up"}.get(k, "none"), []).append(b)
+    r = routing_of(range(G))
+    if r:
+        out["routing"] = r
+        out["routing_by_first_item"] = {k: routing_of(v) for k, v in first.items() if routing_of(v)}
     # expert streaming: from the first routed gate/up start to the last down end
     ks = out["kinds"]
     if "routed gate/up" in ks and "routed down" in ks:
@@ -137,8 +169,12 @@ def main():
     ap.add_argument("--workload", default="verify_t6_h4096_e256_k8_s1")
     ap.add_argument("--calls", type=int, default=7)
     ap.add_argument("--json", default=None, help="also write the summary of the median call here")
+    ap.add_argument("--raw", default=None, help="also save every call's trace array here (.npy)")
     args = ap.parse_args()
     wl, experts, traces = collect(args.workload, args.calls)
+    if args.raw:
+        G = int(traces[0][0, 0, 3])
+        np.save(args.raw, np.stack([t[:G] for t in traces]))
     sums = [summarise(wl, experts, t) for t in traces]
     spans = [s["span_us"] for s in sums]
     med = sums[int(np.argsort(spans)[len(spans) // 2])]
@@ -157,8 +193,17 @@ def main():
           f"median {med['median_gap_between_items_us']:.2f}, mean {med['mean_gap_between_items_us']:.2f} us")
     if "routing" in med:
         r = med["routing"]
-        print(f"  routing: logits in LDS (median) {r['median_logits_in_lds_us']:.1f}, placement done "
-              f"(median) {r['median_placement_done_us']:.1f}, last {r['last_placement_done_us']:.1f} us")
+        print(f"  routing (medians): start {r['median_start_us']:.1f}, gather begins "
+              f"{r['median_gather_begins_us']:.1f}, logits in LDS {r.get('median_logits_in_lds_us', float('nan')):.1f}, "
+              f"row 0 selected {r.get('median_row0_selected_us', float('nan')):.1f}, all rows selected "
+              f"{r.get('median_rows_selected_us', float('nan')):.1f}, top-k done {r['median_topk_done_us']:.1f}, "
+              f"placement done {r['median_placement_done_us']:.1f} (last {r['last_placement_done_us']:.1f}) us")
+        for k, g in med.get("routing_by_first_item", {}).items():
+            print(f"    first item {k:15s} ({g['workgroups']:3d}): start {g['median_start_us']:.1f}, gather "
+                  f"{g['median_gather_begins_us']:.1f}, logits {g.get('median_logits_in_lds_us', float('nan')):.1f}, "
+                  f"row 0 {g.get('median_row0_selected_us', float('nan')):.1f}, top-k {g['median_topk_done_us']:.1f}, "
+                  f"placement {g['median_placement_done_us']:.1f}; top-k {g.get('median_topk_cycles', 0):.0f} cycles "
+                  f"in {g.get('median_topk_wall_us', 0):.2f} us")
     if "expert_window_us" in med:
         a, z = med["expert_window_us"]
         print(f"  experts stream {a:.1f} .. {z:.1f} us: {med['expert_bytes'] / 1e6:.1f} MB at "
