@@ -97,7 +97,7 @@ constexpr int kMaxTopK = 16;
 constexpr size_t kXsMaxBytes = 64 * 1024;   // x kept in LDS up to this size
 constexpr int kHsMaxI = 1024;               // h staged in LDS up to this intermediate width
 constexpr int kFullTiles = 16;              // tiles per wave of the fully unrolled items (H 4096, I 512)
-// Wide items (batches above 16 rows at H = 64 kWideTiles, I = 64 kWideQ2)
+// Wide items (batches above 16 rows at H = 64 kWideTiles, I = 64 kWideQ2 .. 64 kWideQ2 + 128)
 constexpr int kWideTiles = 16;              // K tiles per wave of a wide gate/up item
 constexpr int kWideQ2 = 8;                  // K tiles of a down row block
 constexpr int kWideRb = 4;                  // gate/up row blocks per wide item (one per wave at the end)
@@ -1899,7 +1899,7 @@ __device__ __forceinline__ bool down_item_full(KParams& p, const Lds& L, int slo
 }
 
 // ----------------------------------------------------------------------------
-// Wide items: batches above 16 rows at H = 64 kWideTiles and I = 64 kWideQ2,
+// Wide items: batches above 16 rows at H = 64 kWideTiles and I = 512, 576 or 640,
 // up to kWideRows (two MFMA blocks) rows of one expert per item, two
 // workgroups per compute unit.
 //
@@ -2027,12 +2027,11 @@ __device__ __forceinline__ void gu_item_wide(KParams& p, const Lds& L, int slot,
 // K tile by K tile, each h operand feeding its 8 row blocks, 16 tiles in
 // flight.
 // ----------------------------------------------------------------------------
-template <int NMB>
+template <int NMB, int NQ>
 __device__ __forceinline__ bool dn_item_wide(KParams& p, const Lds& L, int slot, int sbase, int r0, int nrows,
                                              int rg, int h_target, int& pend) {
   constexpr int NB = kWideDnBlocks;
-  constexpr int NQ = kWideQ2;
-  constexpr int NT = NB * NQ;
+  constexpr int NT = NB * NQ;                  // NQ K tiles per row block: I = 64 NQ
   constexpr int P = NMB == 1 ? 16 : 8;         // tiles in flight
   const int w = wave_id(), lane = lane_id();
   const int n = lane & 15, kq = lane >> 4;
@@ -2040,8 +2039,9 @@ __device__ __forceinline__ bool dn_item_wide(KParams& p, const Lds& L, int slot,
   const size_t blk0 = (size_t)slot * p.n_rb2 + (size_t)grp * NB;
   const u32x4* wt = (const u32x4*)p.w2p + blk0 * NQ * kWave + lane;
   const f32x2* sc = (const f32x2*)p.s2p + blk0 * NQ * kTileRows + n;
-  // tile t = NB q + b is K tile q of row block b
-  static_assert(P % NB == 0 && NT % P == 0, "tile ring");
+  // tile t = NB q + b is K tile q of row block b; the ring turns over P / NB
+  // K steps at a time (the last turn may hold fewer when P does not divide NT)
+  static_assert(P % NB == 0 && NT >= P, "tile ring");
   u32x4 wv[P];
   f32x2 sv[P];
   // tile t into ring slot u = t mod P (u passed as a constant)
@@ -2076,6 +2076,7 @@ __device__ __forceinline__ bool dn_item_wide(KParams& p, const Lds& L, int slot,
 #pragma unroll
     for (int qq = 0; qq < P / NB; ++qq) {
       const int q = t0 / NB + qq;
+      if (q >= NQ) continue;                   // resolved at compile time
       bf16x8 a[2][NMB];
 #pragma unroll
       for (int g = 0; g < 2; ++g)
@@ -2439,8 +2440,8 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
   auto run_down = [&](int slot, int sbase, int r0, int nrows, int rg, int ht) __attribute__((always_inline)) -> bool {
     const int nmb = (nrows + kMBlock - 1) / kMBlock;
     if constexpr (WIDE) {
-      if (nmb <= 1) return dn_item_wide<1>(p, L, slot, sbase, r0, nrows, rg, ht, pend_rg);
-      return dn_item_wide<2>(p, L, slot, sbase, r0, nrows, rg, ht, pend_rg);
+      if (nmb <= 1) return dn_item_wide<1, NQ2>(p, L, slot, sbase, r0, nrows, rg, ht, pend_rg);
+      return dn_item_wide<2, NQ2>(p, L, slot, sbase, r0, nrows, rg, ht, pend_rg);
     } else if constexpr (FULL) return down_item_full<NQ2, FMT>(p, L, slot, sbase, r0, nrows, rg, ht, pend_rg);
     else if (XL && p.hs_stride > 0) return down_item<1, XL, FMT>(p, L, slot, sbase, r0, nrows, rg, ht, pend_rg);
     else if (NMBMAX == 1 || nmb <= 1) return down_item<1, false, FMT>(p, L, slot, sbase, r0, nrows, rg, ht, pend_rg);
@@ -2803,9 +2804,9 @@ struct moe_decode_handle {
   hipStream_t last_stream = nullptr;
   int* last_status = nullptr;    // status word of the last run's workspace (handle's or static)
   std::mutex mu;
-  // occupancy cache, by (kernel variant + 6 for block runs, LDS bytes)
-  int occ_lds[12] = {-1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1};
-  int occ_blocks[12] = {};
+  // occupancy cache, by (kernel variant + 8 for block runs, LDS bytes)
+  int occ_lds[16] = {-1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1};
+  int occ_blocks[16] = {};
 };
 
 namespace {
@@ -2879,7 +2880,8 @@ Params make_params(const moe_decode_handle* h, int T) {
   p.n_q2 = p.I / kTileK;
   p.n_rg = (p.H + kDownRows - 1) / kDownRows;
   p.nch = (T + 63) / 64;
-  p.wide = h->fmt == kFmtFp8 && T > kMBlock && p.n_q13 == kWaves * kWideTiles && p.n_q2 == kWideQ2;
+  p.wide = h->fmt == kFmtFp8 && T > kMBlock && p.n_q13 == kWaves * kWideTiles &&
+           p.n_q2 >= kWideQ2 && p.n_q2 <= kWideQ2 + 2;
   p.mrange = p.wide ? kWideRows : kMRange;
   p.n_gu_mr = p.wide ? p.n_rb13 / kWideRb : p.n_rb13;
   p.n_dn_mr = p.wide ? p.H / (kWaves * kWideDnBlocks * kTileRows) : p.n_rg;
@@ -3107,10 +3109,16 @@ namespace {
 template <int FMT>
 const void* kernel_for(int variant, bool norm) {
   constexpr int q = kFullTiles / 2;   // down tiles per row block at I = 32 kFullTiles
-  if (variant == 4) {
+  if (variant == 4 || variant == 6 || variant == 7) {
     if constexpr (FMT != kFmtFp8) return nullptr;
-    else return norm ? (const void*)moe_decode_kernel<2, false, false, true, q, true, FMT>
-                     : (const void*)moe_decode_kernel<2, false, false, true, q, false, FMT>;
+    else if (variant == 6)
+      return norm ? (const void*)moe_decode_kernel<2, false, false, true, kWideQ2 + 1, true, FMT>
+                  : (const void*)moe_decode_kernel<2, false, false, true, kWideQ2 + 1, false, FMT>;
+    else if (variant == 7)
+      return norm ? (const void*)moe_decode_kernel<2, false, false, true, kWideQ2 + 2, true, FMT>
+                  : (const void*)moe_decode_kernel<2, false, false, true, kWideQ2 + 2, false, FMT>;
+    else return norm ? (const void*)moe_decode_kernel<2, false, false, true, kWideQ2, true, FMT>
+                     : (const void*)moe_decode_kernel<2, false, false, true, kWideQ2, false, FMT>;
   }
   if (norm) {
     switch (variant) {
@@ -3198,10 +3206,12 @@ moe_status run_impl(moe_decode_handle* h, const void* x, int32_t T, void* y,
   // I = 32 kFullTiles, h staged in LDS, local routing), 5 = the same with one
   // more down tile per row block (I = 576 at 64-K tiles: the pages' per-GPU
   // width without padding), 4 = more than 16 rows with wide items (FP8 only,
-  // H = 64 kWideTiles, I = 64 kWideQ2)
+  // H = 64 kWideTiles, I = 64 kWideQ2), 6 and 7 = the same at I = 576 and 640
+  // (one and two more down K tiles per row block)
   const bool full = p.xs_stride > 0 && p.hs_stride > 0 && p.n_q13 == 4 * kFullTiles &&
                     (p.n_q2 == kFullTiles / 2 || p.n_q2 == kFullTiles / 2 + 1) && p.local_topk && !p.router_tiles;
-  const int variant = p.wide ? 4 : full ? (p.n_q2 == kFullTiles / 2 ? 3 : 5) : p.xs_stride > 0 ? 0 : (T > kMBlock ? 2 : 1);
+  const int variant = p.wide ? (p.n_q2 == kWideQ2 ? 4 : p.n_q2 == kWideQ2 + 1 ? 6 : 7)
+                      : full ? (p.n_q2 == kFullTiles / 2 ? 3 : 5) : p.xs_stride > 0 ? 0 : (T > kMBlock ? 2 : 1);
   const void* fn = h->fmt == kFmtMxfp4   ? kernel_for<kFmtMxfp4>(variant, norm)
                    : h->fmt == kFmtMxfp8 ? kernel_for<kFmtMxfp8>(variant, norm)
                                          : kernel_for<kFmtFp8>(variant, norm);
@@ -3209,7 +3219,7 @@ moe_status run_impl(moe_decode_handle* h, const void* x, int32_t T, void* y,
     if (prev != h->device) (void)hipSetDevice(prev);
     return MOE_ERR_UNSUPPORTED;
   }
-  const int slot = variant + (norm ? 6 : 0);
+  const int slot = variant + (norm ? 8 : 0);
   if (h->occ_lds[slot] != p.lds_bytes) {
     int nb = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fn, kThreads, p.lds_bytes) != hipSuccess ||

@@ -103,7 +103,13 @@ PRENORM = [dataclasses.replace(w, name=w.name + "_prenorm", prenorm=True) for w 
 MX = [dataclasses.replace(w, name=f"{w.name}_{fmt}", weight_format=fmt)
       for fmt in ("mxfp4", "mxfp8") for w in (WORKLOADS[1], WORKLOADS[2], WORKLOADS[0])]
 
-BY_NAME = {w.name: w for w in WORKLOADS + PRENORM + MX}
+# The pages' per-GPU intermediate width 576 (run natively) at 6, 64 and 384
+# rows, and 384 rows at 640 (576 padded to whole 128-K tiles, as the pages'
+# own kernels run it), for timing the two against each other.
+WIDTHS = [dataclasses.replace(w, name=f"{w.name}_i{I}", I=I) for w, I in
+          ((WORKLOADS[1], 576), (WORKLOADS[3], 576), (WORKLOADS[4], 576), (WORKLOADS[4], 640))]
+
+BY_NAME = {w.name: w for w in WORKLOADS + PRENORM + MX + WIDTHS}
 
 _lib = None
 

@@ -30,7 +30,7 @@ def attempts_for(wl):
 
 def main():
     out = {}
-    for wl in synth.WORKLOADS + synth.PRENORM + synth.MX:
+    for wl in synth.WORKLOADS + synth.PRENORM + synth.MX + synth.WIDTHS:
         out[wl.name] = [int(a) for a in attempts_for(wl)]
     path = os.path.join(HERE, "attempts.json")
     lines = [f'  "{k}": {json.dumps(v)}' for k, v in out.items()]

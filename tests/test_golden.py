@@ -11,7 +11,7 @@ from oracle import moe_oracle as O
 PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "attempts.json")
 
 
-ALL = synth.WORKLOADS + synth.PRENORM + synth.MX
+ALL = synth.WORKLOADS + synth.PRENORM + synth.MX + synth.WIDTHS
 
 
 @pytest.mark.parametrize("i", range(len(ALL)))

@@ -47,6 +47,8 @@ CASES = synth.PRENORM + [block_of(w) for w in (
     synth.Workload("t33_h320_e64_k6_s1", T=33, H=320, E=64, K=6, S=1, I=128, zipf_s=1.2),
     synth.Workload("t6_h4096_e256_k8_s1_i576", T=6, H=4096, E=256, K=8, S=1, I=576),
     synth.Workload("t6_h4096_e256_k8_s1_i288", T=6, H=4096, E=256, K=8, S=1, I=288),
+    # wide items at the pages' per-GPU width 576
+    synth.Workload("t40_h4096_e256_k8_s1_i576", T=40, H=4096, E=256, K=8, S=1, I=576, zipf_s=1.2),
 )]
 
 

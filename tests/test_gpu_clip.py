@@ -34,6 +34,7 @@ BASES = [
     synth.Workload("t9_h4096_e256_k8_s1", T=9, H=4096, E=256, K=8, S=1, I=512),
     synth.Workload("t20_h128_e8_k8_s1", T=20, H=128, E=8, K=8, S=1, I=64),
     synth.Workload("t6_h4096_e256_k8_s1_i576", T=6, H=4096, E=256, K=8, S=1, I=576),
+    synth.BY_NAME["zipf_t64_h4096_e256_k8_s1_i576"],      # wide items at I = 576
 ]
 
 

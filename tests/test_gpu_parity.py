@@ -86,6 +86,8 @@ SMALL = [
     synth.Workload("t6_h4096_e256_k8_s1_i288", T=6, H=4096, E=256, K=8, S=1, I=288),
     synth.Workload("t40_h4096_e256_k8_s1_i288", T=40, H=4096, E=256, K=8, S=1, I=288, zipf_s=1.2),
     synth.Workload("t20_h128_e8_k8_s1_i96", T=20, H=128, E=8, K=8, S=1, I=96),
+    # 576 padded to 640 (the pages' padded width): wide items with 10 down K tiles
+    synth.Workload("t40_h4096_e256_k8_s1_i640", T=40, H=4096, E=256, K=8, S=1, I=640, zipf_s=1.2),
 ]
 
 
@@ -112,11 +114,12 @@ def test_ragged_T_on_one_handle():
     layer.close()
 
 
-def test_ragged_T_on_one_wide_handle():
+@pytest.mark.parametrize("name", ["verify_t384_h4096_e256_k8_s1", "verify_t384_h4096_e256_k8_s1_i576"])
+def test_ragged_T_on_one_wide_handle(name):
     """Batches above 16 rows take the wide items (32-row expert ranges, 4-block
-    gate/up and 512-row down items): the smallest such batch, ragged expert
-    ranges and the full 384 rows, on one handle."""
-    wl = synth.WORKLOADS[4]
+    gate/up and 512-row down items, at I = 512 or 576): the smallest such
+    batch, ragged expert ranges and the full 384 rows, on one handle."""
+    wl = synth.BY_NAME[name]
     inp = inputs_for(wl)
     layer = device.make_layer(inp, max_tokens=wl.T)
     for T in (17, 45, 200, wl.T):
