@@ -118,9 +118,11 @@ def summarise(wl, experts: int, tr: np.ndarray) -> dict:
                 w = tr[b, 1 + i]
                 k = int(w[0] >> 32)
                 if k == 8:
-                    r8.append(((w[1] - t0) * TICK_US, (w[2] - t0) * TICK_US, (w[3] - t0) * TICK_US,
+                    # a stamp of 0: that phase does not exist on this path
+                    go = (w[2] - t0) * TICK_US if w[2] else np.nan
+                    r8.append(((w[1] - t0) * TICK_US, go, (w[3] - t0) * TICK_US,
                                ((w[3] - t0) + (int(w[0]) & 0xffffffff)) * TICK_US))
-                elif k == 9:
+                elif k == 9 and w[1]:
                     # low 16 bits: shader-clock cycles from logits in LDS to all rows selected
                     r9.append(((w[1] - t0) * TICK_US, (w[2] - t0) * TICK_US, (w[3] - t0) * TICK_US,
                                int(w[0]) & 0xffff, (w[3] - w[1]) * TICK_US))
@@ -128,7 +130,7 @@ def summarise(wl, experts: int, tr: np.ndarray) -> dict:
             return None
         r8 = np.array(r8)
         r = {"workgroups": len(r8), "median_start_us": float(np.median(r8[:, 0])),
-             "median_gather_begins_us": float(np.median(r8[:, 1])),
+             "median_gather_begins_us": float(np.nanmedian(r8[:, 1])) if np.isfinite(r8[:, 1]).any() else float("nan"),
              "median_topk_done_us": float(np.median(r8[:, 2])),
              "median_placement_done_us": float(np.median(r8[:, 3])),
              "last_placement_done_us": float(r8[:, 3].max())}
