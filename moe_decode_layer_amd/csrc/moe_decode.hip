@@ -249,6 +249,8 @@ struct Params {
   uint16_t* dbg_norm;      // [T][H] copy of xn (nullable)
   float norm_eps;
   float swiglu_limit;      // clipped SwiGLU: g -> min(g, L), u -> clamp(u, -L, L); +inf: no clip
+  int full;                // 1: the full-tile variant runs this call (host-side choice, see make_params)
+  int gu_pair;             // 1: full-tile MXFP4 gate/up items cover two row blocks (n_gu_mr = n_rb13 / 2)
 };
 // The kernel reads its parameters in place, from the constant kernel-argument
 // segment, so the compiler can reload a field with a scalar load instead of
@@ -1796,6 +1798,66 @@ __device__ __forceinline__ void gu_item_full(KParams& p, const Lds& L, int slot,
   }
 }
 
+// The same for MXFP4 weights, two row blocks (2 rp, 2 rp + 1) per item: each
+// wave has 2 NJ half-size tiles (16 KiB) in flight, as an FP8 item has, and
+// every x operand read from LDS feeds both blocks' MFMAs.  Waves 0 and 1
+// finish one block each.
+template <int NJ>
+__device__ __forceinline__ void gu_item_full_pair(KParams& p, const Lds& L, int slot, int sbase, int r0, int nrows,
+                                                  int rp, bool shared, int parity, int& pend) {
+  using Wt = typename WFmt<kFmtMxfp4>::W;
+  using Sc = typename WFmt<kFmtMxfp4>::Scale;
+  const int w = wave_id(), lane = lane_id();
+  const int n = lane & 15, kq = lane >> 4;
+  const int nq = p.n_q13;                            // == 4 * NJ
+  Wt wv[2][NJ];
+  Sc sv[2][NJ];
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    const size_t blk = (size_t)slot * p.n_rb13 + 2 * rp + b;
+    const Wt* wt = (const Wt*)p.w13p + (blk * nq + w) * kWave + lane;
+    const Sc* sc = (const Sc*)p.s13p + (blk * nq + w) * kTileRows + n;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      wv[b][j] = ld_stream(wt + (size_t)j * kWaves * kWave);
+      sv[b][j] = ld_stream(sc + (size_t)j * kWaves * kTileRows);
+    }
+  }
+  // 4 NJ = 64 loads are in flight; vmcnt holds at most 63, so the deferred
+  // count also waits for the first of them (gate/up items rarely follow a
+  // down item in this variant's list)
+  flush_pending<(4 * NJ < 63 ? 4 * NJ : 63)>(L.ctr, pend);
+  const bool aval = n < nrows;
+  const int tok = shared ? (r0 + (aval ? n : 0)) : (int)L.rows[sbase + r0 + (aval ? n : 0)];
+  const SHARED uint16_t* arow = L.xs + (size_t)tok * p.xs_stride + 8 * kq + kTileK * w;
+  const u32x4 zero4 = {0u, 0u, 0u, 0u};
+  f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      u32x4 a = *(const SHARED u32x4*)(arow + kTileK * kWaves * j + kGroup * g);
+      a = aval ? a : zero4;
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+        acc[b] += mx_scale(sv[b][j], g) * mfma16(as_bf16x8(a), fp4x8_to_bf16(wv[b][j][g]));
+    }
+  }
+  SHARED f32x4* red = (SHARED f32x4*)L.red + (parity & 1) * kWaves * 2 * kWave;
+#pragma unroll
+  for (int b = 0; b < 2; ++b) red[(b * kWaves + w) * kWave + lane] = acc[b];
+  __syncthreads();
+  if (w < 2) {
+    const int b = w;
+    f32x4 s = red[(b * kWaves + 0) * kWave + lane];
+#pragma unroll
+    for (int ww = 1; ww < kWaves; ++ww) s += red[(b * kWaves + ww) * kWave + lane];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) swiglu_out(p, L, s[i], i, sbase, r0, nrows, 2 * rp + b);
+    if (lane == 0) count_done(L.ctr + kCtrHReady + slot * kLine);
+  }
+}
+
 template <int NQ, int FMT>
 __device__ __forceinline__ bool down_item_full(KParams& p, const Lds& L, int slot, int sbase, int r0, int nrows,
                                int rg, int h_target, int& pend) {
@@ -2248,9 +2310,11 @@ __device__ bool wait_rows(KParams& p, const Lds& L, int t0, int n) {
 // carries only the code its batches reach, which keeps register pressure
 // (and spills) down.  FMT: the expert weight format (WFmt); the wide items
 // exist for FP8 only.
-template <int NMBMAX, bool XL, bool FULL, bool WIDE, int NQ2 = kFullTiles / 2, bool NORM = false, int FMT = kFmtFp8>
+template <int NMBMAX, bool XL, bool FULL, bool WIDE, int NQ2 = kFullTiles / 2, bool NORM = false, int FMT = kFmtFp8,
+          bool PAIR = false>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(NMBMAX == 1 || WIDE ? 2 : 1))) moe_decode_kernel(Params arg) {
   static_assert(!WIDE || FMT == kFmtFp8, "wide items read FP8 tiles");
+  static_assert(!PAIR || (FULL && FMT == kFmtMxfp4), "paired gate/up items: full-tile MXFP4 only");
   KParams& p = *(const CONSTANT Params*)__builtin_amdgcn_kernarg_segment_ptr();
   (void)arg;
   extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -2429,6 +2493,10 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
     if constexpr (WIDE) {
       if (nmb <= 1) gu_item_wide<1>(p, L, slot, sbase, r0, nrows, rb, shared, pend_rg);
       else gu_item_wide<2>(p, L, slot, sbase, r0, nrows, rb, shared, pend_rg);
+    } else if constexpr (PAIR) {
+      // launched only for lists built for pairs (gu_pair: n_gu_mr = n_rb13 / 2,
+      // rb the pair index; checked on the host)
+      gu_item_full_pair<kFullTiles>(p, L, slot, sbase, r0, nrows, rb, shared, par, pend_rg);
     } else if constexpr (FULL) gu_item_full<kFullTiles, FMT>(p, L, slot, sbase, r0, nrows, rb, shared, par, pend_rg);
     else if (NMBMAX == 1 || nmb <= 1) gu_item<1, XL, NMBMAX, FMT>(p, L, slot, sbase, r0, nrows, rb, shared, par, pend_rg);
     else if (nmb == 2) gu_item<NMBMAX >= 2 ? 2 : 1, XL, NMBMAX, FMT>(p, L, slot, sbase, r0, nrows, rb, shared, par, pend_rg);
@@ -2804,9 +2872,10 @@ struct moe_decode_handle {
   hipStream_t last_stream = nullptr;
   int* last_status = nullptr;    // status word of the last run's workspace (handle's or static)
   std::mutex mu;
-  // occupancy cache, by (kernel variant + 8 for block runs, LDS bytes)
-  int occ_lds[16] = {-1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1};
-  int occ_blocks[16] = {};
+  // occupancy cache, by (kernel variant + 8 for paired gate/up items + 16 for
+  // block runs, LDS bytes); occ_lds starts at -1 (set in create)
+  int occ_lds[32];
+  int occ_blocks[32] = {};
 };
 
 namespace {
@@ -2883,7 +2952,18 @@ Params make_params(const moe_decode_handle* h, int T) {
   p.wide = h->fmt == kFmtFp8 && T > kMBlock && p.n_q13 == kWaves * kWideTiles &&
            p.n_q2 >= kWideQ2 && p.n_q2 <= kWideQ2 + 2;
   p.mrange = p.wide ? kWideRows : kMRange;
-  p.n_gu_mr = p.wide ? p.n_rb13 / kWideRb : p.n_rb13;
+  // The full-tile variant: x and h in LDS (at most 16 rows), H = 64 kFullTiles,
+  // I = 32 kFullTiles or 576, local routing.  With MXFP4 weights its gate/up
+  // items cover two row blocks, so a wave has as many bytes in flight as with
+  // FP8 tiles (the items are bound by latency, not by bytes), when that still
+  // leaves at least two items per workgroup (the grid holds two per compute
+  // unit) for as many experts as the call can touch: at 1 row the 288 paired
+  // items would leave half the grid idle (measured slower, 34.4 -> 38.1 us).
+  p.full = !p.wide && T <= kMBlock && (size_t)T * (p.H + 8) * 2 <= kXsMaxBytes && p.I <= kHsMaxI &&
+           p.n_q13 == 4 * kFullTiles && (p.n_q2 == kFullTiles / 2 || p.n_q2 == kFullTiles / 2 + 1);
+  const long long max_experts = std::min((long long)T * p.K, (long long)p.E) + p.S;
+  p.gu_pair = p.full && h->fmt == kFmtMxfp4 && max_experts * (p.n_rb13 / 2) >= 2LL * 2 * h->n_cu;
+  p.n_gu_mr = p.wide ? p.n_rb13 / kWideRb : p.gu_pair ? p.n_rb13 / 2 : p.n_rb13;
   p.n_dn_mr = p.wide ? p.H / (kWaves * kWideDnBlocks * kTileRows) : p.n_rg;
   p.h_rows_per_count = p.wide ? kWideRows : kMBlock;
   p.n_mr_sh = p.S ? (T + p.mrange - 1) / p.mrange : 0;
@@ -2910,7 +2990,7 @@ Params make_params(const moe_decode_handle* h, int T) {
   // LDS layout
   const int E = p.E, K = p.K;
   const int max_mr = E + (T * K + p.mrange - 1) / p.mrange;
-  const int nmb = T > kMBlock ? 4 : 1;
+  const int nmb = T > kMBlock ? 4 : p.gu_pair ? 2 : 1;   // MFMA blocks (or row blocks) of partial sums
   size_t off = 0;
   auto take = [&](size_t bytes) __attribute__((always_inline)) { size_t o = off; off = align_up(off + bytes, 16); return (int)o; };
   if (p.wide) {
@@ -3028,6 +3108,7 @@ moe_status moe_decode_create(const moe_decode_config* cfg, const moe_decode_weig
   h->cfg = *cfg;
   h->device = device;
   h->fmt = weight_format(*cfg);
+  for (int& v : h->occ_lds) v = -1;
   moe_status rc = MOE_OK;
   do {
     hipDeviceProp_t prop;
@@ -3105,10 +3186,21 @@ moe_status moe_decode_create(const moe_decode_config* cfg, const moe_decode_weig
 namespace {
 
 // The kernel of a variant (see run_impl) for weight format FMT; nullptr for
-// the wide variant of an MX format (wide items read FP8 tiles).
+// the wide variant of an MX format (wide items read FP8 tiles).  pair: the
+// full-tile MXFP4 kernel with paired gate/up items (variants 3 and 5 only).
 template <int FMT>
-const void* kernel_for(int variant, bool norm) {
+const void* kernel_for(int variant, bool norm, bool pair = false) {
   constexpr int q = kFullTiles / 2;   // down tiles per row block at I = 32 kFullTiles
+  if constexpr (FMT == kFmtMxfp4) {
+    if (pair && (variant == 3 || variant == 5)) {
+      if (variant == 3)
+        return norm ? (const void*)moe_decode_kernel<1, true, true, false, q, true, FMT, true>
+                    : (const void*)moe_decode_kernel<1, true, true, false, q, false, FMT, true>;
+      return norm ? (const void*)moe_decode_kernel<1, true, true, false, q + 1, true, FMT, true>
+                  : (const void*)moe_decode_kernel<1, true, true, false, q + 1, false, FMT, true>;
+    }
+  }
+  if (pair) return nullptr;
   if (variant == 4 || variant == 6 || variant == 7) {
     if constexpr (FMT != kFmtFp8) return nullptr;
     else if (variant == 6)
@@ -3208,18 +3300,25 @@ moe_status run_impl(moe_decode_handle* h, const void* x, int32_t T, void* y,
   // width without padding), 4 = more than 16 rows with wide items (FP8 only,
   // H = 64 kWideTiles, I = 64 kWideQ2), 6 and 7 = the same at I = 576 and 640
   // (one and two more down K tiles per row block)
-  const bool full = p.xs_stride > 0 && p.hs_stride > 0 && p.n_q13 == 4 * kFullTiles &&
-                    (p.n_q2 == kFullTiles / 2 || p.n_q2 == kFullTiles / 2 + 1) && p.local_topk && !p.router_tiles;
+  const bool full = p.full != 0;
+  // paired gate/up items exist only in the full-tile MXFP4 kernel, whose
+  // list then holds n_rb13 / 2 of them per M-range and twice the partial-sum
+  // area: refuse anything else before launching
+  if ((p.gu_pair && (!full || h->fmt != kFmtMxfp4 || 2 * p.n_gu_mr != p.n_rb13)) ||
+      (full && (p.xs_stride <= 0 || p.hs_stride <= 0))) {
+    if (prev != h->device) (void)hipSetDevice(prev);
+    return MOE_ERR_HIP;
+  }
   const int variant = p.wide ? (p.n_q2 == kWideQ2 ? 4 : p.n_q2 == kWideQ2 + 1 ? 6 : 7)
                       : full ? (p.n_q2 == kFullTiles / 2 ? 3 : 5) : p.xs_stride > 0 ? 0 : (T > kMBlock ? 2 : 1);
-  const void* fn = h->fmt == kFmtMxfp4   ? kernel_for<kFmtMxfp4>(variant, norm)
+  const void* fn = h->fmt == kFmtMxfp4   ? kernel_for<kFmtMxfp4>(variant, norm, p.gu_pair != 0)
                    : h->fmt == kFmtMxfp8 ? kernel_for<kFmtMxfp8>(variant, norm)
                                          : kernel_for<kFmtFp8>(variant, norm);
   if (!fn) {
     if (prev != h->device) (void)hipSetDevice(prev);
     return MOE_ERR_UNSUPPORTED;
   }
-  const int slot = variant + (norm ? 8 : 0);
+  const int slot = variant + (p.gu_pair ? 8 : 0) + (norm ? 16 : 0);
   if (h->occ_lds[slot] != p.lds_bytes) {
     int nb = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fn, kThreads, p.lds_bytes) != hipSuccess ||

@@ -94,6 +94,23 @@ def test_mx_ragged_T_on_one_handle():
     layer.close()
 
 
+def test_mxfp4_pairs_switch_with_T_on_one_handle():
+    """The full-tile MXFP4 kernel takes two row blocks per gate/up item when
+    the call can touch enough experts for two such items per workgroup (6 and
+    4 rows here) and single row blocks otherwise (1 and 3 rows): one 6-row
+    handle run at 6, 1, 4, 3 and 6 rows, each run against the oracle."""
+    wl = synth.BY_NAME["verify_t6_h4096_e256_k8_s1_mxfp4"]
+    inp = inputs_for(wl)
+    layer = device.make_layer(inp, max_tokens=wl.T)
+    for T in (6, 1, 4, 3, 6):
+        print(f"case {wl.name} T={T}", flush=True)
+        sub = synth.Inputs(wl.with_rows(T), inp.x[:T], inp.router_w, inp.router_b, inp.w13,
+                           inp.s13, inp.w2, inp.s2, inp.attempts[:T])
+        out = device.run_once(layer, np.ascontiguousarray(sub.x), wl.E, wl.K)
+        check_against_oracle(sub.workload, sub, out)
+    layer.close()
+
+
 BLOCK_CASES = [dataclasses.replace(w, name=w.name + "_prenorm", prenorm=True) for w in (
     mx(synth.BY_NAME["verify_t6_h4096_e256_k8_s1"], "mxfp4"),
     mx(synth.BY_NAME["verify_t6_h4096_e256_k8_s1"], "mxfp8"),
