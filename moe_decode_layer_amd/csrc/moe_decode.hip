@@ -2543,10 +2543,16 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
     if (!dyn && it >= p.i_pre_end) {
       if (!ensure_x()) break;
       if (!ensure_routing()) break;
-      // every gate/up item is static: a claimed one could be queued behind
-      // the busy workgroup that claimed it while an idle one takes a down
-      // item that waits for it
-      i_dyn = max(i_rgu_end, i_total - G);
+      // Up to a few gate/up items per workgroup, every gate/up item is
+      // static: a claimed one could be queued behind the busy workgroup that
+      // claimed it while an idle one takes a down item that waits for it
+      // (1 row 36 -> 42 us, 64 Zipf rows 124 -> 134 us with the last
+      // half-round claimed).  From 6 per workgroup on (384 rows: 8), the
+      // last half-round of them is claimed, so the workgroups that finish
+      // their static items first take it (384 rows 423.7 -> 405.7 us).
+      // Every workgroup computes the same S: it depends on the routing only.
+      i_dyn = i_rgu_end - p.i_pre_end >= 6 * G ? max(p.i_pre_end, min(i_rgu_end, i_total - G) - G / 2)
+                                               : max(i_rgu_end, i_total - G);
       if (it >= i_dyn) {        // past the static part: claim (blocking, once)
         dyn = true;
         if (tid == 0) L.misc[2] = i_dyn + cgroup + kClaimGroups * atomic_add_agent(claim_ctr, 1);
