@@ -147,7 +147,8 @@ typedef struct moe_decode_debug {
    * the 100 MHz device wall clock.  kind: 0 router, 1 shared gate/up,
    * 2 top-k, 3 shared down, 4 routed gate/up, 5 routed down, 6 exit ticket,
    * 7 combine; 8 and 9 time the phases of the workgroup's own routing
-   * (logits, top-k, placement).
+   * (logits, top-k, placement); 12 follows a top-k item: {rounds of its
+   * gather, ends of the first three rounds}.
    */
   int64_t* trace;
   int32_t trace_blocks;

@@ -211,7 +211,6 @@ struct Params {
   int lg_copies, lg_tp_log2;
   FDiv fd_x8;          // H / 8: 16-byte words of an x row
   FDiv fd_h2;          // I / 2: tagged words of an h row
-  FDiv fd_part[4];     // n E for n = 1..4: logits of a distributed top-k item's rows
   int n_rb13;          // gate/up row blocks per expert: I/8
   int n_q13;           // tiles along H: H/64
   int n_rb2;           // down row blocks: H/16
@@ -1285,6 +1284,60 @@ __device__ __forceinline__ bool gather_logits(KParams& p, const Lds& L) {
       want);
 }
 
+// A top-k item's partial logits: KS parts of its nt x E logits (part k of row
+// t0 + r at lgt[k T E + (t0 + r) E .. + E)) into LDS lg[k per_part + j],
+// per_part = nt E.  Thread tid owns words j = tid + b kThreads of every part:
+// at most kRouterKsMax x 4 of them (per_part <= kWaves E <= 4 kThreads), all
+// requested at once at fixed offsets from one base per part, with no
+// per-word division (parts past router_ks are skipped by a uniform branch,
+// so no dummy address is read by every thread: one hot line slows every
+// stream on its channel).  A position past the item's words (E < 256, or the
+// last item's fewer rows) reads the part's last word of the item and is
+// written to the thread's own scratch word.  While any word is stale all are
+// read again, round by round.
+__device__ __forceinline__ bool gather_topk_parts(KParams& p, const Lds& L, int t0, int per_part) {
+  constexpr int kJ = kWaves * kMaxExperts / kThreads;   // words per thread and part
+  const int KS = p.router_ks;
+  const size_t part = (size_t)p.T * p.E;
+  const uint64_t* const rows = p.lgt + (size_t)t0 * p.E;   // part 0 of the item's rows
+  SHARED uint32_t* const sink = L.tks + threadIdx.x;
+  long long t_end = 0;
+  int rounds = 0;
+  while (true) {
+    uint64_t v[kRouterKsMax][kJ];
+#pragma unroll
+    for (int k = 0; k < kRouterKsMax; ++k) {
+      if (k < KS) {                            // uniform
+        const uint64_t* const src = rows + k * part;
+#pragma unroll
+        for (int b = 0; b < kJ; ++b) v[k][b] = ld_tag(src + min((int)threadIdx.x + b * kThreads, per_part - 1));
+      }
+    }
+    bool stale = false;
+#pragma unroll
+    for (int k = 0; k < kRouterKsMax; ++k) {
+      if (k < KS) {
+#pragma unroll
+        for (int b = 0; b < kJ; ++b) {
+          const int j = (int)threadIdx.x + b * kThreads;
+          const bool in = j < per_part;
+          const bool ok = in && tag_ok(v[k][b], L.epoch);
+          *(ok ? (SHARED uint32_t*)L.lg + k * per_part + j : sink) = (uint32_t)v[k][b];
+          stale |= in && !ok;
+        }
+      }
+    }
+    if (p.trace && threadIdx.x == 0 && rounds < 3) ((SHARED long long*)(L.misc + 16))[rounds] = tl_clock(p);
+    if (!block_any(stale, L.misc + 8)) break;
+    if (!poll_round(p, &t_end, &rounds, L.misc + 1)) return false;
+  }
+  if (threadIdx.x == 0) {
+    *(SHARED long long*)(L.misc + 12) = tl_clock(p);
+    L.misc[14] = rounds;
+  }
+  return true;
+}
+
 // Distributed top-k item (large batches): rows 4 item .. 4 item + 3, one per
 // wave, to global memory.  The logits arrive as router_ks partial sums
 // (gathered as [ks][row][E]) and are added in ks order.
@@ -1293,15 +1346,8 @@ __device__ __forceinline__ bool topk_item(KParams& p, const Lds& L, int item) {
   const int nt = min(kWaves, p.T - t0);
   const int KS = p.router_ks;
   const int per_part = nt * p.E;
-  const uint32_t fm = p.fd_part[nt - 1].m, fs = p.fd_part[nt - 1].s;
   __syncthreads();                             // earlier readers of the lg area are done
-  if (!gather_tagged(p, L, KS * per_part,
-                     [&](int i) {
-                       const int k = (int)fdiv((uint32_t)i, fm, fs);
-                       return ld_tag(p.lgt + (size_t)k * p.T * p.E + (size_t)t0 * p.E + (i - k * per_part));
-                     },
-                     [&](int i, uint32_t v) { L.lg[i] = __uint_as_float(v); }))
-    return false;
+  if (!gather_topk_parts(p, L, t0, per_part)) return false;
   __syncthreads();
   for (int i = threadIdx.x; i < per_part; i += kThreads) {
     float v = L.lg[i];
@@ -2671,6 +2717,13 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
       }
     }
     record();
+    if (kind == 2 && trace && tid == 0 && n_ev < p.trace_cap) {
+      // a top-k item's gather: polling rounds, and when its first three ended
+      long long* r = trace + (size_t)(1 + n_ev) * 4;
+      st(r + 0, (long long)12 << 32 | (long long)min(L.misc[14], 0xffff));
+      for (int i = 0; i < 3; ++i) st(r + 1 + i, i <= L.misc[14] ? ((SHARED long long*)(L.misc + 16))[i] : 0ll);
+      ++n_ev;
+    }
     if (claim) {
       // the claim's result is first read here, so the wait for its round
       // trip lands after the item (the empty asm keeps the compiler from
@@ -2936,7 +2989,6 @@ Params make_params(const moe_decode_handle* h, int T) {
   p.fd_x8 = make_fdiv((uint32_t)(p.H / 8));
   p.fd_h2 = make_fdiv((uint32_t)(p.I / 2));
   p.fd_k = make_fdiv((uint32_t)p.K);
-  for (int n = 1; n <= 4; ++n) p.fd_part[n - 1] = make_fdiv((uint32_t)(n * p.E));
   p.topk_idx = h->topk_idx;
   p.topk_w = h->topk_w;
   p.h_scr = h->h_scr;
