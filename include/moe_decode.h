@@ -75,8 +75,9 @@ typedef struct moe_decode_config {
                             in SGLang", section 3.1) */
   int32_t num_shared;    /* S always-on shared experts; 0 or 1 */
   int32_t deadline_us;   /* bound on every in-kernel wait, microseconds; 0 = 1 s */
-  uint32_t flags;        /* bits 0-1: expert weight format, MOE_WEIGHTS_*; other
-                            bits reserved, must be 0 (else MOE_ERR_INVALID_ARG) */
+  uint32_t flags;        /* bits 0-1: expert weight format, MOE_WEIGHTS_*; bit 2:
+                            MOE_FLAG_COOPERATIVE; other bits reserved, must be 0
+                            (else MOE_ERR_INVALID_ARG) */
 } moe_decode_config;
 
 /*
@@ -97,6 +98,22 @@ typedef struct moe_decode_config {
 #define MOE_WEIGHTS_FP8   0u
 #define MOE_WEIGHTS_MXFP8 1u
 #define MOE_WEIGHTS_MXFP4 2u
+
+/*
+ * MOE_FLAG_COOPERATIVE: launch every run as a cooperative kernel.  The
+ * kernel's hand-offs need every workgroup of its grid (sized to what the
+ * device holds at once) to be resident together.  On an otherwise idle
+ * device they are; when another kernel may hold compute units (a shared
+ * device), a plain launch can leave some workgroups waiting for absent ones
+ * until the deadline (MOE_ERR_TIMEOUT).  A cooperative launch instead either
+ * runs the whole grid co-resident or fails (moe_decode_run returns
+ * MOE_ERR_HIP).  It costs about 15 us per call on MI355X, so it is off by
+ * default.  create returns MOE_ERR_UNSUPPORTED on a device without
+ * cooperative launch.  Source: "FlyDSL Mono Kernels for High-Interactivity
+ * LLM Serving in ATOM", section "What FlyDSL Provides" (enough cooperating
+ * blocks must stay resident for progress).
+ */
+#define MOE_FLAG_COOPERATIVE 4u
 
 /*
  * Weights, all device pointers, row-major and contiguous.  create() reads

@@ -25,6 +25,7 @@ MOE_WEIGHTS_FP8 = 0
 MOE_WEIGHTS_MXFP8 = 1
 MOE_WEIGHTS_MXFP4 = 2
 WEIGHT_FORMATS = {"fp8": MOE_WEIGHTS_FP8, "mxfp8": MOE_WEIGHTS_MXFP8, "mxfp4": MOE_WEIGHTS_MXFP4}
+MOE_FLAG_COOPERATIVE = 4
 
 # Functions declared in include/moe_decode.h, in declaration order.
 EXPORTS = (
@@ -181,8 +182,10 @@ def moe_decode_destroy(h) -> None:
 
 
 # ---- convenience layer over torch tensors ---------------------------------
-def make_config(T_max, H, E, K, I, S, deadline_us=0, weight_format: str = "fp8") -> moe_decode_config:
-    return moe_decode_config(T_max, H, E, K, I, S, deadline_us, WEIGHT_FORMATS[weight_format])
+def make_config(T_max, H, E, K, I, S, deadline_us=0, weight_format: str = "fp8",
+                cooperative: bool = False) -> moe_decode_config:
+    flags = WEIGHT_FORMATS[weight_format] | (MOE_FLAG_COOPERATIVE if cooperative else 0)
+    return moe_decode_config(T_max, H, E, K, I, S, deadline_us, flags)
 
 
 def weight_layout(cfg: moe_decode_config, bias: bool = False) -> dict:

@@ -2944,7 +2944,8 @@ int weight_format(const moe_decode_config& c) { return (int)(c.flags & 3u); }
 
 moe_status check_config(const moe_decode_config* c) {
   if (!c) return MOE_ERR_INVALID_ARG;
-  if ((c->flags & ~3u) != 0 || weight_format(*c) == 3 || c->deadline_us < 0) return MOE_ERR_INVALID_ARG;
+  if ((c->flags & ~(3u | MOE_FLAG_COOPERATIVE)) != 0 || weight_format(*c) == 3 || c->deadline_us < 0)
+    return MOE_ERR_INVALID_ARG;
   if (c->max_tokens < 1 || c->hidden < 1 || c->num_experts < 1 || c->top_k < 1 ||
       c->intermediate < 1 || c->num_shared < 0)
     return MOE_ERR_INVALID_ARG;
@@ -3173,6 +3174,7 @@ moe_status moe_decode_create(const moe_decode_config* cfg, const moe_decode_weig
     if (hipGetDeviceProperties(&prop, device) != hipSuccess) { rc = MOE_ERR_HIP; break; }
     h->n_cu = prop.multiProcessorCount;
     h->coop = prop.cooperativeLaunch;
+    if ((cfg->flags & MOE_FLAG_COOPERATIVE) && !h->coop) { rc = MOE_ERR_UNSUPPORTED; break; }
     // I: the packed (padded) width; I_s: the caller's
     const size_t E = cfg->num_experts, S = cfg->num_shared, H = cfg->hidden,
                  I = padded_intermediate(*cfg), I_s = cfg->intermediate, K = cfg->top_k, Tm = cfg->max_tokens;
@@ -3394,9 +3396,12 @@ moe_status run_impl(moe_decode_handle* h, const void* x, int32_t T, void* y,
   }
   // The grid is sized to what the device holds at once, so all workgroups
   // are resident together on an otherwise idle device; every wait has a
-  // deadline for the case where they are not.
+  // deadline for the case where they are not, and MOE_FLAG_COOPERATIVE makes
+  // the runtime guarantee it (or refuse the launch).
   void* args[] = {&p};
-  const hipError_t err = hipLaunchKernel(fn, dim3(grid), dim3(kThreads), args, p.lds_bytes, stream);
+  const hipError_t err = (h->cfg.flags & MOE_FLAG_COOPERATIVE)
+                             ? hipLaunchCooperativeKernel(fn, dim3(grid), dim3(kThreads), args, p.lds_bytes, stream)
+                             : hipLaunchKernel(fn, dim3(grid), dim3(kThreads), args, p.lds_bytes, stream);
   h->last_stream = stream;
   h->last_status = p.status;
   if (prev != h->device) (void)hipSetDevice(prev);

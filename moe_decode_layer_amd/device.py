@@ -32,14 +32,14 @@ def upload_weights(inp: Inputs, dev) -> dict:
 
 
 def make_layer(inp: Inputs, max_tokens: int | None = None, device: int = 0,
-               deadline_us: int = 0, free_weights: bool = True) -> binding.MoeDecode:
+               deadline_us: int = 0, free_weights: bool = True, cooperative: bool = False) -> binding.MoeDecode:
     """Create a handle for the inputs' workload; the standard-layout weight
     copies are dropped after create (the handle holds its own tile layout)."""
     wl = inp.workload
     dev = torch.device("cuda", device)
     w = upload_weights(inp, dev)
     cfg = binding.make_config(max_tokens or wl.T, wl.H, wl.E, wl.K, wl.I, wl.S, deadline_us,
-                              wl.weight_format)
+                              wl.weight_format, cooperative)
     layer = binding.MoeDecode(cfg, w, device)
     if wl.prenorm:
         layer.set_input_norm(to_device(inp.norm_w, dev), wl.norm_eps)

@@ -89,7 +89,9 @@ def test_guard(kw, T, want):
 @pytest.mark.parametrize("flags,want", [
     (0, binding.MOE_OK), (1, binding.MOE_OK), (2, binding.MOE_OK),
     (3, binding.MOE_ERR_INVALID_ARG),            # no fourth format
-    (4, binding.MOE_ERR_INVALID_ARG),            # reserved bits
+    (4, binding.MOE_OK), (6, binding.MOE_OK),    # cooperative launch, with any format
+    (7, binding.MOE_ERR_INVALID_ARG),
+    (8, binding.MOE_ERR_INVALID_ARG),            # reserved bits
     (0x80000001, binding.MOE_ERR_INVALID_ARG),
 ])
 def test_guard_flags(flags, want):

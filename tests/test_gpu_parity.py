@@ -101,6 +101,26 @@ def test_edge_shapes(wl):
     layer.close()
 
 
+@pytest.mark.parametrize("wl", [synth.WORKLOADS[1], SMALL[0]], ids=lambda w: w.name)
+def test_cooperative_launch_matches_the_plain_launch(wl):
+    """MOE_FLAG_COOPERATIVE (the runtime guarantees the grid co-resident or
+    refuses the launch): the same bits as the plain launch, run after run, and
+    the oracle's bars (6 rows: the full-tile variant; 20 rows: router tiles
+    and the distributed top-k)."""
+    print(f"case {wl.name} cooperative", flush=True)
+    inp = inputs_for(wl)
+    plain = device.make_layer(inp)
+    coop = device.make_layer(inp, cooperative=True)
+    want = device.run_once(plain, inp.x, wl.E, wl.K)
+    check_against_oracle(wl, inp, want)
+    for _ in range(3):
+        got = device.run_once(coop, inp.x, wl.E, wl.K)
+        for key in ("y", "topk_idx", "pair_rank", "expert_count"):
+            assert np.array_equal(got[key], want[key]), key
+    plain.close()
+    coop.close()
+
+
 def test_ragged_T_on_one_handle():
     wl = synth.WORKLOADS[1]
     print(f"case ragged T on {wl.name}", flush=True)
