@@ -37,6 +37,11 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_version_and_status_strings():
     assert binding.moe_decode_abi_version() == 4
+    # the check build() runs after compiling: libraries agree with their sources
+    import sys
+    sys.path.insert(0, os.path.dirname(INCLUDE))
+    import __graft_entry__
+    __graft_entry__.check_abi()
     for st in range(6):
         assert binding.moe_decode_status_string(st) != "unknown status"
     assert binding.moe_decode_status_string(99) == "unknown status"

@@ -31,12 +31,26 @@ def _bits(t):
     return t.cpu().numpy().view(np.uint16)
 
 
-@pytest.mark.parametrize("name", ["verify_t6_h4096_e256_k8_s1_prenorm", "verify_t384_h4096_e256_k8_s1_prenorm"],
-                         ids=["t6", "t384"])
-def test_graph_replays_match_eager_runs(name):
-    wl = synth.BY_NAME[name]
+def _inputs(wl):
+    att = GOLDEN["attempts"].get(wl.name)
+    if att is None:
+        att = O.attempts_for(wl, synth.candidate_rows(wl), synth.router_weights(wl),
+                             synth.zipf_bias(wl), synth.norm_weight(wl))
+    return synth.make_inputs(wl, att)
+
+
+CASES = [synth.BY_NAME["verify_t6_h4096_e256_k8_s1_prenorm"],
+         synth.BY_NAME["verify_t384_h4096_e256_k8_s1_prenorm"],
+         # MXFP4 weights: the full-tile kernel with two row blocks per gate/up item
+         dataclasses.replace(synth.BY_NAME["verify_t6_h4096_e256_k8_s1_mxfp4"],
+                             name="verify_t6_h4096_e256_k8_s1_mxfp4_prenorm", prenorm=True)]
+
+
+@pytest.mark.parametrize("wl", CASES, ids=["t6", "t384", "t6_mxfp4"])
+def test_graph_replays_match_eager_runs(wl):
+    name = wl.name
     print(f"case graph replay {name}", flush=True)
-    inp = synth.make_inputs(wl, GOLDEN["attempts"][wl.name])
+    inp = _inputs(wl)
     layer = device.make_layer(inp)
     dev = torch.device("cuda", 0)
     sets = []

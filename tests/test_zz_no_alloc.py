@@ -64,6 +64,23 @@ def test_static_workspace_matches_the_handle_workspace():
     lb.close()
 
 
+def test_static_workspace_with_mxfp4_weights():
+    """The MXFP4 full-tile kernel (two row blocks per gate/up item at 6 and 4
+    rows, one at 2) on the static array, against the handle workspace."""
+    wl = synth.BY_NAME["verify_t6_h4096_e256_k8_s1_mxfp4"]
+    print(f"case static workspace {wl.name}", flush=True)
+    inp = synth.make_inputs(wl, GOLDEN["attempts"][wl.name])
+    layer = device.make_layer(inp)
+    for T in (6, 4, 2):
+        ref = _run(layer, inp.x[:T], wl.E, wl.K, static=False)
+        got = _run(layer, inp.x[:T], wl.E, wl.K, static=True)
+        _same(got, ref, f"MXFP4, {T} rows")
+    r = O.forward(inp)
+    mx, mean = output_errors(O.bf16_bits_to_f64(_run(layer, inp.x, wl.E, wl.K, static=True)["y"]), r.y_bf16)
+    assert mx <= MAX_REL and mean <= MEAN_REL, (mx, mean)
+    layer.close()
+
+
 def test_static_workspace_limit_timeout_and_recovery():
     wa = synth.WORKLOADS[1]
     print(f"case static workspace limit {wa.name}", flush=True)
