@@ -476,6 +476,27 @@ __device__ __forceinline__ void flush_pending(int* ctr, int& pend) {
     pend = -1;
   }
 }
+// The same with N + extra operations younger than the stores, extra in
+// [0, 8] known only at run time (uniform).
+template <int N>
+__device__ __forceinline__ void flush_pending_rt(int* ctr, int& pend, int extra) {
+  static_assert(N + 8 <= 63, "vmcnt is 6 bits");
+  if (pend >= 0) {
+    switch (extra) {
+      case 0: wait_vm_older_than<N>(); break;
+      case 1: wait_vm_older_than<N + 1>(); break;
+      case 2: wait_vm_older_than<N + 2>(); break;
+      case 3: wait_vm_older_than<N + 3>(); break;
+      case 4: wait_vm_older_than<N + 4>(); break;
+      case 5: wait_vm_older_than<N + 5>(); break;
+      case 6: wait_vm_older_than<N + 6>(); break;
+      case 7: wait_vm_older_than<N + 7>(); break;
+      default: wait_vm_older_than<N + 8>(); break;
+    }
+    if (lane_id() == 0) count_done(ctr + kCtrRgDone + pend * kLine);
+    pend = -1;
+  }
+}
 __device__ __forceinline__ void flush_pending_now(int* ctr, int& pend) {
   if (pend >= 0) {
     wait_stores();
@@ -1793,6 +1814,8 @@ __device__ __forceinline__ bool down_item(KParams& p, const Lds& L, int slot, in
 // start of the item (16 KiB in flight per wave), then consumed in order, so
 // each MFMA waits only for its own tile.
 // ----------------------------------------------------------------------------
+constexpr int kAhead = 2;                      // A operand tiles read ahead (full-tile items)
+
 template <int NJ, int FMT>
 __device__ __forceinline__ void gu_item_full(KParams& p, const Lds& L, int slot, int sbase, int r0, int nrows,
                              int rb, bool shared, int parity, int& pend) {
@@ -1806,30 +1829,59 @@ __device__ __forceinline__ void gu_item_full(KParams& p, const Lds& L, int slot,
   const Sc* sc = (const Sc*)p.s13p + (blk * nq + w) * kTileRows + n;
   Wt wv[NJ];
   Sc sv[NJ];
+  // issued in tile order (the scheduler may not reorder them: loads return
+  // in issue order, so tile j must not wait for later tiles)
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
     wv[j] = ld_stream(wt + (size_t)j * kWaves * kWave);
     sv[j] = ld_stream(sc + (size_t)j * kWaves * kTileRows);
+    __builtin_amdgcn_sched_barrier(0);
   }
   flush_pending<2 * NJ>(L.ctr, pend);
-  const bool aval = n < nrows;
-  const int tok = shared ? (r0 + (aval ? n : 0)) : (int)L.rows[sbase + r0 + (aval ? n : 0)];
+  // Lanes past the item's rows read row 0: their products reach only output
+  // rows that are never stored, so the operand needs no masking.
+  const int nr = n < nrows ? n : 0;
+  const int tok = shared ? r0 + nr : (int)L.rows[sbase + r0 + nr];
   const SHARED uint16_t* arow = L.xs + (size_t)tok * p.xs_stride + 8 * kq + kTileK * w;
-  const u32x4 zero4 = {0u, 0u, 0u, 0u};
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  auto lda = [&](int j, int g) __attribute__((always_inline)) {
+    return *(const SHARED u32x4*)(arow + kTileK * kWaves * j + kGroup * g);
+  };
+  // The A operands are read kAhead tiles ahead of their MFMAs, and each
+  // MFMA's scaled sum is added one tile later, so neither the LDS nor the
+  // MFMA latency stalls the wave; the sums keep the (tile, group) order.
+  u32x4 a[NJ][2];
+#pragma unroll
+  for (int j = 0; j < kAhead && j < NJ; ++j) {
+    a[j][0] = lda(j, 0);
+    a[j][1] = lda(j, 1);
+  }
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f}, rl[2];
+  float sl[2];
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
+    if (j + kAhead < NJ) {
+      a[j + kAhead][0] = lda(j + kAhead, 0);
+      a[j + kAhead][1] = lda(j + kAhead, 1);
+    }
+    f32x4 r[2];
+    float s[2];
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
-      u32x4 a = *(const SHARED u32x4*)(arow + kTileK * kWaves * j + kGroup * g);
-      a = aval ? a : zero4;
-      const bf16x8 b = wdecode<FMT>(wv[j], g);
-      float s;
-      if constexpr (FMT == kFmtFp8) s = g ? sv[j].y : sv[j].x;
-      else s = mx_scale(sv[j], g);
-      acc += s * mfma16(as_bf16x8(a), b);
+      r[g] = mfma16(as_bf16x8(a[j][g]), wdecode<FMT>(wv[j], g));
+      if constexpr (FMT == kFmtFp8) s[g] = g ? sv[j].y : sv[j].x;
+      else s[g] = mx_scale(sv[j], g);
     }
+    if (j > 0) {
+      acc += sl[0] * rl[0];
+      acc += sl[1] * rl[1];
+    }
+    rl[0] = r[0];
+    rl[1] = r[1];
+    sl[0] = s[0];
+    sl[1] = s[1];
   }
+  acc += sl[0] * rl[0];
+  acc += sl[1] * rl[1];
   SHARED f32x4* red = (SHARED f32x4*)L.red + (parity & 1) * kWaves * kWave;
   red[w * kWave + lane] = acc;
   __syncthreads();
@@ -1858,37 +1910,70 @@ __device__ __forceinline__ void gu_item_full_pair(KParams& p, const Lds& L, int 
   const int nq = p.n_q13;                            // == 4 * NJ
   Wt wv[2][NJ];
   Sc sv[2][NJ];
+  const Wt* wt[2];
+  const Sc* sc[2];
 #pragma unroll
   for (int b = 0; b < 2; ++b) {
     const size_t blk = (size_t)slot * p.n_rb13 + 2 * rp + b;
-    const Wt* wt = (const Wt*)p.w13p + (blk * nq + w) * kWave + lane;
-    const Sc* sc = (const Sc*)p.s13p + (blk * nq + w) * kTileRows + n;
+    wt[b] = (const Wt*)p.w13p + (blk * nq + w) * kWave + lane;
+    sc[b] = (const Sc*)p.s13p + (blk * nq + w) * kTileRows + n;
+  }
+  // issued in the order the MFMAs consume them (K tile, then block), which
+  // the scheduler may not change: loads return in issue order
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      wv[b][j] = ld_stream(wt + (size_t)j * kWaves * kWave);
-      sv[b][j] = ld_stream(sc + (size_t)j * kWaves * kTileRows);
+  for (int j = 0; j < NJ; ++j) {
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      wv[b][j] = ld_stream(wt[b] + (size_t)j * kWaves * kWave);
+      sv[b][j] = ld_stream(sc[b] + (size_t)j * kWaves * kTileRows);
     }
+    __builtin_amdgcn_sched_barrier(0);
   }
   // 4 NJ = 64 loads are in flight; vmcnt holds at most 63, so the deferred
   // count also waits for the first of them (gate/up items rarely follow a
   // down item in this variant's list)
   flush_pending<(4 * NJ < 63 ? 4 * NJ : 63)>(L.ctr, pend);
-  const bool aval = n < nrows;
-  const int tok = shared ? (r0 + (aval ? n : 0)) : (int)L.rows[sbase + r0 + (aval ? n : 0)];
+  // lanes past the item's rows read row 0 (their output rows are not stored)
+  const int nr = n < nrows ? n : 0;
+  const int tok = shared ? r0 + nr : (int)L.rows[sbase + r0 + nr];
   const SHARED uint16_t* arow = L.xs + (size_t)tok * p.xs_stride + 8 * kq + kTileK * w;
-  const u32x4 zero4 = {0u, 0u, 0u, 0u};
-  f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+  auto lda = [&](int j, int g) __attribute__((always_inline)) {
+    return *(const SHARED u32x4*)(arow + kTileK * kWaves * j + kGroup * g);
+  };
+  // A read kAhead tiles ahead; each MFMA's scaled sum added one step later
+  u32x4 a[NJ][2];
 #pragma unroll
-  for (int j = 0; j < NJ; ++j) {
-#pragma unroll
-    for (int g = 0; g < 2; ++g) {
-      u32x4 a = *(const SHARED u32x4*)(arow + kTileK * kWaves * j + kGroup * g);
-      a = aval ? a : zero4;
-#pragma unroll
-      for (int b = 0; b < 2; ++b)
-        acc[b] += mx_scale(sv[b][j], g) * mfma16(as_bf16x8(a), fp4x8_to_bf16(wv[b][j][g]));
-    }
+  for (int j = 0; j < kAhead && j < NJ; ++j) {
+    a[j][0] = lda(j, 0);
+    a[j][1] = lda(j, 1);
   }
+  f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}}, rl[2];
+  float sl[2];
+#pragma unroll
+  for (int st = 0; st < 2 * NJ; ++st) {
+    const int j = st >> 1, g = st & 1;
+    if (g == 0 && j + kAhead < NJ) {
+      a[j + kAhead][0] = lda(j + kAhead, 0);
+      a[j + kAhead][1] = lda(j + kAhead, 1);
+    }
+    f32x4 r[2];
+    float s[2];
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      r[b] = mfma16(as_bf16x8(a[j][g]), fp4x8_to_bf16(wv[b][j][g]));
+      s[b] = mx_scale(sv[b][j], g);
+    }
+    if (st > 0) {
+      acc[0] += sl[0] * rl[0];
+      acc[1] += sl[1] * rl[1];
+    }
+    rl[0] = r[0];
+    rl[1] = r[1];
+    sl[0] = s[0];
+    sl[1] = s[1];
+  }
+  acc[0] += sl[0] * rl[0];
+  acc[1] += sl[1] * rl[1];
   SHARED f32x4* red = (SHARED f32x4*)L.red + (parity & 1) * kWaves * 2 * kWave;
 #pragma unroll
   for (int b = 0; b < 2; ++b) red[(b * kWaves + w) * kWave + lane] = acc[b];
@@ -1913,9 +1998,9 @@ __device__ __forceinline__ bool down_item_full(KParams& p, const Lds& L, int slo
   const int n = lane & 15, kq = lane >> 4;
   const int rb0 = rg * (kDownRows / kTileRows) + 2 * w;
   const int nrb = min(2, p.n_rb2 - rb0);
-  // The item's h rows (tagged words) are requested first, so they return
-  // before the weights; when every tag is current (h complete, the usual
-  // case) no counter needs to be polled at all.
+  // The item's h rows (tagged words) are requested with its weights; when
+  // every tag is current (h complete, the usual case) no counter needs to
+  // be polled at all.
   constexpr int kHFast = 8;                   // h words per thread on the fast path
   const int per_row = p.I / 2;
   const int nh = nrows * per_row;
@@ -1923,28 +2008,44 @@ __device__ __forceinline__ bool down_item_full(KParams& p, const Lds& L, int slo
   const uint64_t* hsrc = p.h_scr + (size_t)(sbase + r0) * per_row;
   Wt wv[2][NQ];
   Sc sv[2][NQ];
+  const Wt* wt[2];
+  const Sc* sc[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const size_t blk = (size_t)slot * p.n_rb2 + min(rb0 + j, p.n_rb2 - 1);
-    const Wt* wt = (const Wt*)p.w2p + blk * NQ * kWave + lane;
-    const Sc* sc = (const Sc*)p.s2p + blk * NQ * kTileRows + n;
-#pragma unroll
-    for (int q = 0; q < NQ; ++q) {
-      wv[j][q] = ld_stream(wt + (size_t)q * kWave);
-      sv[j][q] = ld_stream(sc + (size_t)q * kTileRows);
-    }
+    wt[j] = (const Wt*)p.w2p + blk * NQ * kWave + lane;
+    sc[j] = (const Sc*)p.s2p + blk * NQ * kTileRows + n;
   }
+  auto ldw = [&](int q) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      wv[j][q] = ld_stream(wt[j] + (size_t)q * kWave);
+      sv[j][q] = ld_stream(sc[j] + (size_t)q * kTileRows);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // Loads return in issue order, and the scheduler may not reorder these:
+  // K tiles [0, NQ1) are requested before the h words and [NQ1, NQ) after
+  // them, in the order the MFMAs consume them, so the first tiles' MFMAs
+  // run while the last tiles arrive.
+  constexpr int NQ1 = (NQ + 1) / 2;
+#pragma unroll
+  for (int q = 0; q < NQ1; ++q) ldw(q);
   uint64_t hv[kHFast];
+  int nb = 0;
   if (fast) {
     // only the batches that hold words are issued (the condition is uniform)
 #pragma unroll
     for (int b = 0; b < kHFast; ++b)
       hv[b] = b * kThreads < nh ? ld_tag(hsrc + min((int)threadIdx.x + b * kThreads, nh - 1)) : 0ull;
+    nb = (nh + kThreads - 1) / kThreads;
   }
-  // the 4 NQ weight and scale loads, then at least one h batch: waiting for
-  // all but the last 4 NQ + 1 operations covers the older stores
-  if (fast) flush_pending<4 * NQ + 1>(L.ctr, pend);
-  else flush_pending<4 * NQ>(L.ctr, pend);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int q = NQ1; q < NQ; ++q) ldw(q);
+  // the item's 4 NQ weight and scale loads and nb h loads are the youngest
+  // operations: waiting for all but those covers the older stores
+  flush_pending_rt<4 * NQ>(L.ctr, pend, nb);
   // the previous item's readers of the h area are done past this barrier
   __syncthreads();
   bool stale = !fast;
@@ -1971,26 +2072,39 @@ __device__ __forceinline__ bool down_item_full(KParams& p, const Lds& L, int slo
   }
   __syncthreads();
   if (nrb <= 0) return true;
-  const bool aval = n < nrows;
-  const SHARED uint16_t* arow = L.hs + (size_t)(aval ? n : 0) * p.hs_stride + 8 * kq;
-  const u32x4 zero4 = {0u, 0u, 0u, 0u};
-  f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+  // lanes past the item's rows read row 0 (their output rows are not stored)
+  const SHARED uint16_t* arow = L.hs + (size_t)(n < nrows ? n : 0) * p.hs_stride + 8 * kq;
+  // (K tile, group) steps st = 2 q + g: A read 2 kAhead steps ahead, each
+  // MFMA's scaled sum added one step later, in the same order
+  constexpr int NS = 2 * NQ;
+  u32x4 a[NS];
 #pragma unroll
-  for (int q = 0; q < NQ; ++q) {
+  for (int st = 0; st < 2 * kAhead && st < NS; ++st) a[st] = *(const SHARED u32x4*)(arow + kGroup * st);
+  f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}}, rl[2];
+  float sl[2];
 #pragma unroll
-    for (int g = 0; g < 2; ++g) {
-      u32x4 a = *(const SHARED u32x4*)(arow + kTileK * q + kGroup * g);
-      a = aval ? a : zero4;
+  for (int st = 0; st < NS; ++st) {
+    if (st + 2 * kAhead < NS) a[st + 2 * kAhead] = *(const SHARED u32x4*)(arow + kGroup * (st + 2 * kAhead));
+    const int q = st >> 1, g = st & 1;
+    f32x4 r[2];
+    float s[2];
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const bf16x8 b = wdecode<FMT>(wv[j][q], g);
-        float s;
-        if constexpr (FMT == kFmtFp8) s = g ? sv[j][q].y : sv[j][q].x;
-        else s = mx_scale(sv[j][q], g);
-        acc[j] += s * mfma16(as_bf16x8(a), b);
-      }
+    for (int j = 0; j < 2; ++j) {
+      r[j] = mfma16(as_bf16x8(a[st]), wdecode<FMT>(wv[j][q], g));
+      if constexpr (FMT == kFmtFp8) s[j] = g ? sv[j][q].y : sv[j][q].x;
+      else s[j] = mx_scale(sv[j][q], g);
     }
+    if (st > 0) {
+      acc[0] += sl[0] * rl[0];
+      acc[1] += sl[1] * rl[1];
+    }
+    rl[0] = r[0];
+    rl[1] = r[1];
+    sl[0] = s[0];
+    sl[1] = s[1];
   }
+  acc[0] += sl[0] * rl[0];
+  acc[1] += sl[1] * rl[1];
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     if (j < nrb) {
