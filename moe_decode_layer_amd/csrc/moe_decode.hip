@@ -982,8 +982,12 @@ __device__ __forceinline__ void router_tile_item(KParams& p, const Lds& L, int i
 // NORM (pre-norm block runs): x is xn; the first pass's weights are
 // requested before the wait for the item's rows.  LLONG_MIN: the wait failed.
 __device__ bool wait_rows(KParams& p, const Lds& L, int t0, int n);
-template <bool NORM = false>
-__device__ __forceinline__ long long router_item(KParams& p, const Lds& L, int item, bool stage_x) {
+struct NoHook {
+  __device__ void operator()() const {}
+};
+template <bool NORM = false, class Pre = NoHook, class Post = NoHook>
+__device__ __forceinline__ long long router_item(KParams& p, const Lds& L, int item, bool stage_x,
+                                                 Pre&& pre_barrier = Pre{}, Post&& post_barrier = Post{}) {
   const int w = wave_id(), lane = lane_id();
   const int e = item % p.E;
   const int t0 = (item / p.E) * kRouterRows;
@@ -1055,7 +1059,9 @@ __device__ __forceinline__ long long router_item(KParams& p, const Lds& L, int i
     const float s = wave_sum(acc[j]);
     if (lane == 0) part[w * kRouterRows + j] = s;
   }
+  pre_barrier();                               // (the run's arrival, when it is still to be read)
   __syncthreads();
+  post_barrier();
   // wave 0, lane 8 c + j: row j's logit, stored as copy c (every copy and row
   // in one store instruction)
   static_assert(kLgCopies * kRouterRows == kWave, "one lane per (copy, row)");
@@ -2511,38 +2517,55 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
   // Arrival: this run's index, hence its tag and counter block (see
   // kArriveGroups).  Every workgroup arrives before anything else, so the
   // counters advance by exactly kRunUnits per run even when a wait fails.
+  // Thread 0 requests it at once; the answer is read (arrival_take, thread
+  // 0, then a barrier, then arrival_use) right away, except in a workgroup
+  // whose first item is a small-batch router item: that item issues its
+  // loads first and takes the answer at its partial-sum barrier, since it
+  // needs the tag only for its stores.
+  unsigned long long arrival = 0;
   if (tid == 0) {
     const int cg = (int)blockIdx.x % kArriveGroups;
     const int in_group = (G - 1 - cg) / kArriveGroups + 1;
     const unsigned long long add = (int)blockIdx.x < kArriveGroups ? kRunUnits - (unsigned)(in_group - 1) : 1ull;
-    const unsigned long long v = __hip_atomic_fetch_add((GLOBAL unsigned long long*)(p.arrive + cg * (kLine / 2)), add,
-                                                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const unsigned long long n = v >> kRunUnitsLog2;
-    s_run.epoch = (uint32_t)(n % 0xffffffffull) + 1u;
-    s_run.ctr = p.ctr_base + (size_t)(n & 1) * kCtrHead;
+    arrival = __hip_atomic_fetch_add((GLOBAL unsigned long long*)(p.arrive + cg * (kLine / 2)), add,
+                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  __syncthreads();
-  L.epoch = __builtin_amdgcn_readfirstlane(s_run.epoch);
-  {
+  auto arrival_take = [&]() __attribute__((always_inline)) {
+    if (tid == 0) {
+      const unsigned long long n = arrival >> kRunUnitsLog2;
+      s_run.epoch = (uint32_t)(n % 0xffffffffull) + 1u;
+      s_run.ctr = p.ctr_base + (size_t)(n & 1) * kCtrHead;
+    }
+  };
+  auto arrival_use = [&]() __attribute__((always_inline)) {
+    L.epoch = __builtin_amdgcn_readfirstlane(s_run.epoch);
     const uint64_t a = (uint64_t)s_run.ctr;
     L.ctr = (int*)(((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32)) << 32) |
                    (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a));
-  }
-  // The last workgroup clears the other counter block for the next run (no
-  // one uses it during this run): every counter any shape can use.
-  if ((int)blockIdx.x == G - 1) {
-    int* q = p.ctr_base + (L.ctr == p.ctr_base ? kCtrHead : 0);
-    constexpr int n_words = 1 + kClaimGroups + (kMaxExperts + 1) + kMaxRowGroups + kGoLines;
-    for (int i = tid; i < n_words; i += kThreads) {
-      int off;
-      if (i < 1) off = kCtrTopkDone;
-      else if (i < 1 + kClaimGroups) off = kCtrTicket + (i - 1) * kLine;
-      else if (i < 1 + kClaimGroups + kMaxExperts + 1) off = kCtrHReady + (i - 1 - kClaimGroups) * kLine;
-      else if (i < 1 + kClaimGroups + kMaxExperts + 1 + kMaxRowGroups)
-        off = kCtrRgDone + (i - 1 - kClaimGroups - kMaxExperts - 1) * kLine;
-      else off = kCtrTopkGo + (i - 1 - kClaimGroups - kMaxExperts - 1 - kMaxRowGroups) * kGoStride;
-      store_agent(q + off, 0);
+    // The last workgroup clears the other counter block for the next run (no
+    // one uses it during this run): every counter any shape can use.
+    if ((int)blockIdx.x == G - 1) {
+      int* q = p.ctr_base + (L.ctr == p.ctr_base ? kCtrHead : 0);
+      constexpr int n_words = 1 + kClaimGroups + (kMaxExperts + 1) + kMaxRowGroups + kGoLines;
+      for (int i = tid; i < n_words; i += kThreads) {
+        int off;
+        if (i < 1) off = kCtrTopkDone;
+        else if (i < 1 + kClaimGroups) off = kCtrTicket + (i - 1) * kLine;
+        else if (i < 1 + kClaimGroups + kMaxExperts + 1) off = kCtrHReady + (i - 1 - kClaimGroups) * kLine;
+        else if (i < 1 + kClaimGroups + kMaxExperts + 1 + kMaxRowGroups)
+          off = kCtrRgDone + (i - 1 - kClaimGroups - kMaxExperts - 1) * kLine;
+        else off = kCtrTopkGo + (i - 1 - kClaimGroups - kMaxExperts - 1 - kMaxRowGroups) * kGoStride;
+        store_agent(q + off, 0);
+      }
     }
+  };
+  // (full-tile kernels: the router item is the workgroup's first item, run
+  // before the item loop below, so the answer is not held across the loop)
+  const bool arrival_lazy = FULL && !NORM && (int)blockIdx.x < p.i_router_end;
+  if (!arrival_lazy) {
+    arrival_take();
+    __syncthreads();
+    arrival_use();
   }
 
   if constexpr (NORM) norm_rows(p, L);
@@ -2697,8 +2720,18 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
   bool dyn = false;
   int i_dyn = INT_MAX;          // S, once routed
   const int cgroup = blockIdx.x % kClaimGroups;
-  int* const claim_ctr = L.ctr + kCtrTicket + cgroup * kLine;
+  auto claim_ctr = [&]() __attribute__((always_inline)) { return L.ctr + kCtrTicket + cgroup * kLine; };
   it = blockIdx.x;
+  if (arrival_lazy) {
+    // the first item, a router item, which also reads the run's arrival
+    kind = 0;
+    t_got = t_ready = tl_clock(p);
+    const bool stage = !x_staged && p.T <= kRouterRows;
+    t_ready = router_item<NORM>(p, L, it, stage, arrival_take, arrival_use);
+    x_staged = x_staged || stage;
+    record();
+    it += G;
+  }
   for (;;) {
     if (!dyn && it >= p.i_pre_end) {
       if (!ensure_x()) break;
@@ -2715,7 +2748,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
                                                : max(i_rgu_end, i_total - G);
       if (it >= i_dyn) {        // past the static part: claim (blocking, once)
         dyn = true;
-        if (tid == 0) L.misc[2] = i_dyn + cgroup + kClaimGroups * atomic_add_agent(claim_ctr, 1);
+        if (tid == 0) L.misc[2] = i_dyn + cgroup + kClaimGroups * atomic_add_agent(claim_ctr(), 1);
         __syncthreads();
         it = __builtin_amdgcn_readfirstlane(L.misc[2]);
         __syncthreads();
@@ -2723,7 +2756,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
     }
     const bool claim = routed && (dyn || it + G >= i_dyn);
     int claimed = 0;              // raw counter value; read only after the item
-    if (tid == 0 && claim) claimed = atomic_add_agent(claim_ctr, 1);
+    if (tid == 0 && claim) claimed = atomic_add_agent(claim_ctr(), 1);
     t_got = t_ready = tl_clock(p);
     if (it < p.i_router_end) {
       kind = 0;
