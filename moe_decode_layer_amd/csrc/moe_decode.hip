@@ -322,6 +322,31 @@ __device__ __forceinline__ bf16x8 wdecode(const typename WFmt<FMT>::W& w, int g)
 // read at each use directly: routed through a helper, even an inlined one,
 // they cost the items registers and spills.)
 __device__ __forceinline__ float mx_scale(uint32_t s, int g) { return e8m0_to_f32((s >> (8 * g)) & 0xffu); }
+// An MX group decoded with its E8M0 scale applied in the conversion: the
+// scale is a power of two, so each scaled element is still exact in bf16
+// (bf16 has fp32's exponent range) and the group's MFMA can accumulate
+// straight into the item's sums.  The full-tile items use this form.
+template <int FMT>
+__device__ __forceinline__ bf16x8 wdecode_scaled(const typename WFmt<FMT>::W& w, int g, float sc) {
+  static_assert(FMT != kFmtFp8, "FP8 scales are not powers of two");
+  bf16x2 a, b, c, d;
+  if constexpr (FMT == kFmtMxfp4) {
+    a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[g], sc, 0);
+    b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[g], sc, 1);
+    c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[g], sc, 2);
+    d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[g], sc, 3);
+  } else {
+    a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[2 * g], sc, false);
+    b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[2 * g], sc, true);
+    c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[2 * g + 1], sc, false);
+    d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[2 * g + 1], sc, true);
+  }
+  bf16x8 r = {a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+  return r;
+}
+__device__ __forceinline__ f32x4 mfma16_acc(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
 
 __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b) {
   const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
@@ -1861,33 +1886,49 @@ __device__ __forceinline__ void gu_item_full(KParams& p, const Lds& L, int slot,
     a[j][0] = lda(j, 0);
     a[j][1] = lda(j, 1);
   }
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f}, rl[2];
-  float sl[2];
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  if constexpr (FMT == kFmtFp8) {
+    f32x4 rl[2];
+    float sl[2];
 #pragma unroll
-  for (int j = 0; j < NJ; ++j) {
-    if (j + kAhead < NJ) {
-      a[j + kAhead][0] = lda(j + kAhead, 0);
-      a[j + kAhead][1] = lda(j + kAhead, 1);
-    }
-    f32x4 r[2];
-    float s[2];
+    for (int j = 0; j < NJ; ++j) {
+      if (j + kAhead < NJ) {
+        a[j + kAhead][0] = lda(j + kAhead, 0);
+        a[j + kAhead][1] = lda(j + kAhead, 1);
+      }
+      f32x4 r[2];
+      float s[2];
 #pragma unroll
-    for (int g = 0; g < 2; ++g) {
-      r[g] = mfma16(as_bf16x8(a[j][g]), wdecode<FMT>(wv[j], g));
-      if constexpr (FMT == kFmtFp8) s[g] = g ? sv[j].y : sv[j].x;
-      else s[g] = mx_scale(sv[j], g);
+      for (int g = 0; g < 2; ++g) {
+        r[g] = mfma16(as_bf16x8(a[j][g]), wdecode<FMT>(wv[j], g));
+        s[g] = g ? sv[j].y : sv[j].x;
+      }
+      if (j > 0) {
+        acc += sl[0] * rl[0];
+        acc += sl[1] * rl[1];
+      }
+      rl[0] = r[0];
+      rl[1] = r[1];
+      sl[0] = s[0];
+      sl[1] = s[1];
     }
-    if (j > 0) {
-      acc += sl[0] * rl[0];
-      acc += sl[1] * rl[1];
+    acc += sl[0] * rl[0];
+    acc += sl[1] * rl[1];
+  } else {
+    // MX: the scale goes into the decode; one running sum per group
+    f32x4 ag[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      if (j + kAhead < NJ) {
+        a[j + kAhead][0] = lda(j + kAhead, 0);
+        a[j + kAhead][1] = lda(j + kAhead, 1);
+      }
+#pragma unroll
+      for (int g = 0; g < 2; ++g)
+        ag[g] = mfma16_acc(as_bf16x8(a[j][g]), wdecode_scaled<FMT>(wv[j], g, mx_scale(sv[j], g)), ag[g]);
     }
-    rl[0] = r[0];
-    rl[1] = r[1];
-    sl[0] = s[0];
-    sl[1] = s[1];
+    acc = ag[0] + ag[1];
   }
-  acc += sl[0] * rl[0];
-  acc += sl[1] * rl[1];
   SHARED f32x4* red = (SHARED f32x4*)L.red + (parity & 1) * kWaves * kWave;
   red[w * kWave + lane] = acc;
   __syncthreads();
@@ -1953,33 +1994,22 @@ __device__ __forceinline__ void gu_item_full_pair(KParams& p, const Lds& L, int 
     a[j][0] = lda(j, 0);
     a[j][1] = lda(j, 1);
   }
-  f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}}, rl[2];
-  float sl[2];
+  // the scale goes into the decode; one running sum per block and group
+  f32x4 ag[2][2] = {{{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}}, {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}}};
 #pragma unroll
-  for (int st = 0; st < 2 * NJ; ++st) {
-    const int j = st >> 1, g = st & 1;
-    if (g == 0 && j + kAhead < NJ) {
+  for (int j = 0; j < NJ; ++j) {
+    if (j + kAhead < NJ) {
       a[j + kAhead][0] = lda(j + kAhead, 0);
       a[j + kAhead][1] = lda(j + kAhead, 1);
     }
-    f32x4 r[2];
-    float s[2];
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      r[b] = mfma16(as_bf16x8(a[j][g]), fp4x8_to_bf16(wv[b][j][g]));
-      s[b] = mx_scale(sv[b][j], g);
-    }
-    if (st > 0) {
-      acc[0] += sl[0] * rl[0];
-      acc[1] += sl[1] * rl[1];
-    }
-    rl[0] = r[0];
-    rl[1] = r[1];
-    sl[0] = s[0];
-    sl[1] = s[1];
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+        ag[b][g] = mfma16_acc(as_bf16x8(a[j][g]), wdecode_scaled<kFmtMxfp4>(wv[b][j], g, mx_scale(sv[b][j], g)),
+                              ag[b][g]);
   }
-  acc[0] += sl[0] * rl[0];
-  acc[1] += sl[1] * rl[1];
+  f32x4 acc[2] = {ag[0][0] + ag[0][1], ag[1][0] + ag[1][1]};
   SHARED f32x4* red = (SHARED f32x4*)L.red + (parity & 1) * kWaves * 2 * kWave;
 #pragma unroll
   for (int b = 0; b < 2; ++b) red[(b * kWaves + w) * kWave + lane] = acc[b];
@@ -2086,31 +2116,46 @@ __device__ __forceinline__ bool down_item_full(KParams& p, const Lds& L, int slo
   u32x4 a[NS];
 #pragma unroll
   for (int st = 0; st < 2 * kAhead && st < NS; ++st) a[st] = *(const SHARED u32x4*)(arow + kGroup * st);
-  f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}}, rl[2];
-  float sl[2];
+  f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+  if constexpr (FMT == kFmtFp8) {
+    f32x4 rl[2];
+    float sl[2];
 #pragma unroll
-  for (int st = 0; st < NS; ++st) {
-    if (st + 2 * kAhead < NS) a[st + 2 * kAhead] = *(const SHARED u32x4*)(arow + kGroup * (st + 2 * kAhead));
-    const int q = st >> 1, g = st & 1;
-    f32x4 r[2];
-    float s[2];
+    for (int st = 0; st < NS; ++st) {
+      if (st + 2 * kAhead < NS) a[st + 2 * kAhead] = *(const SHARED u32x4*)(arow + kGroup * (st + 2 * kAhead));
+      const int q = st >> 1, g = st & 1;
+      f32x4 r[2];
+      float s[2];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      r[j] = mfma16(as_bf16x8(a[st]), wdecode<FMT>(wv[j][q], g));
-      if constexpr (FMT == kFmtFp8) s[j] = g ? sv[j][q].y : sv[j][q].x;
-      else s[j] = mx_scale(sv[j][q], g);
+      for (int j = 0; j < 2; ++j) {
+        r[j] = mfma16(as_bf16x8(a[st]), wdecode<FMT>(wv[j][q], g));
+        s[j] = g ? sv[j][q].y : sv[j][q].x;
+      }
+      if (st > 0) {
+        acc[0] += sl[0] * rl[0];
+        acc[1] += sl[1] * rl[1];
+      }
+      rl[0] = r[0];
+      rl[1] = r[1];
+      sl[0] = s[0];
+      sl[1] = s[1];
     }
-    if (st > 0) {
-      acc[0] += sl[0] * rl[0];
-      acc[1] += sl[1] * rl[1];
+    acc[0] += sl[0] * rl[0];
+    acc[1] += sl[1] * rl[1];
+  } else {
+    // MX: the scale goes into the decode; one running sum per block and group
+    f32x4 ag[2][2] = {{{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}}, {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}}};
+#pragma unroll
+    for (int st = 0; st < NS; ++st) {
+      if (st + 2 * kAhead < NS) a[st + 2 * kAhead] = *(const SHARED u32x4*)(arow + kGroup * (st + 2 * kAhead));
+      const int q = st >> 1, g = st & 1;
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        ag[j][g] = mfma16_acc(as_bf16x8(a[st]), wdecode_scaled<FMT>(wv[j][q], g, mx_scale(sv[j][q], g)), ag[j][g]);
     }
-    rl[0] = r[0];
-    rl[1] = r[1];
-    sl[0] = s[0];
-    sl[1] = s[1];
+    acc[0] = ag[0][0] + ag[0][1];
+    acc[1] = ag[1][0] + ag[1][1];
   }
-  acc[0] += sl[0] * rl[0];
-  acc[1] += sl[1] * rl[1];
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     if (j < nrb) {
