@@ -2183,22 +2183,24 @@ __device__ __forceinline__ bool down_item_full(KParams& p, const Lds& L, int slo
 // per wave.  The waves' partial sums meet in LDS and wave w finishes block
 // kWideRb rg + w, summing the four K quarters in wave order.
 // ----------------------------------------------------------------------------
-template <int NMB>
+template <int NMB, int FMT>
 __device__ __forceinline__ void gu_item_wide(KParams& p, const Lds& L, int slot, int sbase, int r0, int nrows,
                                              int rg, bool shared, int& pend) {
+  using Wt = typename WFmt<FMT>::W;
+  using Sc = typename WFmt<FMT>::Scale;
   constexpr int NJ = kWideTiles;               // K tiles per wave
   constexpr int P = NMB == 1 ? 4 : 3;          // K steps in flight
   const int w = wave_id(), lane = lane_id();
   const int n = lane & 15, kq = lane >> 4;
   const int nq = p.n_q13;
   const int q0 = NJ * w;
-  const u32x4* wt[kWideRb];
-  const f32x2* sc[kWideRb];
+  const Wt* wt[kWideRb];
+  const Sc* sc[kWideRb];
 #pragma unroll
   for (int r = 0; r < kWideRb; ++r) {
     const size_t blk = (size_t)slot * p.n_rb13 + kWideRb * rg + r;
-    wt[r] = (const u32x4*)p.w13p + (blk * nq + q0) * kWave + lane;
-    sc[r] = (const f32x2*)p.s13p + (blk * nq + q0) * kTileRows + n;
+    wt[r] = (const Wt*)p.w13p + (blk * nq + q0) * kWave + lane;
+    sc[r] = (const Sc*)p.s13p + (blk * nq + q0) * kTileRows + n;
   }
   // A operand rows: rows past nrows read row r0 and are zeroed before the MFMA
   const uint16_t* arow[NMB];
@@ -2213,8 +2215,8 @@ __device__ __forceinline__ void gu_item_wide(KParams& p, const Lds& L, int slot,
   }
   struct Step {
     u32x4 a[2][NMB];
-    u32x4 w[kWideRb];
-    f32x2 s[kWideRb];
+    Wt w[kWideRb];
+    Sc s[kWideRb];
   };
   Step S[P];
   auto load = [&](Step& st_, int j) __attribute__((always_inline)) {
@@ -2252,10 +2254,17 @@ __device__ __forceinline__ void gu_item_wide(KParams& p, const Lds& L, int slot,
           for (int mb = 0; mb < NMB; ++mb) a[mb] = as_bf16x8(aval[mb] ? st_.a[g][mb] : zero4);
 #pragma unroll
           for (int r = 0; r < kWideRb; ++r) {
-            const bf16x8 b = fp8x8_to_bf16(st_.w[r][2 * g], st_.w[r][2 * g + 1]);
-            const float s = g ? st_.s[r].y : st_.s[r].x;
+            if constexpr (FMT == kFmtFp8) {
+              const bf16x8 b = fp8x8_to_bf16(st_.w[r][2 * g], st_.w[r][2 * g + 1]);
+              const float s = g ? st_.s[r].y : st_.s[r].x;
 #pragma unroll
-            for (int mb = 0; mb < NMB; ++mb) acc[r][mb] += s * mfma16(a[mb], b);
+              for (int mb = 0; mb < NMB; ++mb) acc[r][mb] += s * mfma16(a[mb], b);
+            } else {
+              // MX: the scale goes into the decode (exact), the MFMA accumulates
+              const bf16x8 b = wdecode_scaled<FMT>(st_.w[r], g, mx_scale(st_.s[r], g));
+#pragma unroll
+              for (int mb = 0; mb < NMB; ++mb) acc[r][mb] = mfma16_acc(a[mb], b, acc[r][mb]);
+            }
           }
         }
         // pin the sums here, step by step, so the step's registers are free
@@ -2300,9 +2309,11 @@ __device__ __forceinline__ void gu_item_wide(KParams& p, const Lds& L, int slot,
 // K tile by K tile, each h operand feeding its 8 row blocks, 16 tiles in
 // flight.
 // ----------------------------------------------------------------------------
-template <int NMB, int NQ>
+template <int NMB, int NQ, int FMT>
 __device__ __forceinline__ bool dn_item_wide(KParams& p, const Lds& L, int slot, int sbase, int r0, int nrows,
                                              int rg, int h_target, int& pend) {
+  using Wt = typename WFmt<FMT>::W;
+  using Sc = typename WFmt<FMT>::Scale;
   constexpr int NB = kWideDnBlocks;
   constexpr int NT = NB * NQ;                  // NQ K tiles per row block: I = 64 NQ
   constexpr int P = NMB == 1 ? 16 : 8;         // tiles in flight
@@ -2310,13 +2321,13 @@ __device__ __forceinline__ bool dn_item_wide(KParams& p, const Lds& L, int slot,
   const int n = lane & 15, kq = lane >> 4;
   const int grp = rg * kWaves + w;             // this wave's 128-column group
   const size_t blk0 = (size_t)slot * p.n_rb2 + (size_t)grp * NB;
-  const u32x4* wt = (const u32x4*)p.w2p + blk0 * NQ * kWave + lane;
-  const f32x2* sc = (const f32x2*)p.s2p + blk0 * NQ * kTileRows + n;
+  const Wt* wt = (const Wt*)p.w2p + blk0 * NQ * kWave + lane;
+  const Sc* sc = (const Sc*)p.s2p + blk0 * NQ * kTileRows + n;
   // tile t = NB q + b is K tile q of row block b; the ring turns over P / NB
   // K steps at a time (the last turn may hold fewer when P does not divide NT)
   static_assert(P % NB == 0 && NT >= P, "tile ring");
-  u32x4 wv[P];
-  f32x2 sv[P];
+  Wt wv[P];
+  Sc sv[P];
   // tile t into ring slot u = t mod P (u passed as a constant)
   auto load = [&](int t, int u) __attribute__((always_inline)) {
     const int q = t / NB, b = t % NB;
@@ -2361,10 +2372,17 @@ __device__ __forceinline__ bool dn_item_wide(KParams& p, const Lds& L, int slot,
         const int u = qq * NB + b;             // ring slot of tile t0 + u
 #pragma unroll
         for (int g = 0; g < 2; ++g) {
-          const bf16x8 bw = fp8x8_to_bf16(wv[u][2 * g], wv[u][2 * g + 1]);
-          const float s = g ? sv[u].y : sv[u].x;
+          if constexpr (FMT == kFmtFp8) {
+            const bf16x8 bw = fp8x8_to_bf16(wv[u][2 * g], wv[u][2 * g + 1]);
+            const float s = g ? sv[u].y : sv[u].x;
 #pragma unroll
-          for (int mb = 0; mb < NMB; ++mb) acc[b][mb] += s * mfma16(a[g][mb], bw);
+            for (int mb = 0; mb < NMB; ++mb) acc[b][mb] += s * mfma16(a[g][mb], bw);
+          } else {
+            // MX: the scale goes into the decode (exact), the MFMA accumulates
+            const bf16x8 bw = wdecode_scaled<FMT>(wv[u], g, mx_scale(sv[u], g));
+#pragma unroll
+            for (int mb = 0; mb < NMB; ++mb) acc[b][mb] = mfma16_acc(a[g][mb], bw, acc[b][mb]);
+          }
         }
         // pin the sums here, in tile order (else the compiler runs every MFMA
         // first and keeps all their results for the multiply-adds at the end)
@@ -2519,12 +2537,10 @@ __device__ bool wait_rows(KParams& p, const Lds& L, int t0, int n) {
 // (H = 64 kFullTiles, I = 32 kFullTiles or, NQ2 = kFullTiles / 2 + 1, 576)
 // and local routing only; the other variants hold the general code.  Each variant
 // carries only the code its batches reach, which keeps register pressure
-// (and spills) down.  FMT: the expert weight format (WFmt); the wide items
-// exist for FP8 only.
+// (and spills) down.  FMT: the expert weight format (WFmt).
 template <int NMBMAX, bool XL, bool FULL, bool WIDE, int NQ2 = kFullTiles / 2, bool NORM = false, int FMT = kFmtFp8,
           bool PAIR = false>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(NMBMAX == 1 || WIDE ? 2 : 1))) moe_decode_kernel(Params arg) {
-  static_assert(!WIDE || FMT == kFmtFp8, "wide items read FP8 tiles");
   static_assert(!PAIR || (FULL && FMT == kFmtMxfp4), "paired gate/up items: full-tile MXFP4 only");
   KParams& p = *(const CONSTANT Params*)__builtin_amdgcn_kernarg_segment_ptr();
   (void)arg;
@@ -2719,8 +2735,8 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
     const int nmb = (nrows + kMBlock - 1) / kMBlock;
     const int par = gu_count++;
     if constexpr (WIDE) {
-      if (nmb <= 1) gu_item_wide<1>(p, L, slot, sbase, r0, nrows, rb, shared, pend_rg);
-      else gu_item_wide<2>(p, L, slot, sbase, r0, nrows, rb, shared, pend_rg);
+      if (nmb <= 1) gu_item_wide<1, FMT>(p, L, slot, sbase, r0, nrows, rb, shared, pend_rg);
+      else gu_item_wide<2, FMT>(p, L, slot, sbase, r0, nrows, rb, shared, pend_rg);
     } else if constexpr (PAIR) {
       // launched only for lists built for pairs (gu_pair: n_gu_mr = n_rb13 / 2,
       // rb the pair index; checked on the host)
@@ -2736,8 +2752,8 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(N
   auto run_down = [&](int slot, int sbase, int r0, int nrows, int rg, int ht) __attribute__((always_inline)) -> bool {
     const int nmb = (nrows + kMBlock - 1) / kMBlock;
     if constexpr (WIDE) {
-      if (nmb <= 1) return dn_item_wide<1, NQ2>(p, L, slot, sbase, r0, nrows, rg, ht, pend_rg);
-      return dn_item_wide<2, NQ2>(p, L, slot, sbase, r0, nrows, rg, ht, pend_rg);
+      if (nmb <= 1) return dn_item_wide<1, NQ2, FMT>(p, L, slot, sbase, r0, nrows, rg, ht, pend_rg);
+      return dn_item_wide<2, NQ2, FMT>(p, L, slot, sbase, r0, nrows, rg, ht, pend_rg);
     } else if constexpr (FULL) return down_item_full<NQ2, FMT>(p, L, slot, sbase, r0, nrows, rg, ht, pend_rg);
     else if (XL && p.hs_stride > 0) return down_item<1, XL, FMT>(p, L, slot, sbase, r0, nrows, rg, ht, pend_rg);
     else if (NMBMAX == 1 || nmb <= 1) return down_item<1, false, FMT>(p, L, slot, sbase, r0, nrows, rg, ht, pend_rg);
@@ -3200,7 +3216,7 @@ Params make_params(const moe_decode_handle* h, int T) {
   p.n_q2 = p.I / kTileK;
   p.n_rg = (p.H + kDownRows - 1) / kDownRows;
   p.nch = (T + 63) / 64;
-  p.wide = h->fmt == kFmtFp8 && T > kMBlock && p.n_q13 == kWaves * kWideTiles &&
+  p.wide = T > kMBlock && p.n_q13 == kWaves * kWideTiles &&
            p.n_q2 >= kWideQ2 && p.n_q2 <= kWideQ2 + 2;
   p.mrange = p.wide ? kWideRows : kMRange;
   // The full-tile variant: x and h in LDS (at most 16 rows), H = 64 kFullTiles,
@@ -3437,8 +3453,7 @@ moe_status moe_decode_create(const moe_decode_config* cfg, const moe_decode_weig
 
 namespace {
 
-// The kernel of a variant (see run_impl) for weight format FMT; nullptr for
-// the wide variant of an MX format (wide items read FP8 tiles).  pair: the
+// The kernel of a variant (see run_impl) for weight format FMT.  pair: the
 // full-tile MXFP4 kernel with paired gate/up items (variants 3 and 5 only).
 template <int FMT>
 const void* kernel_for(int variant, bool norm, bool pair = false) {
@@ -3454,8 +3469,7 @@ const void* kernel_for(int variant, bool norm, bool pair = false) {
   }
   if (pair) return nullptr;
   if (variant == 4 || variant == 6 || variant == 7) {
-    if constexpr (FMT != kFmtFp8) return nullptr;
-    else if (variant == 6)
+    if (variant == 6)
       return norm ? (const void*)moe_decode_kernel<2, false, false, true, kWideQ2 + 1, true, FMT>
                   : (const void*)moe_decode_kernel<2, false, false, true, kWideQ2 + 1, false, FMT>;
     else if (variant == 7)

@@ -98,10 +98,11 @@ WORKLOADS = [
 # around the layer).
 PRENORM = [dataclasses.replace(w, name=w.name + "_prenorm", prenorm=True) for w in WORKLOADS]
 
-# The 6-row, 1-row and tiny workloads with MX expert weights (the pages' MoE
-# formats: MXFP4 and MXFP8 with E8M0 group-32 scales).
+# The workloads with MX expert weights (the pages' MoE formats: MXFP4 and
+# MXFP8 with E8M0 group-32 scales): 6 rows, 1 row, tiny, 64 Zipf rows and
+# 384 rows.
 MX = [dataclasses.replace(w, name=f"{w.name}_{fmt}", weight_format=fmt)
-      for fmt in ("mxfp4", "mxfp8") for w in (WORKLOADS[1], WORKLOADS[2], WORKLOADS[0])]
+      for fmt in ("mxfp4", "mxfp8") for w in (WORKLOADS[1], WORKLOADS[2], WORKLOADS[0], WORKLOADS[3], WORKLOADS[4])]
 
 # The pages' per-GPU intermediate width 576 (run natively) at 6, 64 and 384
 # rows, and 384 rows at 640 (576 padded to whole 128-K tiles, as the pages'

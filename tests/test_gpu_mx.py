@@ -6,9 +6,10 @@ within max|d|/max|o| <= 1e-2 and sum|d|/sum|o| <= 2e-3 on every row.
 Every kernel variant an MX handle can take is reached: x in LDS with the
 full-tile items (H 4096, I 512, up to 16 rows) and its I = 576 form, x in LDS
 with the general items, x in global memory with one and with four MFMA blocks
-per item (batches above 16 rows: MX handles have no wide items), router tiles
-with distributed top-k, an intermediate width padded from 288 to 320, and
-pre-norm block runs and clipped SwiGLU on MX weights.
+per item (batches above 16 rows at other shapes), the wide items (batches
+above 16 rows at H 4096, I 512: 64 Zipf rows and 384 rows, both formats),
+router tiles with distributed top-k, an intermediate width padded from 288 to
+320, and pre-norm block runs and clipped SwiGLU on MX weights.
 """
 import dataclasses
 import json
@@ -58,9 +59,9 @@ EDGE = [
     synth.Workload("t6_h4096_e256_k8_s1_i576", T=6, H=4096, E=256, K=8, S=1, I=576),      # full items, 9 down tiles
     synth.Workload("t6_h4096_e256_k8_s1_i288", T=6, H=4096, E=256, K=8, S=1, I=288),      # padded to 320
     synth.Workload("t9_h4096_e256_k8_s1", T=9, H=4096, E=256, K=8, S=1, I=512),           # x in global memory
-    synth.Workload("t64_h4096_e256_k8_s1", T=64, H=4096, E=256, K=8, S=1, I=512, zipf_s=1.2),  # 4 MFMA blocks
+    synth.Workload("t64_h4096_e256_k8_s1", T=64, H=4096, E=256, K=8, S=1, I=512, zipf_s=1.2),  # wide items
     synth.Workload("t20_h128_e8_k8_s1", T=20, H=128, E=8, K=8, S=1, I=64),                # router tiles, K = E
-    synth.Workload("t70_h192_e4_k2_s1", T=70, H=192, E=4, K=2, S=1, I=192),               # ragged H, 2 chunks
+    synth.Workload("t70_h192_e4_k2_s1", T=70, H=192, E=4, K=2, S=1, I=192),               # ragged H, 2 chunks, 4 MFMA blocks
     synth.Workload("t3_h64_e1_k1_s0", T=3, H=64, E=1, K=1, S=0, I=64),                    # one expert
 ]
 EDGE_CASES = [mx(w, f) for w in EDGE for f in ("mxfp4", "mxfp8")] + [
@@ -81,7 +82,8 @@ def test_mx_edge_shapes(wl):
 
 def test_mx_ragged_T_on_one_handle():
     """One MXFP4 handle for 384 rows run at 384, 17, 64, 1 and 6 rows: the
-    general variants at every batch size, each run against the oracle."""
+    wide items above 16 rows and the general ones below, each run against
+    the oracle."""
     wl = EDGE_CASES[-2]
     inp = inputs_for(wl)
     layer = device.make_layer(inp, max_tokens=wl.T)
