@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define MOE_DECODE_ABI_VERSION 4
+#define MOE_DECODE_ABI_VERSION 5
 
 typedef int32_t moe_status;
 #define MOE_OK                0  /* success */
@@ -299,6 +299,23 @@ moe_status moe_decode_run_block(moe_decode_handle* h, const void* x, int32_t T, 
  * for a NULL handle, L <= 0 or NaN.  No device work.
  */
 moe_status moe_decode_set_swiglu_limit(moe_decode_handle* h, float limit);
+
+/*
+ * Kernel timing, for runs enqueued after this call (all three run forms):
+ * with two events set, each run's single kernel launch records start_event
+ * when the kernel starts and stop_event when it ends (hipExtLaunchKernel's
+ * launch events: the times of the kernel itself, not of event records
+ * queued around it).  Source: "SGLang's Low-Latency Mode Boosts
+ * DeepSeek-V4.1-Flash Speed by 1.56x on AMD", section "AMD keeps the layer
+ * resident" (the layer's latency per call, as the pages report it).
+ * start_event and stop_event are hipEvent_t handles the caller created on the
+ * handle's device and keeps alive while they are set; both NULL turns timing
+ * off (the default).  MOE_ERR_INVALID_ARG for a NULL handle or exactly one
+ * NULL event.  A run with events set on a handle created with
+ * MOE_FLAG_COOPERATIVE returns MOE_ERR_UNSUPPORTED (a cooperative launch
+ * takes no events).  Not for use under graph capture.  No device work.
+ */
+moe_status moe_decode_set_launch_events(moe_decode_handle* h, void* start_event, void* stop_event);
 
 /*
  * Wait for the last run's stream and report its in-kernel status:

@@ -37,6 +37,7 @@ EXPORTS = (
     "moe_decode_set_input_norm",
     "moe_decode_run_block",
     "moe_decode_set_swiglu_limit",
+    "moe_decode_set_launch_events",
     "moe_decode_check",
     "moe_decode_destroy",
     "moe_decode_status_string",
@@ -118,6 +119,8 @@ def lib() -> ctypes.CDLL:
         L.moe_decode_run_block.argtypes = [P, P, ctypes.c_int32, P, ctypes.POINTER(moe_decode_debug), P]
         L.moe_decode_set_swiglu_limit.restype = ctypes.c_int32
         L.moe_decode_set_swiglu_limit.argtypes = [P, ctypes.c_float]
+        L.moe_decode_set_launch_events.restype = ctypes.c_int32
+        L.moe_decode_set_launch_events.argtypes = [P, P, P]
         L.moe_decode_check.restype = ctypes.c_int32
         L.moe_decode_check.argtypes = [P]
         L.moe_decode_destroy.restype = None
@@ -171,6 +174,10 @@ def moe_decode_run_block(h, x_ptr: int, T: int, y_ptr: int, dbg: moe_decode_debu
 
 def moe_decode_set_swiglu_limit(h, limit: float) -> int:
     return lib().moe_decode_set_swiglu_limit(h, limit)
+
+
+def moe_decode_set_launch_events(h, start_event: int | None, stop_event: int | None) -> int:
+    return lib().moe_decode_set_launch_events(h, start_event, stop_event)
 
 
 def moe_decode_check(h) -> int:
@@ -331,6 +338,20 @@ class MoeDecode:
         st = moe_decode_set_swiglu_limit(self.handle, limit)
         if st != MOE_OK:
             raise MoeDecodeError("moe_decode_set_swiglu_limit", st)
+
+    def set_launch_events(self, start=None, stop=None) -> None:
+        """Kernel start and stop events for later runs (torch.cuda.Event with
+        timing, already recorded once so that they exist), or None, None to
+        turn timing off."""
+        def raw(e):
+            if e is None:
+                return None
+            if not e.cuda_event:
+                raise ValueError("the event has not been created yet: record it once first")
+            return e.cuda_event
+        st = moe_decode_set_launch_events(self.handle, raw(start), raw(stop))
+        if st != MOE_OK:
+            raise MoeDecodeError("moe_decode_set_launch_events", st)
 
     def run_block(self, x, y, T: int | None = None, debug: dict | None = None, stream=None) -> None:
         """Enqueue one pre-norm block call: y = x + layer(RMSNorm(x)), [T][H] bf16."""

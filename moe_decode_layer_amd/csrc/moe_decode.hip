@@ -57,6 +57,7 @@
 // points is fp32 accumulation.  Activation rows are the A operand; rows past
 // the expert's row count are zero.
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 
 #include <limits.h>
 #include <stdint.h>
@@ -3136,6 +3137,8 @@ struct moe_decode_handle {
   int* norm_ready = nullptr;     // [max_tokens]
   float norm_eps = 0.f;
   float swiglu_limit = INFINITY; // moe_decode_set_swiglu_limit
+  hipEvent_t ev_start = nullptr;  // moe_decode_set_launch_events
+  hipEvent_t ev_stop = nullptr;
   hipStream_t last_stream = nullptr;
   int* last_status = nullptr;    // status word of the last run's workspace (handle's or static)
   std::mutex mu;
@@ -3605,9 +3608,16 @@ moe_status run_impl(moe_decode_handle* h, const void* x, int32_t T, void* y,
   // deadline for the case where they are not, and MOE_FLAG_COOPERATIVE makes
   // the runtime guarantee it (or refuse the launch).
   void* args[] = {&p};
-  const hipError_t err = (h->cfg.flags & MOE_FLAG_COOPERATIVE)
-                             ? hipLaunchCooperativeKernel(fn, dim3(grid), dim3(kThreads), args, p.lds_bytes, stream)
-                             : hipLaunchKernel(fn, dim3(grid), dim3(kThreads), args, p.lds_bytes, stream);
+  const bool coop = (h->cfg.flags & MOE_FLAG_COOPERATIVE) != 0;
+  if (coop && h->ev_start) {                  // a cooperative launch takes no events
+    if (prev != h->device) (void)hipSetDevice(prev);
+    return MOE_ERR_UNSUPPORTED;
+  }
+  const hipError_t err =
+      coop ? hipLaunchCooperativeKernel(fn, dim3(grid), dim3(kThreads), args, p.lds_bytes, stream)
+      : h->ev_start
+          ? hipExtLaunchKernel(fn, dim3(grid), dim3(kThreads), args, p.lds_bytes, stream, h->ev_start, h->ev_stop, 0)
+          : hipLaunchKernel(fn, dim3(grid), dim3(kThreads), args, p.lds_bytes, stream);
   h->last_stream = stream;
   h->last_status = p.status;
   if (prev != h->device) (void)hipSetDevice(prev);
@@ -3672,6 +3682,14 @@ moe_status moe_decode_set_swiglu_limit(moe_decode_handle* h, float limit) {
   if (!h || !(limit > 0.f)) return MOE_ERR_INVALID_ARG;   // NaN fails the test too
   std::lock_guard<std::mutex> lock(h->mu);
   h->swiglu_limit = limit;
+  return MOE_OK;
+}
+
+moe_status moe_decode_set_launch_events(moe_decode_handle* h, void* start_event, void* stop_event) {
+  if (!h || (start_event == nullptr) != (stop_event == nullptr)) return MOE_ERR_INVALID_ARG;
+  std::lock_guard<std::mutex> lock(h->mu);
+  h->ev_start = (hipEvent_t)start_event;
+  h->ev_stop = (hipEvent_t)stop_event;
   return MOE_OK;
 }
 

@@ -36,7 +36,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert binding.moe_decode_abi_version() == 4
+    assert binding.moe_decode_abi_version() == 5
     # the check build() runs after compiling: libraries agree with their sources
     import sys
     sys.path.insert(0, os.path.dirname(INCLUDE))
@@ -144,3 +144,9 @@ def test_debug_struct_layout_matches_the_header():
     # the pointer appended for block runs sits after the three int32 fields
     assert binding.moe_decode_debug.norm_x.offset == 6 * 8 + 3 * 4 + 4
     assert ctypes.sizeof(binding.moe_decode_debug) == 6 * 8 + 3 * 4 + 4 + 8
+
+
+def test_launch_events_guard():
+    """The timing hook refuses a NULL handle and a half-set pair, without a GPU."""
+    assert binding.moe_decode_set_launch_events(None, None, None) == binding.MOE_ERR_INVALID_ARG
+    assert binding.moe_decode_set_launch_events(None, 0x1000, None) == binding.MOE_ERR_INVALID_ARG
