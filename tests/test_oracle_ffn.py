@@ -146,3 +146,43 @@ def test_power_of_two_down_scales_scale_output_exactly():
     scaled = O.forward(inp)
     assert np.array_equal(scaled.y, 4.0 * base.y)
     assert np.array_equal(scaled.y_bf16, 4.0 * base.y_bf16)
+
+
+@pytest.mark.parametrize("wl", SMALL[1:], ids=lambda w: w.name)
+def test_relabelled_experts_change_nothing(wl):
+    """Moving routed expert e to id p[e] (its router row, bias and weights
+    together) selects p[idx] with the same weights and gives the same y: the
+    layer depends on which expert a row picks, not on its number.  Catches an
+    expert looked up by its top-k slot, or a router row taken by position."""
+    inp = _inputs(wl)
+    base = O.forward(inp)
+    E = wl.E
+    p = np.random.default_rng(11).permutation(E)
+    moved = synth.Inputs(wl, inp.x, inp.router_w.copy(), None if inp.router_b is None else inp.router_b.copy(),
+                         inp.w13.copy(), inp.s13.copy(), inp.w2.copy(), inp.s2.copy(), inp.attempts)
+    moved.router_w[p] = inp.router_w
+    if inp.router_b is not None:
+        moved.router_b[p] = inp.router_b
+    for name in ("w13", "s13", "w2", "s2"):
+        getattr(moved, name)[p] = getattr(inp, name)[:E]   # the shared slot E stays
+    res = O.forward(moved)
+    assert np.array_equal(res.idx, p[base.idx])
+    np.testing.assert_allclose(res.w, base.w, rtol=1e-14, atol=0)
+    np.testing.assert_allclose(res.y, base.y, rtol=1e-12, atol=1e-12 * np.abs(base.y).max())
+
+
+@pytest.mark.parametrize("wl", SMALL[1:], ids=lambda w: w.name)
+def test_permuted_rows_permute_the_output(wl):
+    """Rows are independent: permuting the batch's rows permutes the routing
+    and the output rows and changes nothing else (a row's expert outputs are
+    never mixed with another row's)."""
+    inp = _inputs(wl)
+    base = O.forward(inp)
+    q = np.random.default_rng(12).permutation(wl.T)
+    moved = synth.Inputs(wl, inp.x[q].copy(), inp.router_w, inp.router_b, inp.w13, inp.s13, inp.w2, inp.s2,
+                         inp.attempts[q].copy())
+    res = O.forward(moved)
+    assert np.array_equal(res.idx, base.idx[q])
+    np.testing.assert_allclose(res.w, base.w[q], rtol=1e-14, atol=0)
+    np.testing.assert_allclose(res.y, base.y[q], rtol=1e-12, atol=1e-12 * np.abs(base.y).max())
+    assert np.array_equal(res.placement.count, base.placement.count)
