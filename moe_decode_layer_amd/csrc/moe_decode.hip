@@ -2203,7 +2203,11 @@ __device__ __forceinline__ void gu_item_wide(KParams& p, const Lds& L, int slot,
     wt[r] = (const Wt*)p.w13p + (blk * nq + q0) * kWave + lane;
     sc[r] = (const Sc*)p.s13p + (blk * nq + q0) * kTileRows + n;
   }
-  // A operand rows: rows past nrows read row r0 and are zeroed before the MFMA
+  // A operand rows: rows past nrows read row r0.  Their products reach only
+  // output rows that are never stored, so zeroing them is not needed; it is
+  // kept for the byte formats, whose loops measured faster with it, and
+  // dropped for MXFP4, whose loop (half the bytes per MFMA) pays for the
+  // selects' issue slots
   const uint16_t* arow[NMB];
   bool aval[NMB];
 #pragma unroll
@@ -2252,7 +2256,8 @@ __device__ __forceinline__ void gu_item_wide(KParams& p, const Lds& L, int slot,
         for (int g = 0; g < 2; ++g) {
           bf16x8 a[NMB];
 #pragma unroll
-          for (int mb = 0; mb < NMB; ++mb) a[mb] = as_bf16x8(aval[mb] ? st_.a[g][mb] : zero4);
+          for (int mb = 0; mb < NMB; ++mb)
+            a[mb] = as_bf16x8(FMT == kFmtMxfp4 || aval[mb] ? st_.a[g][mb] : zero4);
 #pragma unroll
           for (int r = 0; r < kWideRb; ++r) {
             if constexpr (FMT == kFmtFp8) {
@@ -2367,7 +2372,8 @@ __device__ __forceinline__ bool dn_item_wide(KParams& p, const Lds& L, int slot,
       for (int g = 0; g < 2; ++g)
 #pragma unroll
         for (int mb = 0; mb < NMB; ++mb)
-          a[g][mb] = as_bf16x8(aval[mb] ? *(const SHARED u32x4*)(arow[mb] + kTileK * q + kGroup * g) : zero4);
+          a[g][mb] = as_bf16x8(FMT == kFmtMxfp4 || aval[mb] ? *(const SHARED u32x4*)(arow[mb] + kTileK * q + kGroup * g)
+                                                             : zero4);   // (rows past nrows: as in gu_item_wide)
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
         const int u = qq * NB + b;             // ring slot of tile t0 + u
