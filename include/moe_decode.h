@@ -313,7 +313,8 @@ moe_status moe_decode_set_swiglu_limit(moe_decode_handle* h, float limit);
  * off (the default).  MOE_ERR_INVALID_ARG for a NULL handle or exactly one
  * NULL event.  A run with events set on a handle created with
  * MOE_FLAG_COOPERATIVE returns MOE_ERR_UNSUPPORTED (a cooperative launch
- * takes no events).  Not for use under graph capture.  No device work.
+ * takes no events), and so does a run with events set on a stream that is
+ * capturing a graph (launch events time eager runs only).  No device work.
  */
 moe_status moe_decode_set_launch_events(moe_decode_handle* h, void* start_event, void* stop_event);
 

@@ -3572,8 +3572,8 @@ moe_status run_impl(moe_decode_handle* h, const void* x, int32_t T, void* y,
   // per item), 3 = x in LDS with full-tile items (H = 64 kFullTiles,
   // I = 32 kFullTiles, h staged in LDS, local routing), 5 = the same with one
   // more down tile per row block (I = 576 at 64-K tiles: the pages' per-GPU
-  // width without padding), 4 = more than 16 rows with wide items (FP8 only,
-  // H = 64 kWideTiles, I = 64 kWideQ2), 6 and 7 = the same at I = 576 and 640
+  // width without padding), 4 = more than 16 rows with wide items
+  // (H = 64 kWideTiles, I = 64 kWideQ2), 6 and 7 = the same at I = 576 and 640
   // (one and two more down K tiles per row block)
   const bool full = p.full != 0;
   // paired gate/up items exist only in the full-tile MXFP4 kernel, whose
@@ -3618,6 +3618,14 @@ moe_status run_impl(moe_decode_handle* h, const void* x, int32_t T, void* y,
   if (coop && h->ev_start) {                  // a cooperative launch takes no events
     if (prev != h->device) (void)hipSetDevice(prev);
     return MOE_ERR_UNSUPPORTED;
+  }
+  if (h->ev_start) {                          // launch events time eager runs only
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    const hipError_t qe = hipStreamIsCapturing(stream, &cs);
+    if (qe != hipSuccess || cs != hipStreamCaptureStatusNone) {
+      if (prev != h->device) (void)hipSetDevice(prev);
+      return qe != hipSuccess ? MOE_ERR_HIP : MOE_ERR_UNSUPPORTED;
+    }
   }
   const hipError_t err =
       coop ? hipLaunchCooperativeKernel(fn, dim3(grid), dim3(kThreads), args, p.lds_bytes, stream)

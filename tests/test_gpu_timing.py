@@ -1,7 +1,8 @@
 """moe_decode_set_launch_events: runs launched with the kernel's own start and
 stop events.  The outputs are those of a run without events, bit for bit; the
 kernel events fall inside event records queued around the call; clearing the
-events restores plain launches; a cooperative handle refuses timed runs."""
+events restores plain launches; a cooperative handle, and a stream that is
+capturing a graph, refuse timed runs."""
 import json
 import os
 
@@ -82,4 +83,36 @@ def test_cooperative_handle_refuses_timed_runs():
     layer.run(x, y)
     torch.cuda.synchronize()
     assert layer.check() == binding.MOE_OK
+    layer.close()
+
+
+def test_launch_events_refused_under_graph_capture():
+    wl = synth.WORKLOADS[0]          # tiny
+    print(f"case launch events under capture {wl.name}", flush=True)
+    inp = synth.make_inputs(wl, GOLDEN["attempts"][wl.name])
+    layer = device.make_layer(inp)
+    dev = torch.device("cuda", 0)
+    x = device.to_device(inp.x, dev)
+    y = torch.empty_like(x)
+    layer.run(x, y)                  # eager first (occupancy query outside the capture)
+    torch.cuda.synchronize()
+    k0, k1 = _events(2)
+    before = k0.elapsed_time(k1)     # the two records of _events
+    layer.set_launch_events(k0, k1)
+    g = torch.cuda.CUDAGraph()
+    status = None
+    with torch.cuda.graph(g):
+        y.zero_()                    # the graph holds this one node
+        try:
+            layer.run(x, y)
+        except binding.MoeDecodeError as e:
+            status = e.status
+    assert status == binding.MOE_ERR_UNSUPPORTED
+    # eager runs with the same events still time the kernel
+    y1 = torch.full_like(x, -1)
+    layer.run(x, y1)
+    torch.cuda.synchronize()
+    assert layer.check() == binding.MOE_OK
+    assert k0.elapsed_time(k1) > 0.0 and k0.elapsed_time(k1) != before
+    layer.set_launch_events(None, None)
     layer.close()
