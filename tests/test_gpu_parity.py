@@ -331,3 +331,36 @@ def test_all_equal_logits_select_the_lowest_expert_ids():
     assert np.array_equal(out["topk_idx"], np.tile(np.arange(wl.K, dtype=np.int32), (wl.T, 1)))
     assert np.abs(out["topk_w"] - 1.0 / wl.K).max() <= 1e-6
     _check_routing_in_kernel_precision(wl, zero, out)
+
+
+@pytest.mark.parametrize("name", ["verify_t6_h4096_e256_k8_s1", "verify_t6_h4096_e256_k8_s1_mxfp4",
+                                  "zipf_t64_h4096_e256_k8_s1"])
+def test_relabelled_experts_give_the_same_y(name):
+    """Routed expert e moved to id p[e] (router row, bias and packed weights
+    together): the kernel selects p[idx] and returns the same y bit for bit,
+    since every logit and every expert output is formed in the same order
+    wherever its expert sits.  Checks the expert id -> weight slot mapping of
+    the router tiles, the placement and the packed layouts."""
+    wl = synth.BY_NAME[name]
+    print(f"case relabelled experts {name}", flush=True)
+    inp = inputs_for(wl)
+    layer = device.make_layer(inp)
+    base = device.run_once(layer, inp.x, wl.E, wl.K)
+    layer.close()
+    p = np.random.default_rng(5).permutation(wl.E)
+    moved = synth.Inputs(wl, inp.x, np.empty_like(inp.router_w), None, np.empty_like(inp.w13),
+                         np.empty_like(inp.s13), np.empty_like(inp.w2), np.empty_like(inp.s2), inp.attempts)
+    moved.router_w[p] = inp.router_w
+    if inp.router_b is not None:
+        moved.router_b = np.empty_like(inp.router_b)
+        moved.router_b[p] = inp.router_b
+    for field in ("w13", "s13", "w2", "s2"):
+        src, dst = getattr(inp, field), getattr(moved, field)
+        dst[p] = src[:wl.E]
+        dst[wl.E:] = src[wl.E:]                      # the shared expert keeps slot E
+    layer = device.make_layer(moved)
+    got = device.run_once(layer, inp.x, wl.E, wl.K)
+    layer.close()
+    assert np.array_equal(got["topk_idx"], p[base["topk_idx"]])
+    assert np.array_equal(got["topk_w"], base["topk_w"])
+    assert np.array_equal(got["y"], base["y"])
