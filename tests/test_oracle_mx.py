@@ -169,3 +169,25 @@ def test_generator_mx_quantiser(fmt, emax, top):
     ok = np.abs(ref) / np.repeat(2.0 ** X, 32, axis=1) < top
     err = np.abs(W - ref) / np.repeat(2.0 ** X, 32, axis=1)
     assert np.all(err[ok] <= np.maximum(step[ok], 2.0 ** (-1 if fmt == "mxfp4" else -9)) / 2 + 1e-12)
+
+
+@pytest.mark.parametrize("fmt", ["mxfp4", "mxfp8"])
+def test_relabelled_experts_change_nothing(fmt):
+    """MX weights moved with their expert to a permuted id (codes and E8M0
+    scales together) give the same selections, mapped, and the same y."""
+    import dataclasses
+    wl = dataclasses.replace(MXSMALL[1], weight_format=fmt)
+    inp = synth.make_inputs(wl)
+    att = O.choose_attempts(wl, lambda a: synth.x_rows(wl, a), inp.router_w, inp.router_b)
+    inp.x = synth.x_rows(wl, att)
+    base = O.forward(inp)
+    p = np.random.default_rng(13).permutation(wl.E)
+    moved = synth.Inputs(wl, inp.x, inp.router_w.copy(), inp.router_b.copy(), inp.w13.copy(),
+                         inp.s13.copy(), inp.w2.copy(), inp.s2.copy(), att)
+    moved.router_w[p] = inp.router_w
+    moved.router_b[p] = inp.router_b
+    for name in ("w13", "s13", "w2", "s2"):
+        getattr(moved, name)[p] = getattr(inp, name)[:wl.E]
+    res = O.forward(moved)
+    assert np.array_equal(res.idx, p[base.idx])
+    np.testing.assert_allclose(res.y, base.y, rtol=1e-12, atol=1e-12 * np.abs(base.y).max())
